@@ -1,0 +1,371 @@
+#!/usr/bin/env python3
+"""Benchmark of the CSA / HCA / DSA hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workloads a,b,...] [--no-cpu]
+
+Prints ONE JSON line.  ``value`` is CSA prefill tokens/s (8192-token sequence,
+64 heads x 512, top-512 of 2048 pool entries, window 128): one step is every
+stage of the path over that batch -- RoPE table, window-row rotation, K=V pool
+and indexer-key compression, index scores, top-k, sparse attention -- with the
+inputs already resident in HBM.  Each stage is timed with HIP events on the
+stream its kernels run on; ``roofline`` reports the dominant kernel's
+algorithmic FLOP/s or bytes/s against the MI355X peak.  CSA decode (64 x 1
+token after 131072 cached tokens) is reported in us/step, and the HCA and DSA
+workloads in tokens/s.  ``cpu_baseline`` times the CPU oracle on a stratified
+sample of the prefill rows.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import glob
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "CSA prefill tokens/s + decode µs/step; % of MI355X HBM / MFMA peak"
+PEAK = {"mfma": (2500.0, "TFLOP/s"), "hbm": (8000.0, "GB/s")}   # bf16 dense MFMA; HBM3E
+
+
+# ------------------------------------------------------------------ work counts
+def ready(t, m, T):
+    return np.clip((t + 1) // m, 0, T)
+
+
+def visible_window(wl, t):
+    if not wl.window:
+        return np.zeros_like(t)
+    return np.minimum(t + 1, wl.window)
+
+
+def work_counts(wl):
+    """Algorithmic work of each stage (flops or bytes), per launch."""
+    t = wl.q_pos0 + np.arange(wl.S, dtype=np.int64)
+    R = ready(t, wl.m, wl.T)
+    e = 2  # bytes per bf16 element
+    B = wl.B
+    w = {}
+    if not wl.decode:
+        w["compress_window"] = ("hbm", B * wl.ctx * wl.D * e * 2)
+        if wl.kind != "dsa":
+            w["compress_kv"] = ("hbm", B * (2 * wl.ctx + wl.T) * wl.D * e)
+        if wl.n_idx_heads:
+            gates = 2 if wl.kind != "dsa" else 1
+            w["compress_idx"] = ("hbm", B * (gates * wl.ctx + wl.T) * wl.idx_dim * e)
+    if wl.n_idx_heads:
+        pairs = int(R.sum()) * B
+        if wl.decode:   # streams the index-key pool once: HBM-bound
+            w["index_scores"] = ("hbm", B * wl.T * wl.idx_dim * e + pairs * 4 +
+                                 B * wl.S * wl.n_idx_heads * (wl.idx_dim * e + 4))
+        else:
+            w["index_scores"] = ("mfma", pairs * wl.n_idx_heads * (2 * wl.idx_dim + 2))
+        w["topk"] = ("hbm", pairs * 4 + B * wl.S * wl.topk * 4)
+        keys = (visible_window(wl, t) + np.minimum(R, wl.topk)).sum() * B
+    else:
+        keys = (visible_window(wl, t) + R).sum() * B
+    flops = int(keys) * wl.H * (2 * wl.D + 2 * wl.dv)
+    if wl.decode:   # gathers the selected K=V rows once: HBM-bound
+        w["attention"] = ("hbm", int(keys) * wl.D * e + B * wl.S * wl.H * (wl.D + wl.dv) * e)
+    else:
+        w["attention"] = ("mfma", flops)
+    return w, int(keys)
+
+
+# ------------------------------------------------------------------ GPU runs
+class Runner:
+    def __init__(self, wl, csa, torch):
+        self.wl, self.csa, self.torch = wl, csa, torch
+        self.stages = []          # (name, launch fn)
+
+    def add(self, name, fn):
+        self.stages.append((name, fn))
+
+    def run(self, steps, warmup, flush=None):
+        torch = self.torch
+        for _ in range(warmup):
+            for _, fn in self.stages:
+                fn()
+        torch.cuda.synchronize()
+        ev = {n: [] for n, _ in self.stages}
+        total_ms = 0.0
+        for _ in range(steps):
+            if flush is not None:
+                flush()
+            s0 = torch.cuda.Event(enable_timing=True)
+            s1 = torch.cuda.Event(enable_timing=True)
+            s0.record()
+            for name, fn in self.stages:
+                a = torch.cuda.Event(enable_timing=True)
+                b = torch.cuda.Event(enable_timing=True)
+                a.record()
+                fn()
+                b.record()
+                ev[name].append((a, b))
+            s1.record()
+            torch.cuda.synchronize()
+            total_ms += s0.elapsed_time(s1)
+        avg = {n: float(np.mean([a.elapsed_time(b) for a, b in v])) for n, v in ev.items()}
+        return total_ms / steps, avg
+
+
+def setup(wl, csa, torch, synth):
+    """Inputs resident on the GPU, outputs preallocated, one closure per stage."""
+    dev = "cuda"
+    a, B, S = wl.act_scale, wl.B, wl.S
+    bf = torch.bfloat16
+
+    def gen(name, n, shape, dtype=bf):
+        return synth.normal_torch(0, name, n, shape, scale=a, dtype=dtype).to(dev)
+
+    r = Runner(wl, csa, torch)
+    # the RoPE table is model set-up (built once, reused by every step); its
+    # build is timed on its own and reported beside the step
+    cs = torch.empty((wl.n_pos, wl.rope_dim // 2, 2), dtype=torch.float32, device=dev)
+    _rope(csa, cs, wl)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    _rope(csa, cs, wl)
+    e1.record()
+    torch.cuda.synchronize()
+    r.setup_ms = {"rope_table": e0.elapsed_time(e1)}
+    q_pos = torch.full((B,), wl.q_pos0, dtype=torch.int32, device=dev)
+    sink = (torch.from_numpy(synth.normal(0, "sink", wl.H, ())).to(dev) if wl.sink else None)
+    q = gen("q", B * S, (wl.H, wl.D)).view(B, S, wl.H, wl.D)
+    out = torch.empty((B, S, wl.H, wl.dv), dtype=bf, device=dev)
+    if wl.decode:
+        pool = gen("pool", B * wl.T, (wl.D,)).view(B, wl.T, wl.D)
+        k_idx = gen("k_idx", B * wl.T, (wl.idx_dim,)).view(B, wl.T, wl.idx_dim)
+        kv_win = gen("kv_win", B * wl.window, (wl.D,)).view(B, wl.window, wl.D)
+        win_pos0 = torch.full((B,), wl.q_pos0 - wl.window + 1, dtype=torch.int32, device=dev)
+    else:
+        x = gen("x", B * wl.ctx, (wl.D,)).view(B, wl.ctx, wl.D)
+        kv_win = torch.empty_like(x)
+        win_pos0 = torch.zeros((B,), dtype=torch.int32, device=dev)
+        r.add("compress_window", lambda: csa.csa_compress(x, m=1, overlap=0,
+                                                          rope_dim=wl.rope_dim, cs=cs, pos0=0,
+                                                          out=kv_win))
+        if wl.kind == "dsa":
+            pool = kv_win
+        else:
+            gate = gen("gate", B * wl.ctx, (wl.D,)).view(B, wl.ctx, wl.D)
+            pool = torch.empty((B, wl.T, wl.D), dtype=bf, device=dev)
+            r.add("compress_kv", lambda: csa.csa_compress(x, gate, m=wl.m, overlap=wl.overlap,
+                                                          rope_dim=wl.rope_dim, cs=cs, pos0=0,
+                                                          out=pool))
+        if wl.n_idx_heads:
+            xi = gen("x_idx", B * wl.ctx, (wl.idx_dim,)).view(B, wl.ctx, wl.idx_dim)
+            gi = (None if wl.kind == "dsa" else
+                  gen("gate_idx", B * wl.ctx, (wl.idx_dim,)).view(B, wl.ctx, wl.idx_dim))
+            k_idx = torch.empty((B, wl.T, wl.idx_dim), dtype=bf, device=dev)
+            r.add("compress_idx", lambda: csa.csa_compress(xi, gi, m=wl.m, overlap=wl.overlap,
+                                                           out=k_idx))
+    kvw = kv_win if wl.window else None
+    if wl.n_idx_heads:
+        q_idx = gen("q_idx", B * S, (wl.n_idx_heads, wl.idx_dim)).view(B, S, wl.n_idx_heads,
+                                                                       wl.idx_dim)
+        w_idx = gen("w_idx", B * S, (wl.n_idx_heads,), torch.float32).view(B, S, wl.n_idx_heads)
+        scores = torch.empty((B, S, wl.T), dtype=torch.float32, device=dev)
+        idx = torch.empty((B, S, wl.topk), dtype=torch.int32, device=dev)
+        r.add("index_scores", lambda: csa.csa_index_scores(q_idx, w_idx, k_idx, q_pos, m=wl.m,
+                                                           out=scores))
+        r.add("topk", lambda: csa.csa_topk(scores, q_pos, k=wl.topk, m=wl.m, out=idx))
+        need = csa.lib().csa_sparse_attn_workspace_size(B, S, wl.H, wl.D, wl.dv, wl.rope_dim,
+                                                        wl.topk, wl.window, 1)
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+        r.add("attention", lambda: csa.csa_sparse_attn(q, kvw, win_pos0, pool, idx, sink, q_pos,
+                                                       rope_dim=wl.rope_dim, cs=cs,
+                                                       window=wl.window, scale=wl.scale,
+                                                       dv=wl.dv, out=out, workspace=ws))
+    else:
+        need = csa.lib().hca_attn_workspace_size(B, S, wl.H, wl.D, wl.dv, wl.rope_dim, wl.T,
+                                                 wl.window, 1)
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+        r.add("attention", lambda: csa.hca_attn(q, kvw, win_pos0, pool, sink, q_pos, m=wl.m,
+                                                rope_dim=wl.rope_dim, cs=cs, window=wl.window,
+                                                scale=wl.scale, dv=wl.dv, out=out, workspace=ws))
+    return r
+
+
+def _rope(csa, cs, wl):
+    import ctypes
+    import torch
+    st = csa.lib().csa_rope_table(ctypes.c_void_p(cs.data_ptr()), wl.n_pos, wl.rope_dim,
+                                  float(wl.theta),
+                                  ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    if st != 0:
+        raise RuntimeError(csa.lib().csa_last_error().decode())
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(ROOT, "sparse_long_context_pool_amd", "csrc", "*"))):
+        h.update(open(p, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload, stage):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel sources (else None)."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    try:
+        d = json.load(open(path))
+    except (OSError, ValueError):
+        return None
+    if d.get("kernel_sources") != kernel_source_hash():
+        return None
+    return d.get("bytes_per_launch", {}).get(f"{workload}/{stage}")
+
+
+def stage_report(wl, avg_ms, work):
+    rep = {}
+    for name, ms in avg_ms.items():
+        bound, amount = work[name]
+        peak, unit = PEAK[bound]
+        scale = 1e12 if bound == "mfma" else 1e9
+        achieved = amount / (ms * 1e-3) / scale
+        rep[name] = {"ms": round(ms, 5), "bound": bound, "achieved": round(achieved, 2),
+                     "peak": peak, "unit": unit, "frac": round(achieved / peak, 4),
+                     "work": amount}
+    return rep
+
+
+def run_workload(name, steps, warmup, csa, torch, synth, WORKLOADS):
+    wl = WORKLOADS[name]
+    t0 = time.time()
+    r = setup(wl, csa, torch, synth)
+    torch.cuda.synchronize()
+    flush = None
+    if wl.decode:
+        # the decode working set fits the 256 MB last-level cache: flush it
+        # between steps so the gather reads HBM, not the cache
+        junk = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        flush = lambda: junk.fill_(1)
+    ms_step, avg = r.run(steps, warmup, flush)
+    work, keys = work_counts(wl)
+    stages = stage_report(wl, avg, work)
+    dom = max(stages, key=lambda n: stages[n]["ms"])
+    print(f"[bench] {name}: {ms_step:.3f} ms/step (setup {time.time() - t0:.1f}s); "
+          + ", ".join(f"{n} {v['ms']*1e3:.1f}us {100*v['frac']:.1f}%" for n, v in stages.items()),
+          file=sys.stderr, flush=True)
+    res = {"workload": name, "ms_per_step": round(ms_step, 5),
+           "setup_ms": {k: round(v, 5) for k, v in r.setup_ms.items()},
+           "tokens_per_s": round(wl.B * wl.S / (ms_step * 1e-3), 1),
+           "us_per_step": round(ms_step * 1e3, 2), "stages": stages, "dominant": dom,
+           "attended_keys": keys}
+    del r
+    torch.cuda.empty_cache()
+    return wl, res
+
+
+def roofline_of(wl_name, res):
+    dom = res["dominant"]
+    st = res["stages"][dom]
+    return {"kernel": dom, "bound": st["bound"], "achieved": st["achieved"], "peak": st["peak"],
+            "unit": st["unit"], "frac": st["frac"],
+            "traffic": measured_traffic(wl_name, dom)}
+
+
+# ------------------------------------------------------------------ CPU baseline
+def cpu_baseline(WORKLOADS, synth, n_rows=512):
+    """The oracle on the prefill workload: full-sequence compression plus a
+    stratified sample of query rows (index scores, top-k, attention), scaled
+    to the whole sequence."""
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    import oracle
+    from parity import Inputs
+    wl = WORKLOADS["csa_prefill_bf16"]
+    inp = Inputs(wl)
+    rows_all = np.arange(wl.ctx)
+    x, gate = inp.get("x", rows=rows_all), inp.get("gate", rows=rows_all)
+    xi, gi = inp.get("x_idx", rows=rows_all), inp.get("gate_idx", rows=rows_all)
+    rows = np.linspace(0, wl.S - 1, n_rows).astype(np.int64)
+    q, qi, wi = inp.get("q", rows=rows), inp.get("q_idx", rows=rows), inp.get("w_idx", rows=rows)
+    sink = inp.get("sink")
+    oracle.ensure_built()
+    t0 = time.perf_counter()
+    kv_win = oracle.compress(x, None, None, m=1, overlap=0, rope_dim=wl.rope_dim, theta=wl.theta,
+                             round_bf16=True)
+    pool = oracle.compress(x, gate, None, m=wl.m, overlap=1, rope_dim=wl.rope_dim,
+                           theta=wl.theta, round_bf16=True)
+    k_idx = oracle.compress(xi, gi, None, m=wl.m, overlap=1, round_bf16=True)
+    t1 = time.perf_counter()
+    sc = oracle.index_scores(qi, wi, rows, k_idx, m=wl.m)
+    idx = oracle.topk(sc, rows, k=wl.topk, m=wl.m)
+    oracle.attention(q, rows, kv_win=kv_win, win_pos0=0, window=wl.window, pool=pool, idx=idx,
+                     m=wl.m, sink=sink, rope_dim=wl.rope_dim, theta=wl.theta, scale=wl.scale)
+    t2 = time.perf_counter()
+    total = (t1 - t0) + (t2 - t1) * wl.S / n_rows
+    cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    return {"value": round(wl.S / total, 2), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": (f"csa_prefill_bf16: compression of all {wl.ctx} tokens "
+                       f"({t1 - t0:.2f}s) + {n_rows} of {wl.S} query rows, evenly spaced "
+                       f"({t2 - t1:.2f}s), scaled to {wl.S} rows"),
+            "seconds_measured": round(t2 - t0, 2)}
+
+
+# ------------------------------------------------------------------ main
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workloads", default="csa_prefill_bf16,csa_decode_bf16,hca_bf16,dsa_bf16")
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU (asked for --gpus {args.gpus}); the path is "
+              "single-GPU by design and multi-GPU scaling is not part of this benchmark",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from sparse_long_context_pool_amd import csa, synth
+    from sparse_long_context_pool_amd.workloads import WORKLOADS
+    csa.lib()
+    torch.cuda.set_device(0)
+
+    names = [n for n in args.workloads.split(",") if n]
+    results = {}
+    for n in names:
+        steps = args.steps if n in ("csa_prefill_bf16", "csa_decode_bf16") else max(3, args.steps // 4)
+        results[n] = run_workload(n, steps, args.warmup, csa, torch, synth, WORKLOADS)
+
+    main_name = "csa_prefill_bf16" if "csa_prefill_bf16" in results else names[0]
+    wl, res = results[main_name]
+    line = {
+        "metric": METRIC, "value": res["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": res["ms_per_step"],
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": main_name, "B": wl.B, "S": wl.S, "H": wl.H, "D": wl.D,
+                   "rope_dim": wl.rope_dim, "m": wl.m, "T": wl.T, "index_heads": wl.n_idx_heads,
+                   "index_dim": wl.idx_dim, "index_topk": wl.topk, "window": wl.window,
+                   "parallelism": "single GPU"},
+        "roofline": roofline_of(main_name, res),
+        "stages": res["stages"], "setup_ms": res["setup_ms"],
+    }
+    for n, (w2, r2) in results.items():
+        if n == main_name:
+            continue
+        key = {"csa_decode_bf16": "decode", "hca_bf16": "hca", "dsa_bf16": "dsa"}.get(n, n)
+        entry = {"workload": n, "ms_per_step": r2["ms_per_step"], "setup_ms": r2["setup_ms"],
+                 "roofline": roofline_of(n, r2), "stages": r2["stages"]}
+        if w2.decode:
+            entry["us_per_step"] = r2["us_per_step"]
+        else:
+            entry["tokens_per_s"] = r2["tokens_per_s"]
+        line[key] = entry
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline(WORKLOADS, synth)
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,60 @@
+"""Build libcsa.so (the gfx950 HIP kernels + the C ABI of include/csa.h).
+
+Each csrc/*.hip file is compiled on its own with hipcc for gfx950 only, then
+the objects are linked into sparse_long_context_pool_amd/libcsa.so in-tree.
+Usage: python -m sparse_long_context_pool_amd.build [--resource-usage]
+"""
+from __future__ import annotations
+
+import glob
+import os
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+BUILD = os.path.join(PKG, "_build")
+LIB = os.path.join(PKG, "libcsa.so")
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+
+HIP_FLAGS = [
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
+    # no packed-fp32 instructions: plain fp32 VALU only
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-I", os.path.join(ROOT, "include"),
+    "-Wall", "-Wno-unused-function",
+]
+
+
+def _compile(src: str, extra: list[str]) -> str:
+    obj = os.path.join(BUILD, os.path.basename(src).replace(".hip", ".o"))
+    cmd = [HIPCC, *HIP_FLAGS, *extra, "-c", src, "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    out = (r.stdout + r.stderr)
+    # hipcc's host pass does not know the gfx950 feature flag; that note is noise
+    lines = [l for l in out.splitlines()
+             if "packed-fp32-ops' is not a recognized feature" not in l]
+    if lines:
+        sys.stderr.write("\n".join(lines) + "\n")
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed on {src}")
+    return obj
+
+
+def build(resource_usage: bool = False) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    extra = ["-Rpass-analysis=kernel-resource-usage"] if resource_usage else []
+    with ThreadPoolExecutor(min(8, len(srcs))) as ex:
+        objs = list(ex.map(lambda s: _compile(s, extra), srcs))
+    tmp = LIB + ".tmp"
+    subprocess.run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs],
+                   check=True)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(resource_usage="--resource-usage" in sys.argv))

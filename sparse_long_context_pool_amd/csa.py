@@ -1,0 +1,196 @@
+"""Python binding of libcsa.so (include/csa.h): argument marshalling only.
+
+Every function has the name of the C entry point it calls.  Tensors are torch
+tensors on the current GPU; the call is enqueued on torch's current stream.
+Outputs are allocated with torch when ``out`` is None.  There is no fallback:
+if libcsa.so is missing or a call fails, an exception is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libcsa.so")
+CSA_F32, CSA_BF16 = 0, 1
+_lib = None
+
+
+def lib():
+    """The loaded libcsa.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(f"{_LIB_PATH} is missing: build it with "
+                               "`python -m sparse_long_context_pool_amd.build`")
+        L = ctypes.CDLL(_LIB_PATH)
+        vp, i32, f32, f64, sz = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_float,
+                                 ctypes.c_double, ctypes.c_size_t)
+        sig = {
+            "csa_last_error": ([], ctypes.c_char_p),
+            "csa_version": ([], ctypes.c_char_p),
+            "csa_rope_table": ([vp, i32, i32, f64, vp], ctypes.c_int),
+            "csa_compress": ([vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp, i32, i32,
+                              i32, vp], ctypes.c_int),
+            "csa_index_scores": ([vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
+                                  vp], ctypes.c_int),
+            "csa_topk": ([vp, vp, vp, i32, i32, i32, i32, i32, vp], ctypes.c_int),
+            "csa_sparse_attn": ([vp, vp, vp, i32, vp, i32, vp, i32, vp, vp, vp, i32, i32,
+                                 i32, i32, i32, i32, vp, i32, i32, f32, vp, sz, i32, vp],
+                                ctypes.c_int),
+            "csa_sparse_attn_workspace_size": ([i32] * 9, sz),
+            "hca_attn": ([vp, vp, vp, i32, vp, i32, i32, vp, vp, vp, i32, i32, i32, i32,
+                          i32, i32, vp, i32, i32, f32, vp, sz, i32, vp], ctypes.c_int),
+            "hca_attn_workspace_size": ([i32] * 9, sz),
+        }
+        for name, (args, res) in sig.items():
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = res
+        _lib = L
+    return _lib
+
+
+EXPORTS = ("csa_last_error", "csa_version", "csa_rope_table", "csa_compress",
+           "csa_index_scores", "csa_topk", "csa_sparse_attn",
+           "csa_sparse_attn_workspace_size", "hca_attn", "hca_attn_workspace_size")
+
+
+def _check(status: int, fn: str):
+    if status != 0:
+        msg = lib().csa_last_error().decode()
+        raise RuntimeError(f"{fn} failed (status {status}): {msg}")
+
+
+def _dtype(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return CSA_BF16
+    if t.dtype == torch.float32:
+        return CSA_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensors must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def version() -> str:
+    return lib().csa_version().decode()
+
+
+def csa_rope_table(n_pos: int, rope_dim: int, theta: float, device=None) -> torch.Tensor:
+    """cos/sin table [n_pos, rope_dim/2, 2] fp32 (angle in fp64)."""
+    cs = torch.empty((n_pos, rope_dim // 2, 2), dtype=torch.float32,
+                     device=device or torch.device("cuda"))
+    _check(lib().csa_rope_table(_ptr(cs), n_pos, rope_dim, float(theta), _stream()),
+           "csa_rope_table")
+    return cs
+
+
+def csa_compress(x, gate=None, slot_bias=None, *, m: int, overlap: int, rope_dim: int = 0,
+                 cs=None, pos0: int = 0, out=None) -> torch.Tensor:
+    """x [B, S, D] (+ gate [B, S, D], slot_bias [(1+overlap)*m, D] fp32) -> pool [B, S//m, D]."""
+    B, S, D = x.shape
+    if gate is not None:
+        assert gate.shape == x.shape and gate.dtype == x.dtype
+    if slot_bias is not None:
+        assert slot_bias.dtype == torch.float32 and slot_bias.shape == ((1 + overlap) * m, D)
+    if out is None:
+        out = torch.empty((B, S // m, D), dtype=x.dtype, device=x.device)
+    n_pos = 0 if cs is None else cs.shape[0]
+    _check(lib().csa_compress(_ptr(x), _ptr(gate), _ptr(slot_bias), _ptr(out), B, S, D, m,
+                              overlap, rope_dim, _ptr(cs), n_pos, pos0, _dtype(x), _stream()),
+           "csa_compress")
+    return out
+
+
+def csa_index_scores(q_idx, w_idx, k_pool, q_pos, *, m: int, out=None) -> torch.Tensor:
+    """q_idx [B, S, nI, cI], w_idx [B, S, nI] fp32, k_pool [B, T, cI] -> scores [B, S, T] fp32.
+
+    Entries w >= R(t) are not written."""
+    B, S, nI, cI = q_idx.shape
+    T = k_pool.shape[1]
+    assert w_idx.dtype == torch.float32 and k_pool.dtype == q_idx.dtype
+    assert q_pos.dtype == torch.int32 and q_pos.numel() == B
+    if out is None:
+        out = torch.empty((B, S, T), dtype=torch.float32, device=q_idx.device)
+    _check(lib().csa_index_scores(_ptr(q_idx), _ptr(w_idx), _ptr(k_pool), _ptr(out),
+                                  _ptr(q_pos), B, S, T, nI, cI, m, _dtype(q_idx), _stream()),
+           "csa_index_scores")
+    return out
+
+
+def csa_topk(scores, q_pos, *, k: int, m: int, out=None) -> torch.Tensor:
+    """scores [B, S, T] fp32 -> idx [B, S, k] int32 (ascending, -1 padded)."""
+    B, S, T = scores.shape
+    assert scores.dtype == torch.float32 and q_pos.dtype == torch.int32
+    if out is None:
+        out = torch.empty((B, S, k), dtype=torch.int32, device=scores.device)
+    _check(lib().csa_topk(_ptr(scores), _ptr(out), _ptr(q_pos), B, S, T, k, m, _stream()),
+           "csa_topk")
+    return out
+
+
+def _ws(size: int, device, workspace):
+    if size == 0:
+        return None, 0
+    if workspace is None:
+        workspace = torch.empty(size, dtype=torch.uint8, device=device)
+    return workspace, workspace.numel() * workspace.element_size()
+
+
+def csa_sparse_attn(q, kv_win, win_pos0, pool, idx, sink, q_pos, *, rope_dim: int, cs,
+                    window: int, scale: float, dv: int | None = None, out=None,
+                    workspace=None) -> torch.Tensor:
+    """q [B, S, H, D]; kv_win [B, L, D] (rotated); pool [B, T, D] (rotated);
+    idx [B, S, k] int32; sink [H] fp32 or None -> out [B, S, H, dv]."""
+    B, S, H, D = q.shape
+    dv = D if dv is None else dv
+    L = 0 if kv_win is None else kv_win.shape[1]
+    T = 0 if pool is None else pool.shape[1]
+    k = 0 if idx is None else idx.shape[2]
+    if out is None:
+        out = torch.empty((B, S, H, dv), dtype=q.dtype, device=q.device)
+    dt = _dtype(q)
+    need = lib().csa_sparse_attn_workspace_size(B, S, H, D, dv, rope_dim, k, window, dt)
+    ws, ws_bytes = _ws(need, q.device, workspace)
+    n_pos = 0 if cs is None else cs.shape[0]
+    _check(lib().csa_sparse_attn(_ptr(q), _ptr(kv_win), _ptr(win_pos0), L, _ptr(pool), T,
+                                 _ptr(idx), k, _ptr(sink), _ptr(out), _ptr(q_pos), B, S, H, D,
+                                 dv, rope_dim, _ptr(cs), n_pos, window, float(scale),
+                                 _ptr(ws), ws_bytes, dt, _stream()),
+           "csa_sparse_attn")
+    return out
+
+
+def hca_attn(q, kv_win, win_pos0, pool, sink, q_pos, *, m: int, rope_dim: int, cs,
+             window: int, scale: float, dv: int | None = None, out=None,
+             workspace=None) -> torch.Tensor:
+    """As csa_sparse_attn with every ready pool entry w < min(T, (t+1)//m)."""
+    B, S, H, D = q.shape
+    dv = D if dv is None else dv
+    L = 0 if kv_win is None else kv_win.shape[1]
+    T = 0 if pool is None else pool.shape[1]
+    if out is None:
+        out = torch.empty((B, S, H, dv), dtype=q.dtype, device=q.device)
+    dt = _dtype(q)
+    need = lib().hca_attn_workspace_size(B, S, H, D, dv, rope_dim, T, window, dt)
+    ws, ws_bytes = _ws(need, q.device, workspace)
+    n_pos = 0 if cs is None else cs.shape[0]
+    _check(lib().hca_attn(_ptr(q), _ptr(kv_win), _ptr(win_pos0), L, _ptr(pool), T, m,
+                          _ptr(sink), _ptr(out), _ptr(q_pos), B, S, H, D, dv, rope_dim,
+                          _ptr(cs), n_pos, window, float(scale), _ptr(ws), ws_bytes, dt,
+                          _stream()),
+           "hca_attn")
+    return out

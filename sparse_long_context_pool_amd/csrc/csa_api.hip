@@ -1,0 +1,266 @@
+// csa_api.hip -- the extern "C" boundary of libcsa.so (declared in include/csa.h).
+// Validates arguments on the host, picks a kernel and launch geometry, enqueues
+// on the caller's stream and reports errors through a thread-local string.
+// Never synchronizes, never allocates device memory, never throws.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "../../include/csa.h"
+#include "csa_device.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+csa_status_t fail(csa_status_t st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+csa_status_t launched(hipError_t e, const char* what) {
+  if (e != hipSuccess)
+    return fail(CSA_ERR_LAUNCH, "%s: launch failed: %s", what, hipGetErrorString(e));
+  g_err[0] = '\0';
+  return CSA_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool dtype_ok(int32_t dt) { return dt == CSA_F32 || dt == CSA_BF16; }
+
+hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+// Shared checks of csa_sparse_attn / hca_attn.
+csa_status_t check_attn(const char* fn, const void* q, const void* kv_win,
+                        const int32_t* win_pos0, int32_t L_win, const void* pool, int32_t T,
+                        void* out, const int32_t* q_pos, int32_t B, int32_t S, int32_t H,
+                        int32_t D, int32_t dv, int32_t rope_dim, const float* cs,
+                        int32_t n_pos, int32_t window, float scale, int32_t dtype) {
+  if (!dtype_ok(dtype)) return fail(CSA_ERR_INVALID, "%s: unknown dtype %d", fn, dtype);
+  if (B < 0 || S < 0 || H < 1 || D < 2 || T < 0 || L_win < 0 || window < 0)
+    return fail(CSA_ERR_INVALID,
+                "%s: bad sizes (B=%d S=%d H=%d D=%d T=%d L_win=%d window=%d)", fn, B, S, H,
+                D, T, L_win, window);
+  if (rope_dim < 0 || (rope_dim & 1) || rope_dim > D)
+    return fail(CSA_ERR_INVALID, "%s: rope_dim=%d must be even and in [0, D=%d]", fn,
+                rope_dim, D);
+  if (dv != D && dv != D - rope_dim)
+    return fail(CSA_ERR_INVALID, "%s: dv=%d must be D=%d or D-rope_dim=%d", fn, dv, D,
+                D - rope_dim);
+  if (dv < 1) return fail(CSA_ERR_INVALID, "%s: dv must be >= 1", fn);
+  if (D % 8 != 0 || dv % 2 != 0)
+    return fail(CSA_ERR_INVALID, "%s: D=%d must be a multiple of 8 and dv=%d even", fn, D,
+                dv);
+  if (D > 1024) return fail(CSA_ERR_UNSUPPORTED, "%s: D=%d > 1024", fn, D);
+  if (!(scale > 0.f) || scale != scale)
+    return fail(CSA_ERR_INVALID, "%s: scale must be positive", fn);
+  if ((long)B * S == 0) return CSA_OK;
+  if (!q || !out || !q_pos) return fail(CSA_ERR_INVALID, "%s: q, out, q_pos are required", fn);
+  if (!aligned16(q) || !aligned16(out))
+    return fail(CSA_ERR_INVALID, "%s: q and out must be 16-byte aligned", fn);
+  if (window > 0 && L_win > 0) {
+    if (!kv_win || !win_pos0)
+      return fail(CSA_ERR_INVALID, "%s: kv_win and win_pos0 are required when window > 0", fn);
+    if (!aligned16(kv_win)) return fail(CSA_ERR_INVALID, "%s: kv_win not 16-byte aligned", fn);
+  }
+  if (T > 0) {
+    if (!pool) return fail(CSA_ERR_INVALID, "%s: pool is required when T > 0", fn);
+    if (!aligned16(pool)) return fail(CSA_ERR_INVALID, "%s: pool not 16-byte aligned", fn);
+  }
+  if (rope_dim > 0 && (!cs || n_pos < 1))
+    return fail(CSA_ERR_INVALID, "%s: the RoPE table (cs, n_pos) is required", fn);
+  return CSA_OK;
+}
+
+csa::AttnParams make_params(const void* q, const void* kv_win, const int32_t* win_pos0,
+                            int32_t L_win, const void* pool, int32_t T, const int32_t* idx,
+                            int32_t k, int32_t m, const float* sink, void* out,
+                            const int32_t* q_pos, int32_t B, int32_t S, int32_t H, int32_t D,
+                            int32_t dv, int32_t rope_dim, const float* cs, int32_t n_pos,
+                            int32_t window, float scale, int32_t dtype) {
+  csa::AttnParams p;
+  const bool has_win = window > 0 && L_win > 0;
+  p.q = q;
+  p.kv_win = has_win ? kv_win : nullptr;
+  p.win_pos0 = has_win ? win_pos0 : nullptr;
+  p.L_win = has_win ? L_win : 0;
+  p.pool = T > 0 ? pool : nullptr;
+  p.T = T;
+  p.idx = idx;
+  p.k = idx ? k : 0;
+  p.dense = idx ? 0 : 1;
+  p.m = m;
+  p.sink = sink;
+  p.out = out;
+  p.q_pos = q_pos;
+  p.B = B; p.S = S; p.H = H; p.D = D; p.dv = dv; p.rope_dim = rope_dim;
+  p.cs = rope_dim > 0 ? cs : nullptr;
+  p.n_pos = n_pos;
+  p.window = has_win ? window : 0;
+  p.scale = scale;
+  p.bf16 = dtype == CSA_BF16;
+  return p;
+}
+
+csa_status_t run_attn(const char* fn, const csa::AttnParams& p, int max_slots,
+                      void* workspace, size_t ws_bytes, hipStream_t s) {
+  csa::AttnPlan plan = csa::plan_attention(p.B, p.S, p.H, p.D, p.dv, p.rope_dim, max_slots,
+                                           p.bf16, std::max<long>(p.L_win, p.T));
+  void* ws = nullptr;
+  if (plan.nsplit > 1) {
+    if (workspace && ws_bytes >= plan.ws_bytes && aligned16(workspace)) ws = workspace;
+    else plan.nsplit = 1;
+  }
+  return launched(csa::launch_attention(p, plan, ws, s), fn);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* csa_last_error(void) { return g_err; }
+
+const char* csa_version(void) { return "csa-mi355x 0.1 (gfx950)"; }
+
+csa_status_t csa_rope_table(float* cs, int32_t n_pos, int32_t rope_dim, double theta,
+                            void* stream) {
+  if (!cs) return fail(CSA_ERR_INVALID, "csa_rope_table: cs is NULL");
+  if (n_pos < 1 || rope_dim < 2 || (rope_dim & 1) || !(theta > 0.0))
+    return fail(CSA_ERR_INVALID,
+                "csa_rope_table: need n_pos >= 1, even rope_dim >= 2, theta > 0 "
+                "(n_pos=%d rope_dim=%d theta=%g)",
+                n_pos, rope_dim, theta);
+  return launched(csa::launch_rope_table(cs, n_pos, rope_dim, theta, as_stream(stream)),
+                  "csa_rope_table");
+}
+
+csa_status_t csa_compress(const void* x, const void* gate, const float* slot_bias,
+                          void* pool, int32_t B, int32_t S, int32_t D, int32_t m,
+                          int32_t overlap, int32_t rope_dim, const float* cs,
+                          int32_t n_pos, int32_t pos0, int32_t dtype, void* stream) {
+  const char* fn = "csa_compress";
+  if (!dtype_ok(dtype)) return fail(CSA_ERR_INVALID, "%s: unknown dtype %d", fn, dtype);
+  if (B < 0 || S < 0 || D < 8 || m < 1 || (overlap != 0 && overlap != 1))
+    return fail(CSA_ERR_INVALID, "%s: bad sizes (B=%d S=%d D=%d m=%d overlap=%d)", fn, B, S,
+                D, m, overlap);
+  if (D % 8 != 0) return fail(CSA_ERR_INVALID, "%s: D=%d must be a multiple of 8", fn, D);
+  if (D > 1024) return fail(CSA_ERR_UNSUPPORTED, "%s: D=%d > 1024", fn, D);
+  if (rope_dim < 0 || (rope_dim & 1) || rope_dim > D)
+    return fail(CSA_ERR_INVALID, "%s: rope_dim=%d must be even and in [0, D]", fn, rope_dim);
+  const int32_t T = S / m;
+  if ((long)B * T == 0) return CSA_OK;
+  if (!x || !pool) return fail(CSA_ERR_INVALID, "%s: x and pool are required", fn);
+  if (!aligned16(x) || !aligned16(pool) || (gate && !aligned16(gate)) ||
+      (slot_bias && !aligned16(slot_bias)))
+    return fail(CSA_ERR_INVALID, "%s: tensors must be 16-byte aligned", fn);
+  if (rope_dim > 0) {
+    if (!cs) return fail(CSA_ERR_INVALID, "%s: the RoPE table is required", fn);
+    if (pos0 < 0 || (long)pos0 + (long)(T - 1) * m >= n_pos)
+      return fail(CSA_ERR_INVALID,
+                  "%s: entry positions pos0=%d .. %ld exceed the RoPE table (n_pos=%d)", fn,
+                  pos0, (long)pos0 + (long)(T - 1) * m, n_pos);
+  }
+  return launched(csa::launch_compress(x, gate, slot_bias, pool, B, S, D, m, overlap,
+                                       rope_dim, cs, pos0, dtype == CSA_BF16,
+                                       as_stream(stream)),
+                  fn);
+}
+
+csa_status_t csa_index_scores(const void* q_idx, const float* w_idx, const void* k_pool,
+                              float* scores, const int32_t* q_pos, int32_t B, int32_t S,
+                              int32_t T, int32_t n_heads, int32_t head_dim, int32_t m,
+                              int32_t dtype, void* stream) {
+  const char* fn = "csa_index_scores";
+  if (!dtype_ok(dtype)) return fail(CSA_ERR_INVALID, "%s: unknown dtype %d", fn, dtype);
+  if (B < 0 || S < 0 || T < 0 || n_heads < 1 || head_dim < 1 || m < 1)
+    return fail(CSA_ERR_INVALID, "%s: bad sizes (B=%d S=%d T=%d heads=%d dim=%d m=%d)", fn,
+                B, S, T, n_heads, head_dim, m);
+  if (head_dim % 8 != 0)
+    return fail(CSA_ERR_INVALID, "%s: head_dim=%d must be a multiple of 8", fn, head_dim);
+  if ((long)n_heads * head_dim + n_heads > 16384)
+    return fail(CSA_ERR_UNSUPPORTED, "%s: n_heads*head_dim=%d too large", fn,
+                n_heads * head_dim);
+  if ((long)B * S * T == 0) return CSA_OK;
+  if (!q_idx || !w_idx || !k_pool || !scores || !q_pos)
+    return fail(CSA_ERR_INVALID, "%s: NULL tensor", fn);
+  if (!aligned16(q_idx) || !aligned16(k_pool))
+    return fail(CSA_ERR_INVALID, "%s: q_idx and k_pool must be 16-byte aligned", fn);
+  return launched(csa::launch_index_scores(q_idx, w_idx, k_pool, scores, q_pos, B, S, T,
+                                           n_heads, head_dim, m, dtype == CSA_BF16,
+                                           as_stream(stream)),
+                  fn);
+}
+
+csa_status_t csa_topk(const float* scores, int32_t* idx, const int32_t* q_pos, int32_t B,
+                      int32_t S, int32_t T, int32_t k, int32_t m, void* stream) {
+  const char* fn = "csa_topk";
+  if (B < 0 || S < 0 || T < 0 || k < 1 || m < 1)
+    return fail(CSA_ERR_INVALID, "%s: bad sizes (B=%d S=%d T=%d k=%d m=%d)", fn, B, S, T, k,
+                m);
+  if ((long)B * S == 0) return CSA_OK;
+  if (!idx || !q_pos || (T > 0 && !scores)) return fail(CSA_ERR_INVALID, "%s: NULL tensor", fn);
+  return launched(csa::launch_topk(scores, idx, q_pos, B, S, T, k, m, as_stream(stream)), fn);
+}
+
+size_t csa_sparse_attn_workspace_size(int32_t B, int32_t S, int32_t H, int32_t D, int32_t dv,
+                                      int32_t rope_dim, int32_t k, int32_t window,
+                                      int32_t dtype) {
+  if (B < 0 || S < 0 || H < 1 || D < 1 || dv < 1 || k < 0 || window < 0) return 0;
+  return csa::plan_attention(B, S, H, D, dv, rope_dim, window + k, dtype == CSA_BF16, 0)
+      .ws_bytes;
+}
+
+size_t hca_attn_workspace_size(int32_t B, int32_t S, int32_t H, int32_t D, int32_t dv,
+                               int32_t rope_dim, int32_t T, int32_t window, int32_t dtype) {
+  if (B < 0 || S < 0 || H < 1 || D < 1 || dv < 1 || T < 0 || window < 0) return 0;
+  return csa::plan_attention(B, S, H, D, dv, rope_dim, window + T, dtype == CSA_BF16, T)
+      .ws_bytes;
+}
+
+csa_status_t csa_sparse_attn(const void* q, const void* kv_win, const int32_t* win_pos0,
+                             int32_t L_win, const void* pool, int32_t T, const int32_t* idx,
+                             int32_t k, const float* sink, void* out, const int32_t* q_pos,
+                             int32_t B, int32_t S, int32_t H, int32_t D, int32_t dv,
+                             int32_t rope_dim, const float* cs, int32_t n_pos,
+                             int32_t window, float scale, void* workspace, size_t ws_bytes,
+                             int32_t dtype, void* stream) {
+  const char* fn = "csa_sparse_attn";
+  csa_status_t st = check_attn(fn, q, kv_win, win_pos0, L_win, pool, T, out, q_pos, B, S, H,
+                               D, dv, rope_dim, cs, n_pos, window, scale, dtype);
+  if (st != CSA_OK) return st;
+  if (k < 0) return fail(CSA_ERR_INVALID, "%s: k=%d must be >= 0", fn, k);
+  if ((long)B * S == 0) return CSA_OK;
+  if (k > 0 && !idx) return fail(CSA_ERR_INVALID, "%s: idx is required when k > 0", fn);
+  csa::AttnParams p = make_params(q, kv_win, win_pos0, L_win, pool, T, idx, k, 1, sink, out,
+                                  q_pos, B, S, H, D, dv, rope_dim, cs, n_pos, window, scale,
+                                  dtype);
+  if (k == 0) {  // no pool slot at all: window-only attention
+    p.idx = nullptr;
+    p.k = 0;
+    p.dense = 0;
+  }
+  return run_attn(fn, p, p.window + p.k, workspace, ws_bytes, as_stream(stream));
+}
+
+csa_status_t hca_attn(const void* q, const void* kv_win, const int32_t* win_pos0,
+                      int32_t L_win, const void* pool, int32_t T, int32_t m,
+                      const float* sink, void* out, const int32_t* q_pos, int32_t B,
+                      int32_t S, int32_t H, int32_t D, int32_t dv, int32_t rope_dim,
+                      const float* cs, int32_t n_pos, int32_t window, float scale,
+                      void* workspace, size_t ws_bytes, int32_t dtype, void* stream) {
+  const char* fn = "hca_attn";
+  csa_status_t st = check_attn(fn, q, kv_win, win_pos0, L_win, pool, T, out, q_pos, B, S, H,
+                               D, dv, rope_dim, cs, n_pos, window, scale, dtype);
+  if (st != CSA_OK) return st;
+  if (m < 1) return fail(CSA_ERR_INVALID, "%s: m=%d must be >= 1", fn, m);
+  if ((long)B * S == 0) return CSA_OK;
+  csa::AttnParams p = make_params(q, kv_win, win_pos0, L_win, pool, T, nullptr, 0, m, sink,
+                                  out, q_pos, B, S, H, D, dv, rope_dim, cs, n_pos, window,
+                                  scale, dtype);
+  return run_attn(fn, p, p.window + T, workspace, ws_bytes, as_stream(stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,158 @@
+// csa_device.hpp -- device helpers and kernel launch declarations shared by the
+// gfx950 kernels of libcsa.so.  CDNA4 only: 64-wide wavefronts, bf16 matrix
+// cores (v_mfma_f32_16x16x32_bf16 / v_mfma_f32_32x32x16_bf16), 160 KiB LDS.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+#include <algorithm>
+#include <stdint.h>
+
+namespace csa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned short u16;
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// ---------------------------------------------------------------- bf16 <-> fp32
+__device__ __forceinline__ float bf_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+__device__ __forceinline__ float bf2f(u16 h) { return __uint_as_float((uint32_t)h << 16); }
+
+// fp32 -> bf16 bits, round to nearest even (NaN stays NaN).
+__device__ __forceinline__ u16 f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u16)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (u16)(u >> 16);
+}
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+  return (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);
+}
+
+// 8 consecutive elements (one 16-byte bf16 chunk, or two 16-byte fp32 chunks)
+// loaded as fp32.
+template <bool BF16>
+__device__ __forceinline__ void load8(const void* base, long elem, float v[8]) {
+  if (BF16) {
+    uint4 u = *reinterpret_cast<const uint4*>(reinterpret_cast<const u16*>(base) + elem);
+    v[0] = bf_lo(u.x); v[1] = bf_hi(u.x); v[2] = bf_lo(u.y); v[3] = bf_hi(u.y);
+    v[4] = bf_lo(u.z); v[5] = bf_hi(u.z); v[6] = bf_lo(u.w); v[7] = bf_hi(u.w);
+  } else {
+    const float4* p = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(base) + elem);
+    float4 a = p[0], b = p[1];
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  }
+}
+
+template <bool BF16>
+__device__ __forceinline__ void store8(void* base, long elem, const float v[8]) {
+  if (BF16) {
+    uint4 u;
+    u.x = pack2(v[0], v[1]); u.y = pack2(v[2], v[3]);
+    u.z = pack2(v[4], v[5]); u.w = pack2(v[6], v[7]);
+    *reinterpret_cast<uint4*>(reinterpret_cast<u16*>(base) + elem) = u;
+  } else {
+    float4* p = reinterpret_cast<float4*>(reinterpret_cast<float*>(base) + elem);
+    p[0] = make_float4(v[0], v[1], v[2], v[3]);
+    p[1] = make_float4(v[4], v[5], v[6], v[7]);
+  }
+}
+
+template <bool BF16>
+__device__ __forceinline__ float load1(const void* base, long elem) {
+  if (BF16) return bf2f(reinterpret_cast<const u16*>(base)[elem]);
+  return reinterpret_cast<const float*>(base)[elem];
+}
+
+template <bool BF16>
+__device__ __forceinline__ void store1(void* base, long elem, float v) {
+  if (BF16) reinterpret_cast<u16*>(base)[elem] = f2bf(v);
+  else reinterpret_cast<float*>(base)[elem] = v;
+}
+
+// ---------------------------------------------------------------- readiness
+// Query at absolute position t sees pool entries w < min(T, floor((t+1)/m)).
+__device__ __forceinline__ int ready_count(long t, int m, int T) {
+  if (t + 1 <= 0) return 0;
+  long r = (t + 1) / m;
+  return r > T ? T : (int)r;
+}
+
+// ---------------------------------------------------------------- matrix cores
+__device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
+
+// ---------------------------------------------------------------- misc
+__device__ __forceinline__ float shfl_xor(float v, int mask) { return __shfl_xor(v, mask, 64); }
+
+}  // namespace csa
+
+// ------------------------------------------------------------------------
+// Host-side launchers (defined in the kernel sources, called by csa_api.hip).
+// Each returns hipSuccess or the launch error.
+namespace csa {
+
+hipError_t launch_rope_table(float* cs, int n_pos, int rope_dim, double theta,
+                             hipStream_t s);
+
+hipError_t launch_compress(const void* x, const void* gate, const float* slot_bias,
+                           void* pool, int B, int S, int D, int m, int overlap,
+                           int rope_dim, const float* cs, int pos0, bool bf16,
+                           hipStream_t s);
+
+hipError_t launch_index_scores(const void* q_idx, const float* w_idx, const void* k_pool,
+                               float* scores, const int* q_pos, int B, int S, int T,
+                               int n_heads, int head_dim, int m, bool bf16,
+                               hipStream_t s);
+
+hipError_t launch_topk(const float* scores, int* idx, const int* q_pos, int B, int S,
+                       int T, int k, int m, hipStream_t s);
+
+struct AttnParams {
+  const void* q;          // [B][S][H][D]
+  const void* kv_win;     // [B][L_win][D]
+  const int* win_pos0;    // [B]
+  int L_win;
+  const void* pool;       // [B][T][D]
+  int T;
+  const int* idx;         // [B][S][k] selected entries (CSA / DSA); unused when dense
+  int k;
+  int dense;              // 1: pool slots are all ready entries w < R(t) (HCA)
+  int m;                  // readiness rate of the dense mode
+  const float* sink;      // [H] or nullptr
+  void* out;              // [B][S][H][dv]
+  const int* q_pos;       // [B]
+  int B, S, H, D, dv, rope_dim;
+  const float* cs;        // [n_pos][rope_dim/2][2]
+  int n_pos;
+  int window;
+  float scale;
+  bool bf16;
+};
+
+// Plan for splitting a row's key slots over several workgroups.
+struct AttnPlan {
+  int kernel;             // 0 = generic, 1 = bf16 matrix-core kernel
+  int nsplit;             // workgroups per query row (1 = no split)
+  int tiles_per_split;
+  size_t ws_bytes;        // workspace the split needs
+};
+
+// max_rows: the larger of L_win and T (rows of one sequence a gather addresses)
+AttnPlan plan_attention(int B, int S, int H, int D, int dv, int rope_dim, int max_slots,
+                        bool bf16, long max_rows);
+hipError_t launch_attention(const AttnParams& p, const AttnPlan& plan, void* ws,
+                            hipStream_t s);
+
+}  // namespace csa

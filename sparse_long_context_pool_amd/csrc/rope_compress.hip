@@ -1,0 +1,176 @@
+// rope_compress.hip -- RoPE cos/sin table and the window compressor.
+//
+// Page "DeepSeek-V4", section "Hybrid attention (§2.3)": partial RoPE with
+// interleaved pairs on the trailing qk_rope_head_dim channels; the CSA pool
+// compresses K=V at rate m with overlapping windows, the HCA pool at rate m'
+// with non-overlapping windows.  Section "Cache layers": the compressor keeps
+// overlap state for CSA and runs a parallel compressor at index_head_dim for
+// the indexer keys.
+//
+// The compressor is HBM-bound (it reads each token row of x and gate once and
+// writes one row per m tokens).  One workgroup owns one entry; its four
+// wavefronts split the window rows, each lane owns 8 consecutive channels
+// (one 16-byte bf16 load per row), and every lane keeps an online softmax per
+// channel.  The four partial states merge through LDS, and the RoPE pair
+// rotation is applied to the merged entry before the store.
+#include "csa_device.hpp"
+
+namespace csa {
+namespace {
+
+__global__ __launch_bounds__(256) void rope_table_kernel(float2* __restrict__ cs, int n_pos,
+                                                         int rope_dim, double theta) {
+  const int half = rope_dim / 2;
+  const long n = (long)n_pos * half;
+  for (long e = blockIdx.x * (long)blockDim.x + threadIdx.x; e < n;
+       e += (long)gridDim.x * blockDim.x) {
+    const long p = e / half;
+    const int i = (int)(e - p * half);
+    const double freq = pow(theta, -2.0 * (double)i / (double)rope_dim);
+    const double ang = (double)p * freq;
+    cs[e] = make_float2((float)cos(ang), (float)sin(ang));
+  }
+}
+
+constexpr int kCompressWaves = 4;
+constexpr int kMaxChunksPerLane = 2;  // D <= 64 lanes * 2 chunks * 8 channels
+
+template <bool BF16>
+__global__ __launch_bounds__(256) void compress_kernel(
+    const void* __restrict__ x, const void* __restrict__ gate,
+    const float* __restrict__ slot_bias, void* __restrict__ pool, int S, int D, int m,
+    int overlap, int rope_dim, const float2* __restrict__ cs, int pos0) {
+  extern __shared__ float smem[];  // [waves][3][D]: running max, sum, weighted sum
+  const int T = S / m;
+  const int w = blockIdx.x;
+  const int b = blockIdx.y;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int nchunk = D >> 3;
+
+  const long first = (long)(w - overlap) * m;  // token held by slot 0
+  const long j0 = first < 0 ? 0 : first;
+  const long j1 = (long)(w + 1) * m;
+  const long row0 = (long)b * S;
+
+  float mx[kMaxChunksPerLane][8], sm[kMaxChunksPerLane][8], ac[kMaxChunksPerLane][8];
+#pragma unroll
+  for (int cc = 0; cc < kMaxChunksPerLane; ++cc)
+#pragma unroll
+    for (int v = 0; v < 8; ++v) { mx[cc][v] = -INFINITY; sm[cc][v] = 0.f; ac[cc][v] = 0.f; }
+
+  for (long j = j0 + wave; j < j1; j += kCompressWaves) {
+#pragma unroll
+    for (int cc = 0; cc < kMaxChunksPerLane; ++cc) {
+      const int ch = lane + 64 * cc;
+      if (ch >= nchunk) break;
+      float xv[8], a[8];
+      load8<BF16>(x, (row0 + j) * D + ch * 8, xv);
+      if (gate) {
+        load8<BF16>(gate, (row0 + j) * D + ch * 8, a);
+      } else {
+#pragma unroll
+        for (int v = 0; v < 8; ++v) a[v] = 0.f;
+      }
+      if (slot_bias) {
+        const float4* sb = reinterpret_cast<const float4*>(slot_bias + (j - first) * D + ch * 8);
+        float4 s0 = sb[0], s1 = sb[1];
+        a[0] += s0.x; a[1] += s0.y; a[2] += s0.z; a[3] += s0.w;
+        a[4] += s1.x; a[5] += s1.y; a[6] += s1.z; a[7] += s1.w;
+      }
+#pragma unroll
+      for (int v = 0; v < 8; ++v) {
+        // online softmax: keep (max, sum e^(a-max), sum e^(a-max) x)
+        if (a[v] > mx[cc][v]) {
+          const float r = __expf(mx[cc][v] - a[v]);
+          sm[cc][v] = sm[cc][v] * r + 1.f;
+          ac[cc][v] = ac[cc][v] * r + xv[v];
+          mx[cc][v] = a[v];
+        } else {
+          const float e = __expf(a[v] - mx[cc][v]);
+          sm[cc][v] += e;
+          ac[cc][v] += e * xv[v];
+        }
+      }
+    }
+  }
+
+  float* st = smem + wave * 3 * D;
+#pragma unroll
+  for (int cc = 0; cc < kMaxChunksPerLane; ++cc) {
+    const int ch = lane + 64 * cc;
+    if (ch >= nchunk) break;
+#pragma unroll
+    for (int v = 0; v < 8; ++v) {
+      st[ch * 8 + v] = mx[cc][v];
+      st[D + ch * 8 + v] = sm[cc][v];
+      st[2 * D + ch * 8 + v] = ac[cc][v];
+    }
+  }
+  __syncthreads();
+
+  // merge the wave states; thread owns a channel pair (2p, 2p+1)
+  const int rope_base = D - rope_dim;
+  const long out_row = ((long)b * T + w) * D;
+  for (int p = threadIdx.x; p < (D >> 1); p += blockDim.x) {
+    float val[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int c = 2 * p + u;
+      float M = -INFINITY;
+#pragma unroll
+      for (int q = 0; q < kCompressWaves; ++q) M = fmaxf(M, smem[q * 3 * D + c]);
+      float den = 0.f, num = 0.f;
+#pragma unroll
+      for (int q = 0; q < kCompressWaves; ++q) {
+        const float mq = smem[q * 3 * D + c];
+        if (mq == -INFINITY) continue;  // wave saw no row of this window
+        const float f = __expf(mq - M);
+        den += f * smem[q * 3 * D + D + c];
+        num += f * smem[q * 3 * D + 2 * D + c];
+      }
+      val[u] = num / den;
+    }
+    if (2 * p >= rope_base) {
+      const int i = (2 * p - rope_base) >> 1;
+      const float2 r = cs[((long)pos0 + (long)w * m) * (rope_dim >> 1) + i];
+      const float a0 = val[0], a1 = val[1];
+      val[0] = a0 * r.x - a1 * r.y;
+      val[1] = a0 * r.y + a1 * r.x;
+    }
+    store1<BF16>(pool, out_row + 2 * p, val[0]);
+    store1<BF16>(pool, out_row + 2 * p + 1, val[1]);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_rope_table(float* cs, int n_pos, int rope_dim, double theta,
+                             hipStream_t s) {
+  const long n = (long)n_pos * (rope_dim / 2);
+  long blocks = (n + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  hipLaunchKernelGGL(rope_table_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
+                     reinterpret_cast<float2*>(cs), n_pos, rope_dim, theta);
+  return hipGetLastError();
+}
+
+hipError_t launch_compress(const void* x, const void* gate, const float* slot_bias,
+                           void* pool, int B, int S, int D, int m, int overlap,
+                           int rope_dim, const float* cs, int pos0, bool bf16,
+                           hipStream_t s) {
+  const int T = S / m;
+  if (T == 0 || B == 0) return hipSuccess;
+  const size_t lds = (size_t)kCompressWaves * 3 * D * sizeof(float);
+  dim3 grid(T, B);
+  if (bf16)
+    hipLaunchKernelGGL(compress_kernel<true>, grid, dim3(256), lds, s, x, gate, slot_bias,
+                       pool, S, D, m, overlap, rope_dim,
+                       reinterpret_cast<const float2*>(cs), pos0);
+  else
+    hipLaunchKernelGGL(compress_kernel<false>, grid, dim3(256), lds, s, x, gate, slot_bias,
+                       pool, S, D, m, overlap, rope_dim,
+                       reinterpret_cast<const float2*>(cs), pos0);
+  return hipGetLastError();
+}
+
+}  // namespace csa

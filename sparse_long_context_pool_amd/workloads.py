@@ -51,8 +51,11 @@ class Workload:
 
     @property
     def n_pos(self) -> int:
-        """RoPE table length covering every position used."""
-        return self.q_pos0 + max(self.S, self.ctx) + 1
+        """RoPE table length covering every position used (queries; and the
+        tokens and entries the compressor rotates when caches are built here)."""
+        if self.decode:
+            return self.q_pos0 + self.S
+        return max(self.q_pos0 + self.S, self.ctx)
 
     def with_(self, **kw) -> "Workload":
         return replace(self, **kw)

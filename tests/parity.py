@@ -1,0 +1,228 @@
+"""Helpers of the GPU parity tests: seeded inputs for both sides, the oracle
+pipeline over chosen query rows, and the comparison rules.
+
+Rules (the tolerances the tests use):
+  * bf16 attention outputs: max |gpu - oracle| <= 2e-2; fp32 path: <= 1e-4.
+  * top-k on identical fp32 scores: bit-exact.
+  * top-k after independently computed scores: equal set sizes, and every
+    entry in which the two sets differ has an oracle score within
+    1e-3 * max(1, |s_k|) of the oracle's k-th score s_k (a near tie).
+  * index scores: |gpu - oracle| <= 1e-5 * sum_j |w_j| sum_c |q_jc k_c| + 1e-6,
+    a summation-order bound (products of bf16 values are exact in fp32).
+  * compressed rows: within one bf16 ulp (2^-7 relative) or 1e-5 relative for
+    fp32 (different summation order and exp evaluation).
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle
+from sparse_long_context_pool_amd import synth
+from sparse_long_context_pool_amd.workloads import Workload
+
+BF16_ATOL = 2e-2
+F32_ATOL = 1e-4
+
+
+def tdt(wl: Workload):
+    return torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+
+
+def dev(a: np.ndarray, dtype) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a)).to(dtype).cuda()
+
+
+def host(t: torch.Tensor) -> np.ndarray:
+    return t.float().cpu().numpy()
+
+
+class Inputs:
+    """All seeded inputs of a workload as fp32 numpy arrays (bf16 values for
+    bf16 workloads).  Large tensors are only materialised on demand."""
+
+    def __init__(self, wl: Workload, seed: int = 0):
+        self.wl, self.seed = wl, seed
+        self.bf16 = wl.dtype == "bf16"
+
+    def get(self, name, rows=None):
+        wl, s, a = self.wl, self.seed, self.wl.act_scale
+        B, S, H, D = wl.B, wl.S, wl.H, wl.D
+        spec = {
+            "q": (B * S, (H, D), a),
+            "x": (B * wl.ctx, (D,), a),
+            "gate": (B * wl.ctx, (D,), a),
+            "x_idx": (B * wl.ctx, (wl.idx_dim,), a),
+            "gate_idx": (B * wl.ctx, (wl.idx_dim,), a),
+            "q_idx": (B * S, (wl.n_idx_heads, wl.idx_dim), a),
+            "w_idx": (B * S, (wl.n_idx_heads,), a),
+            "pool": (B * wl.T, (D,), a),
+            "k_idx": (B * wl.T, (wl.idx_dim,), a),
+            "kv_win": (B * wl.window, (D,), a),
+        }
+        if name == "sink":
+            return synth.normal(s, "sink", wl.H, (), scale=1.0) if wl.sink else None
+        n, shape, sc = spec[name]
+        bf = self.bf16 and name != "w_idx"
+        return synth.normal(s, name, n, shape, scale=sc, rows=rows, bf16=bf)
+
+    def get_torch(self, name):
+        """Whole tensor straight into a device tensor of the workload dtype."""
+        wl, a = self.wl, self.wl.act_scale
+        B, S, H, D = wl.B, wl.S, wl.H, wl.D
+        spec = {
+            "q": (B * S, (H, D)), "x": (B * wl.ctx, (D,)), "gate": (B * wl.ctx, (D,)),
+            "x_idx": (B * wl.ctx, (wl.idx_dim,)), "gate_idx": (B * wl.ctx, (wl.idx_dim,)),
+            "q_idx": (B * S, (wl.n_idx_heads, wl.idx_dim)), "w_idx": (B * S, (wl.n_idx_heads,)),
+            "pool": (B * wl.T, (D,)), "k_idx": (B * wl.T, (wl.idx_dim,)),
+            "kv_win": (B * wl.window, (D,)),
+        }
+        n, shape = spec[name]
+        dt = torch.float32 if (name == "w_idx" or not self.bf16) else torch.bfloat16
+        return synth.normal_torch(self.seed, name, n, shape, scale=a, dtype=dt).cuda()
+
+
+def row_positions(wl: Workload, rows) -> np.ndarray:
+    rows = np.asarray(rows)
+    return wl.q_pos0 + rows % wl.S
+
+
+# ---------------------------------------------------------------- oracle side
+def oracle_caches(wl: Workload, inp: Inputs, b: int = 0):
+    """Oracle window rows, pool and index keys of sequence b (fp32, rounded to
+    bf16 where the GPU stores bf16)."""
+    rb = wl.dtype == "bf16"
+    if wl.decode:
+        sl = slice(b * wl.T, (b + 1) * wl.T)
+        pool = inp.get("pool", rows=np.arange(sl.start, sl.stop))
+        k_idx = inp.get("k_idx", rows=np.arange(sl.start, sl.stop))
+        kv_win = inp.get("kv_win", rows=np.arange(b * wl.window, (b + 1) * wl.window))
+        return kv_win, wl.q_pos0 - wl.window + 1, pool, k_idx
+    rows = np.arange(b * wl.ctx, (b + 1) * wl.ctx)
+    x = inp.get("x", rows=rows)
+    gate = inp.get("gate", rows=rows) if wl.kind != "dsa" else None
+    kv_win = oracle.compress(x, None, None, m=1, overlap=0, rope_dim=wl.rope_dim,
+                             theta=wl.theta, pos0=0, round_bf16=rb)
+    if wl.kind == "dsa":
+        pool = kv_win
+    else:
+        pool = oracle.compress(x, gate, None, m=wl.m, overlap=wl.overlap,
+                               rope_dim=wl.rope_dim, theta=wl.theta, pos0=0, round_bf16=rb)
+    k_idx = None
+    if wl.n_idx_heads:
+        xi = inp.get("x_idx", rows=rows)
+        gi = inp.get("gate_idx", rows=rows) if wl.kind != "dsa" else None
+        k_idx = oracle.compress(xi, gi, None, m=wl.m, overlap=wl.overlap, round_bf16=rb)
+    return (kv_win if wl.window else None), 0, pool, k_idx
+
+
+def oracle_rows(wl: Workload, inp: Inputs, rows, caches=None, idx_override=None):
+    """Oracle scores / idx / out for global query rows (all in one sequence)."""
+    rows = np.asarray(rows)
+    b = int(rows[0]) // wl.S
+    assert np.all(rows // wl.S == b)
+    kv_win, win_pos0, pool, k_idx = caches or oracle_caches(wl, inp, b)
+    t = row_positions(wl, rows)
+    res = {"t": t}
+    idx = None
+    if wl.n_idx_heads:
+        sc = oracle.index_scores(inp.get("q_idx", rows=rows), inp.get("w_idx", rows=rows), t,
+                                 k_idx, m=wl.m)
+        res["scores"] = sc
+        idx = oracle.topk(sc, t, k=wl.topk, m=wl.m)
+        res["idx"] = idx
+    if idx_override is not None:
+        idx = idx_override
+    q = inp.get("q", rows=rows)
+    res["out"] = oracle.attention(q, t, kv_win=kv_win, win_pos0=win_pos0, window=wl.window,
+                                  pool=pool, idx=idx, m=wl.m, sink=inp.get("sink"),
+                                  rope_dim=wl.rope_dim, theta=wl.theta, scale=wl.scale,
+                                  dv=wl.dv)
+    return res
+
+
+# ---------------------------------------------------------------- GPU side
+def gpu_pipeline(wl: Workload, inp: Inputs, ops, keep_intermediates=True):
+    """Run the whole hot path on the GPU through the C ABI; returns tensors."""
+    dt = tdt(wl)
+    B, S = wl.B, wl.S
+    r = {}
+    r["cs"] = cs = ops.csa_rope_table(wl.n_pos, wl.rope_dim, wl.theta)
+    q_pos = torch.full((B,), wl.q_pos0, dtype=torch.int32, device="cuda")
+    r["q_pos"] = q_pos
+    if wl.decode:
+        pool = inp.get_torch("pool").view(B, wl.T, wl.D)
+        k_idx = inp.get_torch("k_idx").view(B, wl.T, wl.idx_dim)
+        kv_win = inp.get_torch("kv_win").view(B, wl.window, wl.D)
+        win_pos0 = torch.full((B,), wl.q_pos0 - wl.window + 1, dtype=torch.int32,
+                              device="cuda")
+    else:
+        x = inp.get_torch("x").view(B, wl.ctx, wl.D)
+        kv_win = ops.csa_compress(x, m=1, overlap=0, rope_dim=wl.rope_dim, cs=cs, pos0=0)
+        if wl.kind == "dsa":
+            pool = kv_win
+        else:
+            gate = inp.get_torch("gate").view(B, wl.ctx, wl.D)
+            pool = ops.csa_compress(x, gate, m=wl.m, overlap=wl.overlap, rope_dim=wl.rope_dim,
+                                    cs=cs, pos0=0)
+            del gate
+        del x
+        k_idx = None
+        if wl.n_idx_heads:
+            xi = inp.get_torch("x_idx").view(B, wl.ctx, wl.idx_dim)
+            gi = None if wl.kind == "dsa" else inp.get_torch("gate_idx").view(B, wl.ctx,
+                                                                              wl.idx_dim)
+            k_idx = ops.csa_compress(xi, gi, m=wl.m, overlap=wl.overlap)
+        win_pos0 = torch.zeros((B,), dtype=torch.int32, device="cuda")
+        if not wl.window:
+            kv_win = None
+    r.update(kv_win=kv_win, win_pos0=win_pos0, pool=pool, k_idx=k_idx)
+    q = inp.get_torch("q").view(B, S, wl.H, wl.D)
+    sink = inp.get("sink")
+    sink_t = None if sink is None else dev(sink, torch.float32)
+    if wl.n_idx_heads:
+        q_idx = inp.get_torch("q_idx").view(B, S, wl.n_idx_heads, wl.idx_dim)
+        w_idx = inp.get_torch("w_idx").view(B, S, wl.n_idx_heads)
+        scores = ops.csa_index_scores(q_idx, w_idx, k_idx, q_pos, m=wl.m)
+        idx = ops.csa_topk(scores, q_pos, k=wl.topk, m=wl.m)
+        r.update(scores=scores, idx=idx)
+        r["out"] = ops.csa_sparse_attn(q, kv_win, win_pos0, pool, idx, sink_t, q_pos,
+                                       rope_dim=wl.rope_dim, cs=cs, window=wl.window,
+                                       scale=wl.scale, dv=wl.dv)
+    else:
+        r["out"] = ops.hca_attn(q, kv_win, win_pos0, pool, sink_t, q_pos, m=wl.m,
+                                rope_dim=wl.rope_dim, cs=cs, window=wl.window,
+                                scale=wl.scale, dv=wl.dv)
+    torch.cuda.synchronize()
+    return r
+
+
+# ---------------------------------------------------------------- comparisons
+def assert_idx_rows_equivalent(gpu_idx, orc_idx, orc_scores, t, k, m, T, tol=1e-3):
+    """Top-k sets equal, or different only by near ties of the oracle scores.
+    Returns the mask of rows whose sets are identical."""
+    same = np.zeros(len(t), bool)
+    for r in range(len(t)):
+        R = oracle.ready_count(int(t[r]), m, T)
+        g, o = gpu_idx[r], orc_idx[r]
+        n = min(k, R)
+        assert np.all(g[n:] == -1) and np.all(g[:n] >= 0), f"row {r}: bad padding"
+        assert np.all(np.diff(g[:n]) > 0), f"row {r}: not ascending"
+        gs, os_ = set(g[:n].tolist()), set(o[:n].tolist())
+        if gs == os_:
+            same[r] = True
+            continue
+        sk = np.sort(orc_scores[r, :R])[::-1][n - 1]
+        for w in gs ^ os_:
+            assert abs(orc_scores[r, w] - sk) <= tol * max(1.0, abs(sk)), \
+                f"row {r}: entry {w} score {orc_scores[r, w]} is not a near tie of {sk}"
+    return same
+
+
+def score_bound(q_idx, w_idx, k_idx, rows_t, m):
+    """Per-element summation-order error bound of the index scores."""
+    T = k_idx.shape[0]
+    absprod = np.einsum("njc,wc->njw", np.abs(q_idx).astype(np.float64),
+                        np.abs(k_idx).astype(np.float64))
+    tot = np.einsum("nj,njw->nw", np.abs(w_idx).astype(np.float64), absprod)
+    return 1e-5 * tot + 1e-6

@@ -1,0 +1,91 @@
+"""The C-ABI library loads, exports every entry point include/csa.h declares,
+and rejects invalid arguments on the host -- all without touching a GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "csa.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(?:csa_status_t|size_t|const char \*)\s*\**\s*(\w+)\s*\(",
+                                 text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    from sparse_long_context_pool_amd import csa
+    return csa.lib()
+
+
+def test_header_declares_the_hot_path():
+    names = declared_functions()
+    for n in ("csa_rope_table", "csa_compress", "csa_index_scores", "csa_topk",
+              "csa_sparse_attn", "hca_attn", "csa_last_error"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(L):
+    for name in declared_functions():
+        assert hasattr(L, name), name
+    from sparse_long_context_pool_amd import csa
+    assert set(csa.EXPORTS) == set(declared_functions())
+    assert b"gfx950" in L.csa_version()
+
+
+def test_invalid_arguments_are_rejected_on_the_host(L):
+    nul = None
+    # unknown dtype
+    assert L.csa_compress(nul, nul, nul, nul, 1, 8, 8, 4, 1, 0, nul, 0, 0, 7, nul) == 1
+    assert b"dtype" in L.csa_last_error()
+    # D not a multiple of 8
+    assert L.csa_compress(nul, nul, nul, nul, 1, 8, 12, 4, 1, 0, nul, 0, 0, 1, nul) == 1
+    # odd rope_dim
+    assert L.csa_compress(nul, nul, nul, nul, 1, 8, 16, 4, 1, 3, nul, 0, 0, 1, nul) == 1
+    # missing tensors
+    assert L.csa_compress(nul, nul, nul, nul, 1, 8, 16, 4, 1, 0, nul, 0, 0, 1, nul) == 1
+    assert b"required" in L.csa_last_error()
+    # RoPE positions beyond the table
+    fake = ctypes.c_void_p(0x10000)
+    assert L.csa_compress(fake, nul, nul, fake, 1, 64, 16, 4, 1, 8, fake, 10, 0, 1, nul) == 1
+    assert b"RoPE table" in L.csa_last_error()
+    # misaligned pointer
+    odd = ctypes.c_void_p(0x10002)
+    assert L.csa_compress(odd, nul, nul, fake, 1, 64, 16, 4, 1, 0, nul, 0, 0, 1, nul) == 1
+    assert b"aligned" in L.csa_last_error()
+    # index scores: k must be >= 1 for top-k, bad sizes
+    assert L.csa_topk(nul, nul, nul, 1, 4, 16, 0, 4, nul) == 1
+    assert L.csa_index_scores(nul, nul, nul, nul, nul, 1, 4, 16, 0, 32, 4, 1, nul) == 1
+    assert L.csa_index_scores(nul, nul, nul, nul, nul, 1, 4, 16, 2, 30, 4, 1, nul) == 1
+    # attention: dv must be D or D - rope_dim
+    args = [fake, fake, fake, 8, fake, 4, fake, 2, nul, fake, fake, 1, 4, 4, 64, 50, 16,
+            fake, 100, 8, ctypes.c_float(0.125), nul, ctypes.c_size_t(0), 1, nul]
+    assert L.csa_sparse_attn(*args) == 1
+    assert b"dv" in L.csa_last_error()
+    args[15] = 48          # D - rope_dim: accepted shape-wise, but a zero scale is not
+    args[20] = ctypes.c_float(0.0)
+    assert L.csa_sparse_attn(*args) == 1
+    assert b"scale" in L.csa_last_error()
+    # hca: m must be >= 1
+    hargs = [fake, fake, fake, 8, fake, 4, 0, nul, fake, fake, 1, 4, 4, 64, 64, 16, fake, 100,
+             8, ctypes.c_float(0.125), nul, ctypes.c_size_t(0), 1, nul]
+    assert L.hca_attn(*hargs) == 1
+    # empty work is OK and enqueues nothing
+    assert L.csa_topk(nul, nul, nul, 0, 4, 16, 2, 4, nul) == 0
+    assert L.csa_compress(nul, nul, nul, nul, 1, 3, 16, 4, 1, 0, nul, 0, 0, 1, nul) == 0
+
+
+def test_workspace_plans(L):
+    # decode shape: few rows, many keys -> split over workgroups, workspace > 0
+    ws = L.csa_sparse_attn_workspace_size(64, 1, 64, 512, 512, 64, 2048, 128, 1)
+    assert ws > 0 and ws % (64 * 64 * 514 * 4) == 0
+    # prefill shape: enough rows -> no split
+    assert L.csa_sparse_attn_workspace_size(1, 8192, 64, 512, 512, 64, 512, 128, 1) == 0
+    # fp32 never splits
+    assert L.csa_sparse_attn_workspace_size(1, 4, 4, 64, 64, 16, 16, 32, 0) == 0
+    assert L.hca_attn_workspace_size(1, 2, 64, 512, 512, 64, 512, 128, 1) > 0

@@ -1,0 +1,104 @@
+"""End-to-end GPU parity of the whole hot path against the CPU oracle.
+
+The tiny fp32 CSA workload is compared everywhere.  The four bf16 workloads
+run at their full sizes, in the launch configuration the benchmark times, and
+sampled query rows (first, last and spread over the sequence) are recomputed
+one by one by the oracle from the same seeded inputs."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from parity import (BF16_ATOL, F32_ATOL, Inputs, assert_idx_rows_equivalent, gpu_pipeline,
+                    host, oracle_caches, oracle_rows, row_positions)
+from sparse_long_context_pool_amd.workloads import WORKLOADS
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def ops():
+    from sparse_long_context_pool_amd import csa
+    assert torch.cuda.is_available()
+    return csa
+
+
+def _sample_rows(wl, n, seed=0):
+    S = wl.S
+    base = [0, 1, 2, 3, 4, 5, 7, S // 4, S // 2, S - 2, S - 1]
+    r = np.random.default_rng(seed).integers(0, S, n)
+    rows = sorted(set(i for i in base + r.tolist() if 0 <= i < S))
+    return np.array(rows)
+
+
+def _check_caches(wl, inp, g, caches, b):
+    kv_win, _, pool, k_idx = caches
+    rel = 2.0 ** -7 if wl.dtype == "bf16" else 1e-5
+    if not wl.decode:
+        if kv_win is not None:
+            np.testing.assert_allclose(host(g["kv_win"][b]), kv_win, rtol=rel, atol=1e-5)
+        np.testing.assert_allclose(host(g["pool"][b]), pool, rtol=rel, atol=1e-5)
+        if k_idx is not None:
+            np.testing.assert_allclose(host(g["k_idx"][b]), k_idx, rtol=rel, atol=1e-5)
+
+
+def _compare_rows(wl, g, res, b, rows_local):
+    tol = BF16_ATOL if wl.dtype == "bf16" else F32_ATOL
+    same = np.ones(len(rows_local), bool)
+    if wl.n_idx_heads:
+        gi = host(g["idx"][b]).astype(np.int32)[rows_local]
+        same = assert_idx_rows_equivalent(gi, res["idx"], res["scores"], res["t"], wl.topk,
+                                          wl.m, wl.T)
+        gs = host(g["scores"][b])[rows_local]
+        for r, t in enumerate(res["t"]):
+            R = oracle.ready_count(int(t), wl.m, wl.T)
+            d = np.abs(gs[r, :R] - res["scores"][r, :R])
+            assert np.all(d <= 2e-4 * np.abs(res["scores"][r, :R]) + 2e-3), (r, float(d.max()))
+    go = host(g["out"][b])[rows_local]
+    err = np.abs(go[same] - res["out"][same]).max() if same.any() else 0.0
+    assert err <= tol, float(err)
+    assert same.mean() >= 0.9
+    return err
+
+
+def test_tiny_csa_f32_end_to_end(ops):
+    wl = WORKLOADS["tiny_csa_f32"]
+    inp = Inputs(wl)
+    g = gpu_pipeline(wl, inp, ops)
+    caches = oracle_caches(wl, inp, 0)
+    _check_caches(wl, inp, g, caches, 0)
+    rows = np.arange(wl.S)
+    res = oracle_rows(wl, inp, rows, caches)
+    # with fp32 scores the GPU's index sets equal the oracle's
+    gi = host(g["idx"][0]).astype(np.int32)
+    same = assert_idx_rows_equivalent(gi, res["idx"], res["scores"], res["t"], wl.topk, wl.m,
+                                      wl.T, tol=1e-5)
+    assert same.mean() >= 0.99
+    err = np.abs(host(g["out"][0])[same] - res["out"][same]).max()
+    assert err <= F32_ATOL, float(err)
+    # the top-k kernel alone, fed the oracle's fp32 scores, is bit-exact
+    sc = torch.from_numpy(np.where(np.isfinite(res["scores"]), res["scores"], 0)).cuda()
+    idx = host(ops.csa_topk(sc[None].contiguous(), g["q_pos"], k=wl.topk, m=wl.m))
+    assert np.array_equal(idx[0].astype(np.int32), res["idx"])
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", ["csa_prefill_bf16", "hca_bf16", "csa_decode_bf16", "dsa_bf16"])
+def test_full_size_sampled(ops, name):
+    wl = WORKLOADS[name]
+    inp = Inputs(wl)
+    print(f"[{name}] GPU pipeline at full size", flush=True)
+    g = gpu_pipeline(wl, inp, ops)
+    if wl.decode:
+        seqs = [0, 1, 37, 63]
+        for b in seqs:
+            caches = oracle_caches(wl, inp, b)
+            res = oracle_rows(wl, inp, [b], caches)
+            _compare_rows(wl, g, res, b, [0])
+        return
+    caches = oracle_caches(wl, inp, 0)
+    _check_caches(wl, inp, g, caches, 0)
+    rows = _sample_rows(wl, 24)
+    print(f"[{name}] oracle on {len(rows)} sampled rows", flush=True)
+    res = oracle_rows(wl, inp, rows, caches)
+    _compare_rows(wl, g, res, 0, rows)

@@ -1,0 +1,243 @@
+"""GPU parity, stage by stage, against the CPU oracle on the same seeded
+inputs.  Each GPU stage receives the ORACLE's upstream tensors, so a stage is
+judged on its own.  Sizes span several tiles and end in ragged tails."""
+import math
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from parity import BF16_ATOL, F32_ATOL, dev, host
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def ops():
+    from sparse_long_context_pool_amd import csa
+    assert torch.cuda.is_available()
+    csa.lib()
+    return csa
+
+
+def rng(s):
+    return np.random.default_rng(s)
+
+
+def rnd(shape, seed, bf16, scale=1.0):
+    a = (rng(seed).standard_normal(shape) * scale).astype(np.float32)
+    return oracle.round_bf16(a) if bf16 else a
+
+
+# ------------------------------------------------------------------ RoPE table
+@pytest.mark.parametrize("theta,rope_dim", [(160000.0, 64), (10000.0, 64), (160000.0, 16)])
+def test_rope_table(ops, theta, rope_dim):
+    n = 131073
+    g = host(ops.csa_rope_table(n, rope_dim, theta))
+    o = oracle.rope_table(n, rope_dim, theta)
+    assert np.max(np.abs(g - o)) <= 1.2e-7
+
+
+# ------------------------------------------------------------------ compressor
+@pytest.mark.parametrize("bf16", [False, True])
+@pytest.mark.parametrize("m,ov,D,rope,gate,bias", [
+    (4, 1, 512, 64, True, False), (4, 1, 64, 16, True, True), (128, 0, 512, 64, True, False),
+    (1, 0, 576, 64, False, False), (1, 0, 128, 0, False, False), (8, 0, 96, 32, False, True),
+    (4, 1, 128, 0, True, False)])
+def test_compress(ops, bf16, m, ov, D, rope, gate, bias):
+    B = 2
+    S = 3 * m * 4 + 3 if m < 128 else 5 * 128 + 17       # ragged tail
+    x = rnd((B, S, D), 1, bf16)
+    g = rnd((B, S, D), 2, bf16) if gate else None
+    sb = rnd(((1 + ov) * m, D), 3, False) if bias else None
+    theta, pos0 = 160000.0, 12
+    dt = torch.bfloat16 if bf16 else torch.float32
+    cs = ops.csa_rope_table(pos0 + S + 1, max(rope, 2), theta) if rope else None
+    out = host(ops.csa_compress(dev(x, dt), None if g is None else dev(g, dt),
+                                None if sb is None else dev(sb, torch.float32), m=m,
+                                overlap=ov, rope_dim=rope, cs=cs, pos0=pos0))
+    for b in range(B):
+        ref = oracle.compress(x[b], None if g is None else g[b], sb, m=m, overlap=ov,
+                              rope_dim=rope, theta=theta, pos0=pos0, round_bf16=bf16)
+        rel = 2.0 ** -7 if bf16 else 1e-5
+        np.testing.assert_allclose(out[b], ref, rtol=rel, atol=1e-5)
+
+
+# ------------------------------------------------------------------ index scores
+def _score_bound(q, w, k):
+    tot = np.einsum("nj,njw->nw", np.abs(w).astype(np.float64),
+                    np.einsum("njc,wc->njw", np.abs(q).astype(np.float64),
+                              np.abs(k).astype(np.float64)))
+    return 1e-5 * tot + 1e-6
+
+
+@pytest.mark.parametrize("case", [
+    # (dtype, B, S, nI, cI, T, m, q_pos): the 64x128 bf16 shape runs on matrix cores
+    ("bf16", 2, 61, 64, 128, 300, 4, [0, 700]),     # prefill mode, ragged rows
+    ("bf16", 5, 1, 64, 128, 3000, 4, [12000, 11999, 3, 0, 40000]),  # decode mode
+    ("bf16", 1, 200, 64, 128, 200, 1, [0]),         # token level (m=1)
+    ("f32", 2, 33, 2, 32, 64, 4, [0, 100]),         # generic kernel
+    ("bf16", 1, 20, 4, 64, 50, 4, [150]),           # generic kernel, bf16
+])
+def test_index_scores(ops, case):
+    dt_s, B, S, nI, cI, T, m, qp = case
+    bf16 = dt_s == "bf16"
+    dt = torch.bfloat16 if bf16 else torch.float32
+    q = rnd((B, S, nI, cI), 10, bf16, 0.5)
+    w = rnd((B, S, nI), 11, False, 0.5)
+    k = rnd((B, T, cI), 12, bf16, 0.5)
+    q_pos = torch.tensor(qp, dtype=torch.int32, device="cuda")
+    sc = ops.csa_index_scores(dev(q, dt), dev(w, torch.float32), dev(k, dt), q_pos, m=m)
+    sc = host(sc)
+    for b in range(B):
+        t = qp[b] + np.arange(S)
+        ref = oracle.index_scores(q[b], w[b], t, k[b], m=m)
+        bound = _score_bound(q[b], w[b], k[b])
+        for i in range(S):
+            R = oracle.ready_count(int(t[i]), m, T)
+            if not bf16:  # fp32: same order, no fused multiply-add -> identical bits
+                assert np.array_equal(sc[b, i, :R], ref[i, :R]), (b, i)
+            d = np.abs(sc[b, i, :R] - ref[i, :R])
+            assert np.all(d <= bound[i, :R]), (b, i, float(d.max()))
+            assert not np.any(np.signbit(sc[b, i, :R]) & (sc[b, i, :R] == 0))
+
+
+# ------------------------------------------------------------------ top-k
+@pytest.mark.parametrize("T,k,m,qp,S", [
+    (64, 16, 4, [0, 120], 37), (2048, 512, 4, [0, 6000], 70), (2048, 512, 1, [1000, 1500], 20),
+    (32768, 2048, 4, [131071, 90000], 3), (40000, 2048, 1, [39990, 20000], 4),
+    (300, 300, 1, [0, 100], 9)])
+def test_topk_bit_exact(ops, T, k, m, qp, S):
+    B = 2
+    r = rng(T + k)
+    sc = r.standard_normal((B, S, T)).astype(np.float32)
+    # ties: exact zeros, signed zeros, repeated values, an all-equal row
+    sc[:, :, ::5] = 0.0
+    sc[:, :, 2::7] = -0.0
+    sc[:, :, 3::9] = 0.75
+    sc[0, S // 2, :] = -1.25
+    q_pos = torch.tensor(qp, dtype=torch.int32, device="cuda")
+    idx = host(ops.csa_topk(dev(sc, torch.float32), q_pos, k=k, m=m)).astype(np.int32)
+    for b in range(B):
+        t = qp[b] + np.arange(S)
+        ref = oracle.topk(sc[b], t, k=k, m=m)
+        assert np.array_equal(idx[b], ref), b
+
+
+# ------------------------------------------------------------------ attention
+def _attn_case(seed, B, S, H, D, dv, rope, T, k, window, m, qp, sink, bf16, dense):
+    r = rng(seed)
+    q = rnd((B, S, H, D), seed + 1, bf16)
+    L = max(qp) + S if window else 0
+    kv = rnd((B, L, D), seed + 2, bf16) if window else None
+    pool = rnd((B, T, D), seed + 3, bf16)
+    z = rnd((H,), seed + 4, False) if sink else None
+    idx = None
+    if not dense:
+        idx = np.full((B, S, k), -1, np.int32)
+        for b in range(B):
+            for i in range(S):
+                R = oracle.ready_count(qp[b] + i, m, T)
+                sel = np.sort(r.choice(R, size=min(k, R), replace=False)) if R else []
+                idx[b, i, :len(sel)] = sel
+    return q, kv, pool, z, idx
+
+
+ATTN_CASES = {
+    # name: (B, S, H, D, dv, rope, T, k, window, m, q_pos, sink, bf16, dense)
+    # >= 256 query rows x head groups run unsplit; fewer rows split their keys
+    "csa_mfma": (2, 150, 64, 512, 512, 64, 100, 48, 32, 4, [0, 300], True, True, False),
+    "csa_mfma_split": (2, 1, 64, 512, 512, 64, 700, 600, 128, 4, [2900, 5000], True, True,
+                       False),
+    "hca_mfma": (1, 300, 64, 512, 512, 64, 12, 0, 32, 8, [40], True, True, True),
+    "hca_mfma_split": (1, 2, 64, 512, 512, 64, 520, 0, 128, 128, [70000], True, True, True),
+    "dsa_mfma": (1, 150, 128, 576, 512, 64, 160, 40, 0, 1, [10], False, True, False),
+    "dsa_mfma_split": (1, 24, 128, 576, 512, 64, 80, 40, 0, 1, [40], False, True, False),
+    "small_mfma_split": (2, 50, 16, 64, 64, 16, 30, 20, 16, 4, [0, 64], True, True, False),
+    "small_mfma": (1, 300, 16, 64, 64, 16, 40, 20, 16, 4, [0], True, True, False),
+    "small_mfma_latent": (1, 33, 32, 96, 64, 32, 40, 12, 0, 1, [5], False, True, False),
+    "generic_f32": (2, 45, 4, 64, 64, 16, 64, 16, 32, 4, [0, 200], True, False, False),
+    "generic_bf16": (1, 30, 6, 40, 40, 8, 20, 8, 8, 4, [60], True, True, False),
+    "generic_hca_f32": (1, 40, 3, 32, 24, 8, 10, 0, 5, 4, [0], False, False, True),
+}
+
+
+@pytest.mark.parametrize("name", sorted(ATTN_CASES))
+def test_attention(ops, name):
+    B, S, H, D, dv, rope, T, k, window, m, qp, sink, bf16, dense = ATTN_CASES[name]
+    q, kv, pool, z, idx = _attn_case(zlib.crc32(name.encode()) % 1000, B, S, H, D, dv, rope, T, k, window,
+                                     m, qp, sink, bf16, dense)
+    theta = 160000.0
+    dt = torch.bfloat16 if bf16 else torch.float32
+    n_pos = max(qp) + S + 1
+    cs = ops.csa_rope_table(n_pos, rope, theta)
+    q_pos = torch.tensor(qp, dtype=torch.int32, device="cuda")
+    win_pos0 = torch.zeros(B, dtype=torch.int32, device="cuda")
+    kvd = dev(kv, dt) if kv is not None else None
+    zd = dev(z, torch.float32) if z is not None else None
+    scale = 1.0 / math.sqrt(D)
+    if dense:
+        out = ops.hca_attn(dev(q, dt), kvd, win_pos0, dev(pool, dt), zd, q_pos, m=m,
+                           rope_dim=rope, cs=cs, window=window, scale=scale, dv=dv)
+    else:
+        out = ops.csa_sparse_attn(dev(q, dt), kvd, win_pos0, dev(pool, dt), dev(idx, torch.int32),
+                                  zd, q_pos, rope_dim=rope, cs=cs, window=window, scale=scale,
+                                  dv=dv)
+    out = host(out)
+    tol = BF16_ATOL if bf16 else F32_ATOL
+    for b in range(B):
+        t = qp[b] + np.arange(S)
+        ref = oracle.attention(q[b], t, kv_win=None if kv is None else kv[b], win_pos0=0,
+                               window=window, pool=pool[b], idx=None if dense else idx[b],
+                               m=m, sink=z, rope_dim=rope, theta=theta, scale=scale, dv=dv)
+        err = np.abs(out[b] - ref).max()
+        assert err <= tol, (name, b, float(err))
+
+
+def test_attention_edge_rows(ops):
+    """Rows with nothing visible and no sink give zeros; a query position past
+    the RoPE table gives NaN; both on the matrix-core and the generic kernel."""
+    for (H, D, dv, rope, bf16) in [(64, 512, 512, 64, True), (4, 64, 64, 16, False)]:
+        B, S, T, k = 1, 3, 8, 4
+        dt = torch.bfloat16 if bf16 else torch.float32
+        q = dev(rnd((B, S, H, D), 5, bf16), dt)
+        pool = dev(rnd((B, T, D), 6, bf16), dt)
+        idx = torch.full((B, S, k), -1, dtype=torch.int32, device="cuda")
+        cs = ops.csa_rope_table(10, rope, 1e4)
+        q_pos = torch.tensor([2], dtype=torch.int32, device="cuda")
+        out = host(ops.csa_sparse_attn(q, None, None, pool, idx, None, q_pos, rope_dim=rope,
+                                       cs=cs, window=0, scale=0.1, dv=dv))
+        assert np.all(out == 0)
+        q_pos = torch.tensor([8], dtype=torch.int32, device="cuda")   # rows at t = 8, 9, 10
+        idx[..., 0] = 1
+        out = host(ops.csa_sparse_attn(q, None, None, pool, idx, None, q_pos, rope_dim=rope,
+                                       cs=cs, window=0, scale=0.1, dv=dv))
+        assert np.all(np.isfinite(out[0, :2])) and np.all(np.isnan(out[0, 2]))
+    # unsplit launch (many rows): rows past the table are NaN, the rest finite
+    H, D, rope = 64, 512, 64
+    S = 300
+    q = dev(rnd((1, S, H, D), 8, True), torch.bfloat16)
+    pool = dev(rnd((1, 8, D), 9, True), torch.bfloat16)
+    idx = torch.full((1, S, 4), -1, dtype=torch.int32, device="cuda")
+    idx[..., 0] = 2
+    cs = ops.csa_rope_table(250, rope, 1e4)
+    q_pos = torch.tensor([0], dtype=torch.int32, device="cuda")
+    out = host(ops.csa_sparse_attn(q, None, None, pool, idx, None, q_pos, rope_dim=rope, cs=cs,
+                                   window=0, scale=0.1))
+    assert np.all(np.isfinite(out[0, :250])) and np.all(np.isnan(out[0, 250:]))
+
+
+def test_attention_deterministic(ops):
+    B, S, H, D, dv, rope, T, k, window, m, qp, sink, bf16, dense = ATTN_CASES["csa_mfma_split"]
+    q, kv, pool, z, idx = _attn_case(7, B, S, H, D, dv, rope, T, k, window, m, qp, sink, bf16,
+                                     dense)
+    cs = ops.csa_rope_table(max(qp) + S + 1, rope, 160000.0)
+    args = (dev(q, torch.bfloat16), dev(kv, torch.bfloat16),
+            torch.zeros(B, dtype=torch.int32, device="cuda"), dev(pool, torch.bfloat16),
+            dev(idx, torch.int32), dev(z, torch.float32),
+            torch.tensor(qp, dtype=torch.int32, device="cuda"))
+    a = ops.csa_sparse_attn(*args, rope_dim=rope, cs=cs, window=window, scale=0.05)
+    b = ops.csa_sparse_attn(*args, rope_dim=rope, cs=cs, window=window, scale=0.05)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
