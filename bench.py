@@ -273,10 +273,10 @@ def roofline_of(wl_name, res):
 
 
 # ------------------------------------------------------------------ CPU baseline
-def cpu_baseline(WORKLOADS, synth, n_rows=512):
-    """The oracle on the prefill workload: full-sequence compression plus a
-    stratified sample of query rows (index scores, top-k, attention), scaled
-    to the whole sequence."""
+def cpu_baseline(WORKLOADS, synth, n_rows=8192):
+    """The oracle on the prefill workload: full-sequence compression plus evenly
+    spaced query rows (index scores, top-k, attention), scaled to the whole
+    sequence (with n_rows = S every row is computed and nothing is scaled)."""
     sys.path.insert(0, os.path.join(ROOT, "tests"))
     import oracle
     from parity import Inputs

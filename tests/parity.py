@@ -126,9 +126,12 @@ def oracle_rows(wl: Workload, inp: Inputs, rows, caches=None, idx_override=None)
     res = {"t": t}
     idx = None
     if wl.n_idx_heads:
-        sc = oracle.index_scores(inp.get("q_idx", rows=rows), inp.get("w_idx", rows=rows), t,
-                                 k_idx, m=wl.m)
+        qi, wi = inp.get("q_idx", rows=rows), inp.get("w_idx", rows=rows)
+        sc = oracle.index_scores(qi, wi, t, k_idx, m=wl.m)
         res["scores"] = sc
+        # sum_j |w_j| sum_c |q_jc| |k_c| per (row, entry): the scale of score errors
+        res["abs_terms"] = np.einsum("nj,njw->nw", np.abs(wi).astype(np.float64),
+                                     np.einsum("njc,wc->njw", np.abs(qi), np.abs(k_idx)))
         idx = oracle.topk(sc, t, k=wl.topk, m=wl.m)
         res["idx"] = idx
     if idx_override is not None:

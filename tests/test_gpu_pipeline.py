@@ -49,11 +49,15 @@ def _compare_rows(wl, g, res, b, rows_local):
         gi = host(g["idx"][b]).astype(np.int32)[rows_local]
         same = assert_idx_rows_equivalent(gi, res["idx"], res["scores"], res["t"], wl.topk,
                                           wl.m, wl.T)
+        # end to end, the GPU scores use the GPU's compressed index keys, which
+        # may differ from the oracle's by one bf16 ulp (2^-8 relative) per
+        # element: |dI| <= (2^-8 + 1e-5) * sum_j |w_j| sum_c |q_jc k_c|
         gs = host(g["scores"][b])[rows_local]
+        bound = (2.0 ** -8 + 1e-5) * res["abs_terms"] + 1e-6
         for r, t in enumerate(res["t"]):
             R = oracle.ready_count(int(t), wl.m, wl.T)
             d = np.abs(gs[r, :R] - res["scores"][r, :R])
-            assert np.all(d <= 2e-4 * np.abs(res["scores"][r, :R]) + 2e-3), (r, float(d.max()))
+            assert np.all(d <= bound[r, :R]), (r, float(d.max()))
     go = host(g["out"][b])[rows_local]
     err = np.abs(go[same] - res["out"][same]).max() if same.any() else 0.0
     assert err <= tol, float(err)
