@@ -130,8 +130,8 @@ def oracle_rows(wl: Workload, inp: Inputs, rows, caches=None, idx_override=None)
         sc = oracle.index_scores(qi, wi, t, k_idx, m=wl.m)
         res["scores"] = sc
         # sum_j |w_j| sum_c |q_jc| |k_c| per (row, entry): the scale of score errors
-        res["abs_terms"] = np.einsum("nj,njw->nw", np.abs(wi).astype(np.float64),
-                                     np.einsum("njc,wc->njw", np.abs(qi), np.abs(k_idx)))
+        per_head = np.matmul(np.abs(qi), np.abs(k_idx).T)          # [n, nI, T], BLAS
+        res["abs_terms"] = np.einsum("nj,njw->nw", np.abs(wi).astype(np.float64), per_head)
         idx = oracle.topk(sc, t, k=wl.topk, m=wl.m)
         res["idx"] = idx
     if idx_override is not None:
