@@ -29,6 +29,7 @@
 #include "csa_device.hpp"
 
 #include <algorithm>
+#include <type_traits>
 
 namespace csa {
 namespace {
@@ -149,50 +150,98 @@ __global__ __launch_bounds__(256) void attn_generic_kernel(AttnParams p) {
 }
 
 // ------------------------------------------------------------------ matrix-core
+typedef __attribute__((address_space(3))) void lds_void;
+constexpr int kIdxCap = 4096;  // index slots the matrix-core kernel stages in LDS
+
 struct MfmaArgs {
   AttnParams p;
   float* ws;              // split partials, or nullptr
   int nsplit;
   int tiles_per_split;
   int rows_per_xcd;       // query-row remap: consecutive rows on one XCD
+  int idx_cap;            // ints of LDS holding the staged index row
+};
+
+// LDS barrier that waits only for this wave's LDS traffic, not for global
+// loads still in flight (the gathers of later tiles must stay in flight).
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// K=V tile of 32 rows in LDS, each row padded by 16 bytes (row stride
+// 2D+16 bytes = 4 or 36 dwords mod 64 banks), so that the S-phase reads (16
+// rows, one 16-byte chunk) and the PV-phase reads (4 rows x 8 consecutive
+// chunks) fall in distinct banks, while every address is a per-lane base plus
+// an immediate offset.  Rows are filled by direct global->LDS 16-byte buffer
+// loads: one wave instruction writes up to 1 KiB contiguous (lane l at +16*l),
+// one instruction per row (plus an 8-lane one for the last 128 bytes when
+// D = 576); lanes whose row slot is empty read past the buffer bound, which
+// writes zeros.
+template <int D>
+struct KTile {
+  static constexpr int ROWB = D * 2 + 16;
+  static constexpr int BYTES = kNK * ROWB;
+  static constexpr int G = (D > 512) ? 8 : 4;   // loads per wave per tile (8 waves)
 };
 
 // Split workspace (fp32): [rows][nsplit][H][2] running (max, sum) in the log2
 // domain, then [rows][nsplit][H][dv] unnormalised partial outputs.
 //
-// Template: NW waves (16 heads each in the S phase, dv/NW output columns each
-// in the PV phase), NB = 16-column blocks per wave, D = K=V row width, R =
-// rope_dim (trailing rotated channels).  Lane c16 of a wave owns the NB
-// consecutive output columns wave*16*NB + NB*c16 ..; its V operand for one key
-// is then a single NB*2-byte LDS read.
+// One workgroup = one query row x one group of 64 heads, 8 waves (2 per SIMD).
+// S phase: wave w computes S^T for heads 16(w%4) .. +15 over keys 16(w/4) ..
+// +15 of the 32-key tile; the two key halves of a head exchange their tile
+// maxima through LDS.  PV phase: wave w owns output columns 64w .. 64w+63,
+// lane c16 the 4 consecutive columns 64w + 4*c16 .. (one 8-byte LDS read per
+// key, 8-byte output stores, lane-local de-rotation).  The gathers run
+// NBUF-1 tiles ahead of the compute.
 //
-// Key list of a query row: the visible window rows (one contiguous run of
-// kv_win), then the pool slots; each part is padded to whole 32-key tiles so
-// that every tile reads one tensor.  Rows are fetched with buffer loads whose
-// bound is the sequence's slice of that tensor: an empty slot gets an offset
-// past the bound and reads zeros, with no branch.
-template <int NW, int NB, int D, int R>
-__global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(MfmaArgs args) {
-  constexpr int NT = NW * 64;
-  constexpr int HG = 16 * NW;           // heads per workgroup (one head group)
-  constexpr int DVW = 16 * NB;          // output columns per wave
-  constexpr int KS = D / 32;            // k-steps of the S phase
-  constexpr int ROWB = D * 2 + 16;      // padded LDS row (bytes)
-  constexpr int CPR = D / 8;            // 16-byte chunks per K=V row
-  constexpr int GATHER_IT = (kNK * CPR + NT - 1) / NT;
-  constexpr int half = R / 2, rbase = D - R;
-  static_assert(NB == 2 || NB == 4 || NB == 8, "V read width");
+// Softmax: a per-head reference max m (the sink logit to start with) is raised
+// only when a tile's max exceeds it by more than 8 (log2 units); otherwise the
+// probabilities exp2(s - m) may reach 2^8, which bf16 and fp32 carry exactly
+// in relative terms, and O / l is unchanged.  So the accumulators are rescaled
+// only in the rare tile that raises m.
+template <int D, int NBUF>
+__global__ __launch_bounds__(512) void attn_mfma_kernel(MfmaArgs args) {
+  constexpr int NW = 8, NT = 512, HG = 64, NB = 4;
+  constexpr int KS = D / 32;
+  constexpr int R = 64, half = R / 2, rbase = D - R;
+  constexpr float kLazy = 8.f;
+  using KT = KTile<D>;
+  static_assert(NBUF == 3 || NBUF == 4, "buffer count");
+  // One static array per K buffer: with distinct objects the compiler can
+  // tell that an in-flight gather into one buffer does not alias reads of
+  // another, so it does not wait for the gather before those reads.
+  __shared__ __attribute__((aligned(16))) unsigned char kb0[KT::BYTES];
+  __shared__ __attribute__((aligned(16))) unsigned char kb1[KT::BYTES];
+  __shared__ __attribute__((aligned(16))) unsigned char kb2[KT::BYTES];
+  __shared__ __attribute__((aligned(16))) unsigned char kb3[NBUF == 4 ? KT::BYTES : 16];
+  // every other LDS array is static as well, for the same reason
+  __shared__ __attribute__((aligned(16))) u16 Ps[HG * kNK];        // P, bf16
+  __shared__ __attribute__((aligned(16))) float alpha_s[HG];       // rescale factors
+  __shared__ __attribute__((aligned(16))) float fin_s[HG];         // 1/l
+  __shared__ __attribute__((aligned(16))) float tm_s[2 * HG];      // tile maxima
+  __shared__ __attribute__((aligned(16))) float l_s[HG];           // second half's sum
+  __shared__ __attribute__((aligned(16))) int rid_s[NBUF * kNK];   // row ids per buffer
+  __shared__ int flags[16];                                        // rescale, scan
+  __shared__ int idx_s[kIdxCap];                                   // the index row
   const AttnParams& p = args.p;
-  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  unsigned char* ktile = smem;                                   // [32][ROWB]
-  u16* Ps = reinterpret_cast<u16*>(smem + kNK * ROWB);           // [HG][32] bf16
-  float* alpha_s = reinterpret_cast<float*>(Ps + HG * kNK);      // [HG]
-  float* fin_s = alpha_s + HG;                                   // [HG] 1/l
-  int* rid_s = reinterpret_cast<int*>(fin_s + HG);               // [2][32] row ids
-  int* flags = rid_s + 2 * kNK;                                  // [2] rescale, [NW] scan
+  auto kbuf_of = [&](auto JC) -> unsigned char* {
+    constexpr int J = decltype(JC)::value;
+    if constexpr (J == 0) return kb0;
+    else if constexpr (J == 1) return kb1;
+    else if constexpr (J == 2) return kb2;
+    else return kb3;
+  };
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  // the wave index is uniform: keep it (and everything derived from it) scalar
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
   const int g = lane >> 4, c16 = lane & 15;
+  const int hgrp = wave & 3, kh = wave >> 2;   // S phase: head block, key half
 
   // query row: consecutive rows stay on one XCD (workgroups go round-robin
   // over the 8 XCDs), so neighbouring rows share window rows in one L2
@@ -207,7 +256,7 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(MfmaArgs args) {
   const float2* cs = reinterpret_cast<const float2*>(p.cs);
   const bool split_mode = args.nsplit > 1;
 
-  if (R > 0 && (t < 0 || t >= p.n_pos)) {
+  if (t < 0 || t >= p.n_pos) {
     // position outside the RoPE table: the row is written as NaN
     if (split_mode) {
       float* ml = args.ws + ((size_t)row * args.nsplit + split) * H * 2;
@@ -222,7 +271,8 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(MfmaArgs args) {
     return;
   }
 
-  // ---- effective key list
+  // ---- effective key list: visible window rows, then the pool slots, each
+  // part padded to whole tiles so that a tile reads one tensor
   int n_win = 0, r_lo = 0;
   if (p.window > 0 && p.kv_win != nullptr) {
     const long wp0 = p.win_pos0[b];
@@ -231,14 +281,15 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(MfmaArgs args) {
     if (hi >= lo) { n_win = (int)(hi - lo + 1); r_lo = (int)(lo - wp0); }
   }
   int npool = 0;
-  const int* idx_row = p.dense ? nullptr : p.idx + row * p.k;
   if (p.dense) {
     npool = p.pool ? ready_count(t, p.m, p.T) : 0;
   } else if (p.k > 0 && p.pool) {
-    // the last non-empty slot bounds the list (top-k pads with -1 at the tail)
+    // stage the index row in LDS; the last non-empty slot bounds the list
+    const int* idx_row = p.idx + row * p.k;
     int last = -1;
     for (int j = tid; j < p.k; j += NT) {
       const int w = idx_row[j];
+      idx_s[j] = w;
       if (w >= 0 && w < p.T) last = j;
     }
 #pragma unroll
@@ -263,149 +314,170 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(MfmaArgs args) {
       const_cast<u16*>(pool_base), 0, pool_base ? p.T * D * 2 : 0, 0x00020000);
 
   // row id of key j of a tile: kv_win / pool row of this sequence, -1 = empty
-  auto resolve = [&](int tile, int buf) {
-    if (wave == 0 && lane < kNK) {
-      int rid = -1;
-      if (tile < WT) {
-        const int jj = tile * kNK + lane;
-        if (jj < n_win) rid = r_lo + jj;
-      } else {
-        const int jj = (tile - WT) * kNK + lane;
-        if (jj < npool) {
-          const int w = p.dense ? jj : idx_row[jj];
-          if (w >= 0 && w < p.T) rid = w;
-        }
+  auto rid_of = [&](int tile, int j) -> int {
+    if (tile < WT) {
+      const int jj = tile * kNK + j;
+      return jj < n_win ? r_lo + jj : -1;
+    }
+    const int jj = (tile - WT) * kNK + j;
+    if (jj >= npool) return -1;
+    const int w = p.dense ? jj : idx_s[jj];
+    return (w >= 0 && w < p.T) ? w : -1;
+  };
+
+  // this wave's share of a tile's gather into buffer J: rows 4*wave ..
+  // 4*wave+3, one 1 KiB load per row (and one 8-lane load of the last 128
+  // bytes when D = 576)
+  auto issue = [&](auto JC, int tile) {
+    constexpr int J = decltype(JC)::value;
+    unsigned char* kbuf = kbuf_of(JC);
+    int my_rid = -1;
+    if (lane < 4) {
+      my_rid = rid_of(tile, wave * 4 + lane);
+      rid_s[J * kNK + wave * 4 + lane] = my_rid;
+    }
+    const __amdgpu_buffer_rsrc_t rs = tile < WT ? rs_win : rs_pool;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int r = wave * 4 + q;
+      const int rid = __shfl(my_rid, q, 64);
+      const int off = rid >= 0 ? rid * (D * 2) + (lane << 4) : 0x7ffffff0;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(kbuf + r * KT::ROWB), 16, off,
+                                               0, 0, 0);
+      if constexpr (D > 512) {
+        if (lane < (D - 512) / 8)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(kbuf + r * KT::ROWB + 1024),
+                                                   16, rid >= 0 ? off + 1024 : off, 0, 0, 0);
       }
-      rid_s[buf * kNK + lane] = rid;
     }
   };
 
-  // ---- Q fragments (B operand of S^T = K Q^T): head hl, dims 32ks + 8g .. +7,
-  // rotated at +t on the rope slice, rounded to bf16
-  const int hl = 16 * wave + c16;
-  bf16x8 qf[KS];
+  // ---- Q fragments (B operand of S^T = K Q^T): head hq, dims 32ks + 8g .. +7
+  const int hq = 16 * hgrp + c16;
+  uint4 qraw[KS];
   {
-    const u16* qrow = reinterpret_cast<const u16*>(p.q) + (row * H + h0 + hl) * D;
+    const u16* qrow = reinterpret_cast<const u16*>(p.q) + (row * H + h0 + hq) * D;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const int d0 = 32 * ks + 8 * g;
-      uint4 u = *reinterpret_cast<const uint4*>(qrow + d0);
-      if (32 * ks + 32 > rbase && d0 >= rbase) {
-        float v[8] = {bf_lo(u.x), bf_hi(u.x), bf_lo(u.y), bf_hi(u.y),
-                      bf_lo(u.z), bf_hi(u.z), bf_lo(u.w), bf_hi(u.w)};
+    for (int ks = 0; ks < KS; ++ks)
+      qraw[ks] = *reinterpret_cast<const uint4*>(qrow + 32 * ks + 8 * g);
+  }
+  if (tid == 0) { flags[0] = 1; flags[1] = 1; }
+  if (tile0 + 0 < tile1) issue(std::integral_constant<int, 0>{}, tile0 + 0);
+  if (tile0 + 1 < tile1) issue(std::integral_constant<int, 1>{}, tile0 + 1);
+  if (tile0 + 2 < tile1) issue(std::integral_constant<int, 2>{}, tile0 + 2);
+  if constexpr (NBUF == 4)
+    if (tile0 + 3 < tile1) issue(std::integral_constant<int, 3>{}, tile0 + 3);
+
+  // rotate the rope slice of q at +t, round to bf16
+  bf16x8 qf[KS];
 #pragma unroll
-        for (int e = 0; e < 8; e += 2) {
-          const float2 r = cs[t * half + ((d0 + e - rbase) >> 1)];
-          const float a = v[e], bb = v[e + 1];
-          v[e] = a * r.x - bb * r.y;
-          v[e + 1] = a * r.y + bb * r.x;
-        }
-        u.x = pack2(v[0], v[1]); u.y = pack2(v[2], v[3]);
-        u.z = pack2(v[4], v[5]); u.w = pack2(v[6], v[7]);
+  for (int ks = 0; ks < KS; ++ks) {
+    const int d0 = 32 * ks + 8 * g;
+    uint4 u = qraw[ks];
+    if (32 * ks + 32 > rbase && d0 >= rbase) {
+      float v[8] = {bf_lo(u.x), bf_hi(u.x), bf_lo(u.y), bf_hi(u.y),
+                    bf_lo(u.z), bf_hi(u.z), bf_lo(u.w), bf_hi(u.w)};
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        const float2 r = cs[t * half + ((d0 + e - rbase) >> 1)];
+        const float a = v[e], bb = v[e + 1];
+        v[e] = a * r.x - bb * r.y;
+        v[e + 1] = a * r.y + bb * r.x;
       }
-      qf[ks] = as_bf16x8(u);
+      u.x = pack2(v[0], v[1]); u.y = pack2(v[2], v[3]);
+      u.z = pack2(v[4], v[5]); u.w = pack2(v[6], v[7]);
     }
+    qf[ks] = as_bf16x8(u);
   }
 
-  // ---- softmax state of head hl (replicated over the 4 lane groups), log2 domain
+  // ---- softmax state of head hq (replicated over the 4 lane groups, and the
+  // same in both key-half waves), log2 domain; lrun sums this wave's keys only
   const float sl2 = p.scale * kLog2e;
-  float mrun = -INFINITY, lrun = 0.f;
-  if (p.sink && !split_mode) { mrun = p.sink[h0 + hl] * kLog2e; lrun = 1.f; }
+  float mref = -INFINITY, lrun = 0.f;
+  if (p.sink && !split_mode) {
+    mref = p.sink[h0 + hq] * kLog2e;
+    if (kh == 0) lrun = 1.f;
+  }
 
-  f32x4 acc[NW][NB];
+  f32x4 acc[4][NB];
 #pragma unroll
-  for (int mb = 0; mb < NW; ++mb)
+  for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const int col0 = wave * DVW + NB * c16;  // this lane's first output column
+  const int col0 = 64 * wave + 4 * c16;          // this lane's first output column
 
-  if (tid == 0) { flags[0] = 1; flags[1] = 1; }
-  if (tile0 < tile1) resolve(tile0, 0);
-  __syncthreads();
+  // one tile, read from buffer J; the gather NBUF-1 tiles ahead goes to the
+  // buffer the previous tile used
+  auto step = [&](auto JC, int tile) {
+    constexpr int J = decltype(JC)::value;
+    const int it = tile - tile0;
+    const int par = it & 1;
+    // this wave's loads of `tile` are done once at most the loads of the
+    // tiles issued after it are still outstanding
+    const int later = min(NBUF - 2, tile1 - 1 - tile);
+    if (later >= 2) wait_vmcnt<2 * KT::G>();
+    else if (later == 1) wait_vmcnt<KT::G>();
+    else wait_vmcnt<0>();
+    lds_barrier();  // every wave's loads of this tile have landed
+    if (tile + NBUF - 1 < tile1)
+      issue(std::integral_constant<int, (J + NBUF - 1) % NBUF>{}, tile + NBUF - 1);
+    if (tid == 0) flags[par ^ 1] = 0;  // the next tile's rescale flag starts clear
 
-  for (int tile = tile0; tile < tile1; ++tile) {
-    const int buf = (tile - tile0) & 1;
-    // ---- gather: 32 rows x D bf16 into the LDS tile (16-byte buffer loads)
-    {
-      const __amdgpu_buffer_rsrc_t rs = tile < WT ? rs_win : rs_pool;
-#pragma unroll
-      for (int it = 0; it < GATHER_IT; ++it) {
-        const int c = tid + it * NT;
-        if (GATHER_IT * NT == kNK * CPR || c < kNK * CPR) {
-          const int r = c / CPR, col = c - r * CPR;
-          const int rid = rid_s[buf * kNK + r];
-          const int off = rid >= 0 ? rid * (D * 2) + col * 16 : 0x7ffffff0;
-          const uint4 v =
-              __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
-          *reinterpret_cast<uint4*>(ktile + r * ROWB + col * 16) = v;
-        }
-      }
-    }
-    if (tid == 0) flags[buf ^ 1] = 0;  // next tile's rescale flag starts clear
-    __syncthreads();
-    if (tile + 1 < tile1) resolve(tile + 1, buf ^ 1);
-
-    // ---- S phase: S^T[key][head] for this wave's 16 heads, 4 k-steps per
-    // group (the scheduling barrier bounds the K fragments in flight)
-    f32x4 st[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+    const unsigned char* kbuf = kbuf_of(JC);
+    // ---- S phase: S^T[16 keys][16 heads] (groups of 4 k-steps; the fence
+    // bounds the K fragments held in registers at once)
+    __builtin_amdgcn_sched_barrier(0);
+    f32x4 st0 = f32x4{0.f, 0.f, 0.f, 0.f}, st1 = st0;  // even / odd k-steps
+    // this lane supplies K row 16kh + c16, 16-byte chunk 4ks + g
+    const unsigned char* krow = kbuf + (16 * kh + c16) * KT::ROWB + 16 * g;
 #pragma unroll
     for (int k4 = 0; k4 < KS; k4 += 4) {
-      uint4 kv[4][2];
+      uint4 kv[4];
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk)
+      for (int kk = 0; kk < 4; ++kk) {
+        const int ks = k4 + kk;
+        if (ks < KS) kv[kk] = *reinterpret_cast<const uint4*>(krow + 64 * ks);
+      }
 #pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2)
-          if (k4 + kk < KS)
-            kv[kk][h2] = *reinterpret_cast<const uint4*>(
-                ktile + (16 * h2 + c16) * ROWB + 64 * (k4 + kk) + 16 * g);
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2)
-          if (k4 + kk < KS) st[h2] = mfma16x16x32(as_bf16x8(kv[kk][h2]), qf[k4 + kk], st[h2]);
+      for (int kk = 0; kk < 4; kk += 2) {
+        if (k4 + kk < KS) st0 = mfma16x16x32(as_bf16x8(kv[kk]), qf[k4 + kk], st0);
+        if (k4 + kk + 1 < KS) st1 = mfma16x16x32(as_bf16x8(kv[kk + 1]), qf[k4 + kk + 1], st1);
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
-    // lane holds keys 16*h2 + 4g + j of head hl
-    const int4 ra = *reinterpret_cast<const int4*>(rid_s + buf * kNK + 4 * g);
-    const int4 rb = *reinterpret_cast<const int4*>(rid_s + buf * kNK + 16 + 4 * g);
-    const int rv[8] = {ra.x, ra.y, ra.z, ra.w, rb.x, rb.y, rb.z, rb.w};
-    float sv[8];
-    float tmax = -INFINITY;
-#pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float x = rv[4 * h2 + j] >= 0 ? st[h2][j] * sl2 : -INFINITY;
-        sv[4 * h2 + j] = x;
-        tmax = fmaxf(tmax, x);
-      }
+    const f32x4 st = st0 + st1;
+    // lane holds keys 16kh + 4g + j of head hq
+    const int4 rv = *reinterpret_cast<const int4*>(rid_s + J * kNK + 16 * kh + 4 * g);
+    float sv[4] = {rv.x >= 0 ? st[0] * sl2 : -INFINITY, rv.y >= 0 ? st[1] * sl2 : -INFINITY,
+                   rv.z >= 0 ? st[2] * sl2 : -INFINITY, rv.w >= 0 ? st[3] * sl2 : -INFINITY};
+    float tmax = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
     tmax = fmaxf(tmax, shfl_xor(tmax, 16));
     tmax = fmaxf(tmax, shfl_xor(tmax, 32));
-    const float mnew = fmaxf(mrun, tmax);
+    if (g == 0) tm_s[kh * HG + hq] = tmax;
+    lds_barrier();
+    tmax = fmaxf(tmax, tm_s[(kh ^ 1) * HG + hq]);
+    const float mnew = (tmax > mref + kLazy) ? tmax : mref;
+    const float alpha = (mnew == mref) ? 1.f : exp2f(mref - mnew);
     const float mbase = (mnew == -INFINITY) ? 0.f : mnew;
-    const float alpha = exp2f(mrun - mbase);
-    float psum = 0.f;
-    uint32_t pk[4];
-#pragma unroll
-    for (int e = 0; e < 8; e += 2) {
-      const float p0 = exp2f(sv[e] - mbase), p1 = exp2f(sv[e + 1] - mbase);
-      psum += p0 + p1;
-      pk[e >> 1] = pack2(p0, p1);
-    }
+    const float p0 = exp2f(sv[0] - mbase), p1 = exp2f(sv[1] - mbase);
+    const float p2 = exp2f(sv[2] - mbase), p3 = exp2f(sv[3] - mbase);
+    float psum = (p0 + p1) + (p2 + p3);
     psum += shfl_xor(psum, 16);
     psum += shfl_xor(psum, 32);
     lrun = lrun * alpha + psum;
-    mrun = mnew;
-    // P row of head hl; key 16*h2 + 4g + j sits at position 8g + 4*h2 + j
-    *reinterpret_cast<uint4*>(Ps + hl * kNK + 8 * g) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
-    if (g == 0) alpha_s[hl] = alpha;
-    if (__ballot(alpha != 1.f) != 0ull && lane == 0) flags[buf] = 1;
-    __syncthreads();
+    mref = mnew;
+    // P row of head hq; key 16*kh + 4g + j sits at position 8g + 4*kh + j
+    *reinterpret_cast<uint2*>(Ps + hq * kNK + 8 * g + 4 * kh) =
+        make_uint2(pack2(p0, p1), pack2(p2, p3));
+    if (kh == 0 && g == 0) alpha_s[hq] = alpha;
+    if (kh == 0 && __ballot(alpha != 1.f) != 0ull && lane == 0) flags[par] = 1;
+    lds_barrier();
 
-    // ---- PV phase: O[all HG heads][this wave's DVW columns] += P V
-    if (flags[buf]) {
+    // ---- PV phase: O[all 64 heads][this wave's 64 columns] += P V
+    __builtin_amdgcn_sched_barrier(0);
+    if (flags[par]) {
 #pragma unroll
-      for (int mb = 0; mb < NW; ++mb) {
+      for (int mb = 0; mb < 4; ++mb) {
         const float4 al = *reinterpret_cast<const float4*>(alpha_s + 16 * mb + 4 * g);
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
@@ -414,25 +486,18 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(MfmaArgs args) {
         }
       }
     }
-    bf16x8 pa[NW];
+    bf16x8 pa[4];
 #pragma unroll
-    for (int mb = 0; mb < NW; ++mb)
+    for (int mb = 0; mb < 4; ++mb)
       pa[mb] = as_bf16x8(*reinterpret_cast<const uint4*>(Ps + (16 * mb + c16) * kNK + 8 * g));
-    // V: for key position q (key 16*(q/4) + 4g + q%4), this lane's NB columns
-    uint32_t vr[8][NB / 2];
+    // V: for key position q (key 16*(q/4) + 4g + q%4), this lane's 4 columns
+    uint32_t vr[8][2];
+    const unsigned char* vcol = kbuf + 4 * g * KT::ROWB + 2 * col0;
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
-      const unsigned char* src =
-          ktile + (16 * (q >> 2) + 4 * g + (q & 3)) * ROWB + col0 * 2;
-      if constexpr (NB == 8) {
-        const uint4 u = *reinterpret_cast<const uint4*>(src);
-        vr[q][0] = u.x; vr[q][1] = u.y; vr[q][2] = u.z; vr[q][3] = u.w;
-      } else if constexpr (NB == 4) {
-        const uint2 u = *reinterpret_cast<const uint2*>(src);
-        vr[q][0] = u.x; vr[q][1] = u.y;
-      } else {
-        vr[q][0] = *reinterpret_cast<const uint32_t*>(src);
-      }
+      const uint2 u = *reinterpret_cast<const uint2*>(
+          vcol + (16 * (q >> 2) + (q & 3)) * KT::ROWB);
+      vr[q][0] = u.x; vr[q][1] = u.y;
     }
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
@@ -445,34 +510,48 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(MfmaArgs args) {
       }
       const bf16x8 vb = as_bf16x8(make_uint4(f[0], f[1], f[2], f[3]));
 #pragma unroll
-      for (int mb = 0; mb < NW; ++mb) acc[mb][nb] = mfma16x16x32(pa[mb], vb, acc[mb][nb]);
+      for (int mb = 0; mb < 4; ++mb) acc[mb][nb] = mfma16x16x32(pa[mb], vb, acc[mb][nb]);
     }
-    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  for (int tile = tile0; tile < tile1; tile += NBUF) {
+    step(std::integral_constant<int, 0>{}, tile);
+    if (tile + 1 < tile1) step(std::integral_constant<int, 1>{}, tile + 1);
+    if (tile + 2 < tile1) step(std::integral_constant<int, 2>{}, tile + 2);
+    if constexpr (NBUF == 4)
+      if (tile + 3 < tile1) step(std::integral_constant<int, 3>{}, tile + 3);
   }
 
-  // ---- epilogue
+  // ---- epilogue: l = sum over both key halves
+  if (kh == 1 && g == 0) l_s[hq] = lrun;
+  lds_barrier();
+  if (kh == 0 && g == 0) {
+    const float l = lrun + l_s[hq];
+    if (split_mode) {
+      float* ml = args.ws + ((size_t)row * args.nsplit + split) * H * 2;
+      ml[2 * (h0 + hq)] = mref;
+      ml[2 * (h0 + hq) + 1] = l;
+    } else {
+      fin_s[hq] = l > 0.f ? 1.f / l : 0.f;
+    }
+  }
   if (split_mode) {
-    float* ml = args.ws + ((size_t)row * args.nsplit + split) * H * 2;
-    if (g == 0) { ml[2 * (h0 + hl)] = mrun; ml[2 * (h0 + hl) + 1] = lrun; }
     float* po = args.ws + (size_t)((long)p.B * p.S) * args.nsplit * H * 2 +
                 ((size_t)row * args.nsplit + split) * H * dv;
 #pragma unroll
-    for (int mb = 0; mb < NW; ++mb)
+    for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        float* dst = po + (size_t)(h0 + 16 * mb + 4 * g + j) * dv + col0;
-#pragma unroll
-        for (int nb = 0; nb < NB; nb += 2)
-          *reinterpret_cast<float2*>(dst + nb) = make_float2(acc[mb][nb][j], acc[mb][nb + 1][j]);
-      }
+      for (int j = 0; j < 4; ++j)
+        *reinterpret_cast<float4*>(po + (size_t)(h0 + 16 * mb + 4 * g + j) * dv + col0) =
+            make_float4(acc[mb][0][j], acc[mb][1][j], acc[mb][2][j], acc[mb][3][j]);
     return;
   }
-  if (g == 0) fin_s[hl] = lrun > 0.f ? 1.f / lrun : 0.f;
-  __syncthreads();
+  lds_barrier();
   u16* out = reinterpret_cast<u16*>(p.out) + (row * H + h0) * dv;
-  const bool derot = (dv == D) && R > 0 && col0 + NB > rbase;
+  const bool derot = (dv == D) && col0 + NB > rbase;
 #pragma unroll
-  for (int mb = 0; mb < NW; ++mb) {
+  for (int mb = 0; mb < 4; ++mb) {
     const float4 li = *reinterpret_cast<const float4*>(fin_s + 16 * mb + 4 * g);
     const float lv[4] = {li.x, li.y, li.z, li.w};
 #pragma unroll
@@ -485,97 +564,87 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(MfmaArgs args) {
         for (int nb = 0; nb < NB; nb += 2) {
           const int col = col0 + nb;
           if (col >= rbase) {
-            const float2 r = cs[t * half + ((col - rbase) >> 1)];
+            const float2 rr = cs[t * half + ((col - rbase) >> 1)];
             const float a = v[nb], bb = v[nb + 1];
-            v[nb] = a * r.x + bb * r.y;
-            v[nb + 1] = -a * r.y + bb * r.x;
+            v[nb] = a * rr.x + bb * rr.y;
+            v[nb + 1] = -a * rr.y + bb * rr.x;
           }
         }
       }
-      uint32_t w[NB / 2];
-#pragma unroll
-      for (int nb = 0; nb < NB; nb += 2) w[nb >> 1] = pack2(v[nb], v[nb + 1]);
-      u16* dst = out + (16 * mb + 4 * g + j) * dv + col0;
-      if constexpr (NB == 8)
-        *reinterpret_cast<uint4*>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
-      else if constexpr (NB == 4)
-        *reinterpret_cast<uint2*>(dst) = make_uint2(w[0], w[1]);
-      else
-        *reinterpret_cast<uint32_t*>(dst) = w[0];
+      *reinterpret_cast<uint2*>(out + (16 * mb + 4 * g + j) * dv + col0) =
+          make_uint2(pack2(v[0], v[1]), pack2(v[2], v[3]));
     }
   }
 }
 
 // Merge split partials: M = max(z, m_s), L = e^(z-M) + sum e^(m_s-M) l_s,
 // O = sum e^(m_s-M) O_s / L, then the output rope slice is rotated at -t.
+// Thread = 8 consecutive columns of one head; 4 heads per workgroup.
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnParams p, const float* ws,
                                                            int nsplit) {
   const long row = blockIdx.x;
   const int H = p.H, dv = p.dv;
-  const RowInfo ri = row_info(p, row);
+  const int per_head = dv >> 3;
+  const int h = blockIdx.y * (256 / per_head) + threadIdx.x / per_head;
+  if (h >= H) return;
+  const int c = (threadIdx.x % per_head) * 8;
+  const int b = (int)(row / p.S);
+  const long t = (long)p.q_pos[b] + (row - (long)b * p.S);
   const int half = p.rope_dim >> 1, rbase = p.D - p.rope_dim;
   const float2* cs = reinterpret_cast<const float2*>(p.cs);
   const float* ml = ws + (size_t)row * nsplit * H * 2;
-  const float* po = ws + (size_t)(p.B * (long)p.S) * nsplit * H * 2 + (size_t)row * nsplit * H * dv;
-  u16* out = reinterpret_cast<u16*>(p.out) + row * H * dv;
-  for (int e = threadIdx.x; e < H * (dv >> 1); e += blockDim.x) {
-    const int h = e / (dv >> 1);
-    const int c = 2 * (e - h * (dv >> 1));
-    float M = p.sink ? p.sink[h] * kLog2e : -INFINITY;
-    bool nan = false;
-    for (int s = 0; s < nsplit; ++s) {
-      const float ms = ml[(s * H + h) * 2];
-      if (ms != ms) nan = true;
-      M = fmaxf(M, ms);
-    }
-    const float Mb = (M == -INFINITY) ? 0.f : M;
-    float L = p.sink ? exp2f(p.sink[h] * kLog2e - Mb) : 0.f;
-    float o0 = 0.f, o1 = 0.f;
-    for (int s = 0; s < nsplit; ++s) {
-      const float f = exp2f(ml[(s * H + h) * 2] - Mb);
-      L += f * ml[(s * H + h) * 2 + 1];
-      const float* os = po + ((size_t)s * H + h) * dv;
-      o0 += f * os[c];
-      o1 += f * os[c + 1];
-    }
-    const float inv = L > 0.f ? 1.f / L : 0.f;
-    o0 *= inv;
-    o1 *= inv;
-    if (p.dv == p.D && p.rope_dim > 0 && c >= rbase && ri.t >= 0 && ri.t < p.n_pos) {
-      const float2 r = cs[ri.t * half + ((c - rbase) >> 1)];
-      const float a = o0, bb = o1;
-      o0 = a * r.x + bb * r.y;
-      o1 = -a * r.y + bb * r.x;
-    }
-    if (nan) o0 = o1 = __int_as_float(0x7fc00000);
-    out[h * dv + c] = f2bf(o0);
-    out[h * dv + c + 1] = f2bf(o1);
+  const float* po =
+      ws + (size_t)((long)p.B * p.S) * nsplit * H * 2 + (size_t)row * nsplit * H * dv;
+  float M = p.sink ? p.sink[h] * kLog2e : -INFINITY;
+  bool nan = false;
+  for (int s = 0; s < nsplit; ++s) {
+    const float ms = ml[(s * H + h) * 2];
+    if (ms != ms) nan = true;
+    M = fmaxf(M, ms);
   }
+  const float Mb = (M == -INFINITY) ? 0.f : M;
+  float L = p.sink ? exp2f(p.sink[h] * kLog2e - Mb) : 0.f;
+  float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < nsplit; ++s) {
+    const float f = exp2f(ml[(s * H + h) * 2] - Mb);
+    L += f * ml[(s * H + h) * 2 + 1];
+    const float4* os = reinterpret_cast<const float4*>(po + ((size_t)s * H + h) * dv + c);
+    const float4 a = os[0], bq = os[1];
+    o[0] += f * a.x; o[1] += f * a.y; o[2] += f * a.z; o[3] += f * a.w;
+    o[4] += f * bq.x; o[5] += f * bq.y; o[6] += f * bq.z; o[7] += f * bq.w;
+  }
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) o[e] *= inv;
+  const bool tin = t >= 0 && t < p.n_pos;
+  if (p.dv == p.D && p.rope_dim > 0 && tin) {
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+      if (c + e >= rbase) {
+        const float2 r = cs[t * half + ((c + e - rbase) >> 1)];
+        const float a = o[e], bb = o[e + 1];
+        o[e] = a * r.x + bb * r.y;
+        o[e + 1] = -a * r.y + bb * r.x;
+      }
+    }
+  }
+  if (nan || !tin)
+    for (int e = 0; e < 8; ++e) o[e] = __int_as_float(0x7fc00000);
+  *reinterpret_cast<uint4*>(reinterpret_cast<u16*>(p.out) + (row * H + h) * dv + c) =
+      make_uint4(pack2(o[0], o[1]), pack2(o[2], o[3]), pack2(o[4], o[5]), pack2(o[6], o[7]));
 }
 
-// Matrix-core shapes compiled in.  Heads run in groups of 16*NW; every
-// group is its own workgroup (so H = 128 runs as two 64-head groups).
-struct MfmaShape {
-  int nw, nb, d, r;
-};
+// Matrix-core shapes: heads in groups of 64 (H = 128 runs as two groups),
+// D = 512 (CSA / HCA) or 576 (DSA: 512 latent + 64 rope), dv = 512, rope 64.
 
-bool mfma_shape(int H, int D, int dv, int rope_dim, MfmaShape* sh) {
-  if (H % 64 == 0 && dv == 512 && rope_dim == 64 && (D == 512 || D == 576)) {
-    *sh = {4, 8, D, 64};
-    return true;
-  }
-  if (H % 16 == 0 && dv == 64 && ((D == 64 && rope_dim == 16) || (D == 96 && rope_dim == 32))) {
-    *sh = {1, 4, D, rope_dim};
-    return true;
-  }
-  return false;
+bool mfma_shape(int H, int D, int dv, int rope_dim, int k) {
+  return H % 64 == 0 && dv == 512 && rope_dim == 64 && (D == 512 || D == 576) &&
+         k <= kIdxCap;
 }
 
-size_t mfma_lds_bytes(int nw, int D) {
-  const int hg = 16 * nw;
-  return (size_t)kNK * (D * 2 + 16) + (size_t)hg * kNK * 2 + (size_t)hg * 4 * 2 +
-         2 * kNK * sizeof(int) + (2 + nw) * sizeof(int);
-}
+int mfma_nbuf(int) { return 3; }
+
+
 
 int device_cus() {
   static thread_local int cached_dev = -1, cached_cus = 0;
@@ -595,14 +664,13 @@ int device_cus() {
 }  // namespace
 
 AttnPlan plan_attention(int B, int S, int H, int D, int dv, int rope_dim, int max_slots,
-                        bool bf16, long max_rows) {
+                        bool bf16, long max_rows, int k) {
   AttnPlan pl{0, 1, 1 << 30, 0};
-  MfmaShape sh;
-  if (!bf16 || !mfma_shape(H, D, dv, rope_dim, &sh)) return pl;
+  if (!bf16 || !mfma_shape(H, D, dv, rope_dim, k)) return pl;
   // the gather addresses one sequence's rows with 32-bit buffer offsets
   if (max_rows * D * 2 >= 0x7ffffff0L) return pl;
   pl.kernel = 1;
-  const long wgs = (long)B * S * (H / (16 * sh.nw));
+  const long wgs = (long)B * S * (H / 64);
   const int tiles = (max_slots + kNK - 1) / kNK;
   const int cus = device_cus();
   if (wgs < cus && tiles > 1) {
@@ -636,8 +704,6 @@ hipError_t launch_attention(const AttnParams& p, const AttnPlan& plan, void* ws,
 #undef CSA_GENERIC
     return hipGetLastError();
   }
-  MfmaShape sh;
-  mfma_shape(p.H, p.D, p.dv, p.rope_dim, &sh);
   MfmaArgs a;
   a.p = p;
   const bool split = plan.nsplit > 1 && ws != nullptr;
@@ -645,20 +711,17 @@ hipError_t launch_attention(const AttnParams& p, const AttnPlan& plan, void* ws,
   a.nsplit = split ? plan.nsplit : 1;
   a.tiles_per_split = split ? plan.tiles_per_split : (1 << 30);
   a.rows_per_xcd = (int)((rows + 7) / 8);
-  dim3 grid((unsigned)(8 * (long)a.rows_per_xcd), a.nsplit, p.H / (16 * sh.nw));
-  const size_t lds = mfma_lds_bytes(sh.nw, p.D);
-  if (sh.nw == 4 && sh.d == 512)
-    hipLaunchKernelGGL((attn_mfma_kernel<4, 8, 512, 64>), grid, dim3(256), lds, s, a);
-  else if (sh.nw == 4 && sh.d == 576)
-    hipLaunchKernelGGL((attn_mfma_kernel<4, 8, 576, 64>), grid, dim3(256), lds, s, a);
-  else if (sh.nw == 1 && sh.d == 64)
-    hipLaunchKernelGGL((attn_mfma_kernel<1, 4, 64, 16>), grid, dim3(64), lds, s, a);
-  else if (sh.nw == 1 && sh.d == 96)
-    hipLaunchKernelGGL((attn_mfma_kernel<1, 4, 96, 32>), grid, dim3(64), lds, s, a);
+  a.idx_cap = p.dense ? 0 : p.k;
+  dim3 grid((unsigned)(8 * (long)a.rows_per_xcd), a.nsplit, p.H / 64);
+  if (p.D == 512)
+    hipLaunchKernelGGL((attn_mfma_kernel<512, 3>), grid, dim3(512), 0, s, a);
+  else
+    hipLaunchKernelGGL((attn_mfma_kernel<576, 3>), grid, dim3(512), 0, s, a);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || !split) return err;
-  hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)rows), dim3(256), 0, s, p,
-                     reinterpret_cast<const float*>(ws), a.nsplit);
+  const int per_wg = 256 / (p.dv / 8);
+  hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)rows, (p.H + per_wg - 1) / per_wg),
+                     dim3(256), 0, s, p, reinterpret_cast<const float*>(ws), a.nsplit);
   return hipGetLastError();
 }
 

@@ -108,7 +108,8 @@ csa::AttnParams make_params(const void* q, const void* kv_win, const int32_t* wi
 csa_status_t run_attn(const char* fn, const csa::AttnParams& p, int max_slots,
                       void* workspace, size_t ws_bytes, hipStream_t s) {
   csa::AttnPlan plan = csa::plan_attention(p.B, p.S, p.H, p.D, p.dv, p.rope_dim, max_slots,
-                                           p.bf16, std::max<long>(p.L_win, p.T));
+                                           p.bf16, std::max<long>(p.L_win, p.T),
+                                           p.dense ? 0 : p.k);
   void* ws = nullptr;
   if (plan.nsplit > 1) {
     if (workspace && ws_bytes >= plan.ws_bytes && aligned16(workspace)) ws = workspace;
@@ -209,14 +210,14 @@ size_t csa_sparse_attn_workspace_size(int32_t B, int32_t S, int32_t H, int32_t D
                                       int32_t rope_dim, int32_t k, int32_t window,
                                       int32_t dtype) {
   if (B < 0 || S < 0 || H < 1 || D < 1 || dv < 1 || k < 0 || window < 0) return 0;
-  return csa::plan_attention(B, S, H, D, dv, rope_dim, window + k, dtype == CSA_BF16, 0)
+  return csa::plan_attention(B, S, H, D, dv, rope_dim, window + k, dtype == CSA_BF16, 0, k)
       .ws_bytes;
 }
 
 size_t hca_attn_workspace_size(int32_t B, int32_t S, int32_t H, int32_t D, int32_t dv,
                                int32_t rope_dim, int32_t T, int32_t window, int32_t dtype) {
   if (B < 0 || S < 0 || H < 1 || D < 1 || dv < 1 || T < 0 || window < 0) return 0;
-  return csa::plan_attention(B, S, H, D, dv, rope_dim, window + T, dtype == CSA_BF16, T)
+  return csa::plan_attention(B, S, H, D, dv, rope_dim, window + T, dtype == CSA_BF16, T, 0)
       .ws_bytes;
 }
 

@@ -149,9 +149,10 @@ struct AttnPlan {
   size_t ws_bytes;        // workspace the split needs
 };
 
-// max_rows: the larger of L_win and T (rows of one sequence a gather addresses)
+// max_rows: the larger of L_win and T (rows of one sequence a gather
+// addresses); k: index slots per query (0 in dense mode)
 AttnPlan plan_attention(int B, int S, int H, int D, int dv, int rope_dim, int max_slots,
-                        bool bf16, long max_rows);
+                        bool bf16, long max_rows, int k);
 hipError_t launch_attention(const AttnParams& p, const AttnPlan& plan, void* ws,
                             hipStream_t s);
 
