@@ -35,6 +35,7 @@ namespace csa {
 namespace {
 
 constexpr int kNK = 32;     // keys per tile
+constexpr int kPS = kNK + 8;  // P row stride (u16): 80 bytes keeps P reads conflict-free
 
 struct RowInfo {
   int b;
@@ -151,7 +152,6 @@ __global__ __launch_bounds__(256) void attn_generic_kernel(AttnParams p) {
 
 // ------------------------------------------------------------------ matrix-core
 typedef __attribute__((address_space(3))) void lds_void;
-constexpr int kIdxCap = 4096;  // index slots the matrix-core kernel stages in LDS
 
 struct MfmaArgs {
   AttnParams p;
@@ -159,7 +159,6 @@ struct MfmaArgs {
   int nsplit;
   int tiles_per_split;
   int rows_per_xcd;       // query-row remap: consecutive rows on one XCD
-  int idx_cap;            // ints of LDS holding the staged index row
 };
 
 // LDS barrier that waits only for this wave's LDS traffic, not for global
@@ -208,6 +207,7 @@ template <int D, int NBUF>
 __global__ __launch_bounds__(512) void attn_mfma_kernel(MfmaArgs args) {
   constexpr int NW = 8, NT = 512, HG = 64, NB = 4;
   constexpr int KS = D / 32;
+  constexpr int KH = KS / 2;  // k-steps per wave: the two waves of a head block split D
   constexpr int R = 64, half = R / 2, rbase = D - R;
   constexpr float kLazy = 8.f;
   using KT = KTile<D>;
@@ -220,16 +220,15 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(MfmaArgs args) {
   __shared__ __attribute__((aligned(16))) unsigned char kb2[KT::BYTES];
   __shared__ __attribute__((aligned(16))) unsigned char kb3[NBUF == 4 ? KT::BYTES : 16];
   // every other LDS array is static as well, for the same reason
-  __shared__ __attribute__((aligned(16))) u16 Ps[HG * kNK];        // P, bf16
+  __shared__ __attribute__((aligned(16))) u16 Ps[HG * kPS];        // P, bf16
+  __shared__ __attribute__((aligned(16))) float spart[NW * 2 * 64 * 4];  // S^T partials
   __shared__ __attribute__((aligned(16))) float alpha_s[HG];       // rescale factors
   __shared__ __attribute__((aligned(16))) float fin_s[HG];         // 1/l
-  __shared__ __attribute__((aligned(16))) float tm_s[2 * HG];      // tile maxima
   __shared__ __attribute__((aligned(16))) float l_s[HG];           // second half's sum
-  __shared__ __attribute__((aligned(16))) int rid_s[NBUF * kNK];   // row ids per buffer
-  __shared__ int flags[16];                                        // rescale, scan
-  __shared__ int idx_s[kIdxCap];                                   // the index row
+  __shared__ __attribute__((aligned(16))) float bias_s[NBUF * kNK];  // 0 / -inf per key slot
+  __shared__ int flags[20];                                        // rescale, scan
   const AttnParams& p = args.p;
-  auto kbuf_of = [&](auto JC) -> unsigned char* {
+  auto kbuf_of = [&](auto JC) __attribute__((always_inline)) -> unsigned char* {
     constexpr int J = decltype(JC)::value;
     if constexpr (J == 0) return kb0;
     else if constexpr (J == 1) return kb1;
@@ -241,7 +240,7 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(MfmaArgs args) {
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int g = lane >> 4, c16 = lane & 15;
-  const int hgrp = wave & 3, kh = wave >> 2;   // S phase: head block, key half
+  const int hgrp = wave & 3, kh = wave >> 2;   // head block; D half in S, key half in P
 
   // query row: consecutive rows stay on one XCD (workgroups go round-robin
   // over the 8 XCDs), so neighbouring rows share window rows in one L2
@@ -280,24 +279,34 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(MfmaArgs args) {
     const long hi = min(t, wp0 + (long)p.L_win - 1);
     if (hi >= lo) { n_win = (int)(hi - lo + 1); r_lo = (int)(lo - wp0); }
   }
-  int npool = 0;
+  int npool = 0, pool_stand_in = 0;
   if (p.dense) {
     npool = p.pool ? ready_count(t, p.m, p.T) : 0;
   } else if (p.k > 0 && p.pool) {
-    // stage the index row in LDS; the last non-empty slot bounds the list
+    // the last non-empty slot of the index row bounds the list; the row of the
+    // first non-empty one stands in for the empty slots
     const int* idx_row = p.idx + row * p.k;
-    int last = -1;
+    int last = -1, first = p.k;
     for (int j = tid; j < p.k; j += NT) {
       const int w = idx_row[j];
-      idx_s[j] = w;
-      if (w >= 0 && w < p.T) last = j;
+      if (w >= 0 && w < p.T) { last = j; first = min(first, j); }
     }
 #pragma unroll
-    for (int sh = 32; sh > 0; sh >>= 1) last = max(last, __shfl_xor(last, sh, 64));
-    if (lane == 0) flags[2 + wave] = last;
+    for (int sh = 32; sh > 0; sh >>= 1) {
+      last = max(last, __shfl_xor(last, sh, 64));
+      first = min(first, __shfl_xor(first, sh, 64));
+    }
+    if (lane == 0) { flags[2 + wave] = last; flags[10 + wave] = first; }
     __syncthreads();
 #pragma unroll
-    for (int q = 0; q < NW; ++q) npool = max(npool, flags[2 + q] + 1);
+    for (int q = 0; q < NW; ++q) {
+      npool = max(npool, flags[2 + q] + 1);
+      first = min(first, flags[10 + q]);
+    }
+    // (values read back from LDS or memory: made wave-uniform explicitly so
+    // that they stay in scalar registers)
+    npool = __builtin_amdgcn_readfirstlane(npool);
+    if (npool > 0) pool_stand_in = __builtin_amdgcn_readfirstlane(idx_row[first]);
   }
   const int WT = (n_win + kNK - 1) / kNK;
   const int ntiles = WT + (npool + kNK - 1) / kNK;
@@ -308,73 +317,119 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(MfmaArgs args) {
                                  : nullptr;
   const u16* pool_base = p.pool ? reinterpret_cast<const u16*>(p.pool) + (size_t)b * p.T * D
                                 : nullptr;
-  const __amdgpu_buffer_rsrc_t rs_win = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<u16*>(win_base), 0, win_base ? p.L_win * D * 2 : 0, 0x00020000);
-  const __amdgpu_buffer_rsrc_t rs_pool = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<u16*>(pool_base), 0, pool_base ? p.T * D * 2 : 0, 0x00020000);
+  // gather descriptors are built per tile from these (a zero size past the
+  // tile range: the loads then fill zeros)
+  const int win_bytes = win_base ? p.L_win * D * 2 : 0;
+  const int pool_bytes = pool_base ? p.T * D * 2 : 0;
+  const int lane_off = lane << 4;
 
-  // row id of key j of a tile: kv_win / pool row of this sequence, -1 = empty
-  auto rid_of = [&](int tile, int j) -> int {
+  // row ids of this wave's 4 rows (4w .. 4w+3) of a tile: kv_win / pool row of
+  // this sequence, -1 = empty (or past the tile range).  Wave-uniform: the
+  // index entries come in with scalar loads (read through the constant
+  // address space: the index is never written while the kernel runs).
+  typedef __attribute__((address_space(4))) const int cint;
+  cint* idx_row = p.idx ? (cint*)(p.idx + row * p.k) : nullptr;
+  typedef int i32x4 __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(4))) const i32x4 ci32x4;
+  auto rid4 = [=](int tile) __attribute__((always_inline)) -> int4 {
+    int4 r = make_int4(-1, -1, -1, -1);
+    if (tile >= tile1) return r;
     if (tile < WT) {
-      const int jj = tile * kNK + j;
-      return jj < n_win ? r_lo + jj : -1;
+      const int jj = tile * kNK + wave * 4;
+      r.x = jj + 0 < n_win ? r_lo + jj + 0 : -1;
+      r.y = jj + 1 < n_win ? r_lo + jj + 1 : -1;
+      r.z = jj + 2 < n_win ? r_lo + jj + 2 : -1;
+      r.w = jj + 3 < n_win ? r_lo + jj + 3 : -1;
+      return r;
     }
-    const int jj = (tile - WT) * kNK + j;
-    if (jj >= npool) return -1;
-    const int w = p.dense ? jj : idx_s[jj];
-    return (w >= 0 && w < p.T) ? w : -1;
+    const int jj = (tile - WT) * kNK + wave * 4;
+    int4 w;
+    if (p.dense) {
+      w = make_int4(jj, jj + 1, jj + 2, jj + 3);
+    } else if (jj + 4 <= p.k) {
+      const i32x4 v = *(ci32x4*)(idx_row + jj);  // one scalar load of the 4 entries
+      w = make_int4(v[0], v[1], v[2], v[3]);
+    } else {
+      w.x = jj + 0 < p.k ? idx_row[jj + 0] : -1;
+      w.y = jj + 1 < p.k ? idx_row[jj + 1] : -1;
+      w.z = jj + 2 < p.k ? idx_row[jj + 2] : -1;
+      w.w = jj + 3 < p.k ? idx_row[jj + 3] : -1;
+    }
+    r.x = (jj + 0 < npool && w.x >= 0 && w.x < p.T) ? w.x : -1;
+    r.y = (jj + 1 < npool && w.y >= 0 && w.y < p.T) ? w.y : -1;
+    r.z = (jj + 2 < npool && w.z >= 0 && w.z < p.T) ? w.z : -1;
+    r.w = (jj + 3 < npool && w.w >= 0 && w.w < p.T) ? w.w : -1;
+    return r;
   };
 
   // this wave's share of a tile's gather into buffer J: rows 4*wave ..
   // 4*wave+3, one 1 KiB load per row (and one 8-lane load of the last 128
   // bytes when D = 576)
-  auto issue = [&](auto JC, int tile) {
+  // An empty slot gathers a stand-in row of the same tensor (finite data that
+  // the -inf bias of the slot cancels: its probability is exactly 0); a tile
+  // past the range gathers through a zero-size descriptor (zero fill).  The
+  // row is wave-uniform: its offset goes in the scalar operand, so the
+  // per-lane operand is the loop-invariant lane_off (the compiler's wait-count
+  // model treats a register that fed a gather as pending until the gather
+  // lands, so a per-gather temporary reused later for other data would cost a
+  // wait).
+  auto issue = [=](auto JC, int tile, const int4 rids) __attribute__((always_inline)) {
     constexpr int J = decltype(JC)::value;
     unsigned char* kbuf = kbuf_of(JC);
-    int my_rid = -1;
-    if (lane < 4) {
-      my_rid = rid_of(tile, wave * 4 + lane);
-      rid_s[J * kNK + wave * 4 + lane] = my_rid;
-    }
-    const __amdgpu_buffer_rsrc_t rs = tile < WT ? rs_win : rs_pool;
+    const int rl = lane == 0 ? rids.x : lane == 1 ? rids.y : lane == 2 ? rids.z : rids.w;
+    if (lane < 4) bias_s[J * kNK + wave * 4 + lane] = rl >= 0 ? 0.f : -INFINITY;
+    const bool win = tile < WT;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<u16*>(win ? win_base : pool_base), 0,
+        tile >= tile1 ? 0 : win ? win_bytes : pool_bytes, 0x00020000);
+    const int stand_in = win ? r_lo : pool_stand_in;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int r = wave * 4 + q;
-      const int rid = __shfl(my_rid, q, 64);
-      const int off = rid >= 0 ? rid * (D * 2) + (lane << 4) : 0x7ffffff0;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(kbuf + r * KT::ROWB), 16, off,
-                                               0, 0, 0);
+      const int rid = q == 0 ? rids.x : q == 1 ? rids.y : q == 2 ? rids.z : rids.w;
+      const int soff = (rid >= 0 ? rid : stand_in) * (D * 2);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(kbuf + r * KT::ROWB), 16,
+                                               lane_off, soff, 0, 0);
       if constexpr (D > 512) {
+        // (the immediate offset would move the LDS address too: the extra
+        // 1024 bytes go in the scalar offset, which addresses memory only)
         if (lane < (D - 512) / 8)
           __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(kbuf + r * KT::ROWB + 1024),
-                                                   16, rid >= 0 ? off + 1024 : off, 0, 0, 0);
+                                                   16, lane_off, soff + 1024, 0, 0);
       }
     }
   };
 
-  // ---- Q fragments (B operand of S^T = K Q^T): head hq, dims 32ks + 8g .. +7
+  // ---- Q fragments (B operand of S^T = K Q^T): head hq, this wave's half of
+  // the k-steps, dims 32ks + 8g .. +7
   const int hq = 16 * hgrp + c16;
-  uint4 qraw[KS];
+  const int ks0 = KH * kh;                       // first k-step of this wave
+  uint4 qraw[KH];
   {
     const u16* qrow = reinterpret_cast<const u16*>(p.q) + (row * H + h0 + hq) * D;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      qraw[ks] = *reinterpret_cast<const uint4*>(qrow + 32 * ks + 8 * g);
+    for (int ks = 0; ks < KH; ++ks)
+      qraw[ks] = *reinterpret_cast<const uint4*>(qrow + 32 * (ks0 + ks) + 8 * g);
   }
+  // the sink logit, loaded before the gathers so that waiting for it does not
+  // wait for them
+  const bool use_sink = p.sink && !split_mode;
+  const float sink_l2 = use_sink ? p.sink[h0 + hq] * kLog2e : -INFINITY;
   if (tid == 0) { flags[0] = 1; flags[1] = 1; }
-  if (tile0 + 0 < tile1) issue(std::integral_constant<int, 0>{}, tile0 + 0);
-  if (tile0 + 1 < tile1) issue(std::integral_constant<int, 1>{}, tile0 + 1);
-  if (tile0 + 2 < tile1) issue(std::integral_constant<int, 2>{}, tile0 + 2);
-  if constexpr (NBUF == 4)
-    if (tile0 + 3 < tile1) issue(std::integral_constant<int, 3>{}, tile0 + 3);
+  // the first NBUF-1 gathers (issued whether or not the tiles exist, as in the
+  // loop, so that the wait counts are the same on every path)
+  issue(std::integral_constant<int, 0>{}, tile0, rid4(tile0));
+  issue(std::integral_constant<int, 1>{}, tile0 + 1, rid4(tile0 + 1));
+  if constexpr (NBUF == 4) issue(std::integral_constant<int, 2>{}, tile0 + 2, rid4(tile0 + 2));
 
   // rotate the rope slice of q at +t, round to bf16
-  bf16x8 qf[KS];
+  bf16x8 qf[KH];
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    const int d0 = 32 * ks + 8 * g;
+  for (int ks = 0; ks < KH; ++ks) {
+    // the rope slice is the last R dims: the last R/32 k-steps of the upper half
+    const int d0 = 32 * (ks0 + ks) + 8 * g;
     uint4 u = qraw[ks];
-    if (32 * ks + 32 > rbase && d0 >= rbase) {
+    if (ks >= KH - R / 32 && kh == 1) {
       float v[8] = {bf_lo(u.x), bf_hi(u.x), bf_lo(u.y), bf_hi(u.y),
                     bf_lo(u.z), bf_hi(u.z), bf_lo(u.w), bf_hi(u.w)};
 #pragma unroll
@@ -391,13 +446,10 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(MfmaArgs args) {
   }
 
   // ---- softmax state of head hq (replicated over the 4 lane groups, and the
-  // same in both key-half waves), log2 domain; lrun sums this wave's keys only
+  // same in both waves of the head block), log2 domain; lrun sums the keys of
+  // this wave's key half only
   const float sl2 = p.scale * kLog2e;
-  float mref = -INFINITY, lrun = 0.f;
-  if (p.sink && !split_mode) {
-    mref = p.sink[h0 + hq] * kLog2e;
-    if (kh == 0) lrun = 1.f;
-  }
+  float mref = sink_l2, lrun = (use_sink && kh == 0) ? 1.f : 0.f;
 
   f32x4 acc[4][NB];
 #pragma unroll
@@ -406,75 +458,95 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(MfmaArgs args) {
     for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int col0 = 64 * wave + 4 * c16;          // this lane's first output column
 
-  // one tile, read from buffer J; the gather NBUF-1 tiles ahead goes to the
-  // buffer the previous tile used
-  auto step = [&](auto JC, int tile) {
-    constexpr int J = decltype(JC)::value;
-    const int it = tile - tile0;
-    const int par = it & 1;
-    // this wave's loads of `tile` are done once at most the loads of the
-    // tiles issued after it are still outstanding
-    const int later = min(NBUF - 2, tile1 - 1 - tile);
-    if (later >= 2) wait_vmcnt<2 * KT::G>();
-    else if (later == 1) wait_vmcnt<KT::G>();
-    else wait_vmcnt<0>();
-    lds_barrier();  // every wave's loads of this tile have landed
-    if (tile + NBUF - 1 < tile1)
-      issue(std::integral_constant<int, (J + NBUF - 1) % NBUF>{}, tile + NBUF - 1);
-    if (tid == 0) flags[par ^ 1] = 0;  // the next tile's rescale flag starts clear
+  // this wave's partial S^T of the pending tile (its half of the k-steps),
+  // key blocks 0 and 1; empty key slots hold -inf
+  f32x4 sp[2];
 
-    const unsigned char* kbuf = kbuf_of(JC);
-    // ---- S phase: S^T[16 keys][16 heads] (groups of 4 k-steps; the fence
-    // bounds the K fragments held in registers at once)
-    __builtin_amdgcn_sched_barrier(0);
-    f32x4 st0 = f32x4{0.f, 0.f, 0.f, 0.f}, st1 = st0;  // even / odd k-steps
-    // this lane supplies K row 16kh + c16, 16-byte chunk 4ks + g
-    const unsigned char* krow = kbuf + (16 * kh + c16) * KT::ROWB + 16 * g;
+  // ---- S phase pieces.  Lane supplies K row 16kb + c16, 16-byte chunk
+  // 4(ks0 + ks) + g for key block kb and k-step ks of this wave's half.
+  auto k_row = [&](auto JC) __attribute__((always_inline)) -> const unsigned char* {
+    return kbuf_of(JC) + c16 * KT::ROWB + 16 * g + 64 * ks0;
+  };
+  // bias the partials (0 / -inf per key slot; the lower D-half wave adds it,
+  // so the sum of the two partials carries it once) and publish them for the
+  // other wave of the head block
+  auto s_finish = [&](auto JC, const f32x4 st0, const f32x4 st1) __attribute__((always_inline)) {
+    constexpr int J = decltype(JC)::value;
+    sp[0] = st0;
+    sp[1] = st1;
+    if (kh == 0) {
+      sp[0] += *reinterpret_cast<const f32x4*>(bias_s + J * kNK + 4 * g);
+      sp[1] += *reinterpret_cast<const f32x4*>(bias_s + J * kNK + 16 + 4 * g);
+    }
+    *reinterpret_cast<f32x4*>(spart + (wave * 2 + 0) * 64 * 4 + 4 * lane) = sp[0];
+    *reinterpret_cast<f32x4*>(spart + (wave * 2 + 1) * 64 * 4 + 4 * lane) = sp[1];
+  };
+  // the S phase on its own (first tile): groups of 2 k-steps x 2 key blocks,
+  // the fence bounds the K fragments held in registers at once
+  auto s_phase = [&](auto JC) __attribute__((always_inline)) {
+    const unsigned char* krow = k_row(JC);
+    f32x4 st0 = f32x4{0.f, 0.f, 0.f, 0.f}, st1 = st0;  // key blocks 0 / 1
 #pragma unroll
-    for (int k4 = 0; k4 < KS; k4 += 4) {
-      uint4 kv[4];
+    for (int k2 = 0; k2 < KH; k2 += 2) {
+      uint4 kv[2][2];
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const int ks = k4 + kk;
-        if (ks < KS) kv[kk] = *reinterpret_cast<const uint4*>(krow + 64 * ks);
-      }
+      for (int kk = 0; kk < 2; ++kk)
+        if (k2 + kk < KH) {
+          kv[kk][0] = *reinterpret_cast<const uint4*>(krow + 64 * (k2 + kk));
+          kv[kk][1] = *reinterpret_cast<const uint4*>(krow + 16 * KT::ROWB + 64 * (k2 + kk));
+        }
 #pragma unroll
-      for (int kk = 0; kk < 4; kk += 2) {
-        if (k4 + kk < KS) st0 = mfma16x16x32(as_bf16x8(kv[kk]), qf[k4 + kk], st0);
-        if (k4 + kk + 1 < KS) st1 = mfma16x16x32(as_bf16x8(kv[kk + 1]), qf[k4 + kk + 1], st1);
-      }
+      for (int kk = 0; kk < 2; ++kk)
+        if (k2 + kk < KH) {
+          st0 = mfma16x16x32(as_bf16x8(kv[kk][0]), qf[k2 + kk], st0);
+          st1 = mfma16x16x32(as_bf16x8(kv[kk][1]), qf[k2 + kk], st1);
+        }
       __builtin_amdgcn_sched_barrier(0);
     }
-    const f32x4 st = st0 + st1;
-    // lane holds keys 16kh + 4g + j of head hq
-    const int4 rv = *reinterpret_cast<const int4*>(rid_s + J * kNK + 16 * kh + 4 * g);
-    float sv[4] = {rv.x >= 0 ? st[0] * sl2 : -INFINITY, rv.y >= 0 ? st[1] * sl2 : -INFINITY,
-                   rv.z >= 0 ? st[2] * sl2 : -INFINITY, rv.w >= 0 ? st[3] * sl2 : -INFINITY};
-    float tmax = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
-    tmax = fmaxf(tmax, shfl_xor(tmax, 16));
-    tmax = fmaxf(tmax, shfl_xor(tmax, 32));
-    if (g == 0) tm_s[kh * HG + hq] = tmax;
-    lds_barrier();
-    tmax = fmaxf(tmax, tm_s[(kh ^ 1) * HG + hq]);
+    s_finish(JC, st0, st1);
+  };
+
+  // ---- softmax of the pending tile, once both waves' partials are in LDS:
+  // the full logits of the 32 keys of head hq (identical in both waves: the
+  // two partials are added in either order), the new reference max, P of this
+  // wave's key half to LDS (key 16kh + 4g + j at position 8g + 4kh + j), the
+  // rescale factor of head hq, and the rescale flag of parity par
+  auto softmax = [&](auto JC, int par) __attribute__((always_inline)) {
+    const int pw = wave ^ 4;
+    const f32x4 o0 = *reinterpret_cast<const f32x4*>(spart + (pw * 2 + 0) * 64 * 4 + 4 * lane);
+    const f32x4 o1 = *reinterpret_cast<const f32x4*>(spart + (pw * 2 + 1) * 64 * 4 + 4 * lane);
+    // raw logits; the scale (> 0) commutes with the max and goes into the
+    // exponent's fused multiply-add
+    const f32x4 f0 = sp[0] + o0, f1 = sp[1] + o1;
+    const float m0 = fmaxf(fmaxf(f0[0], f0[1]), fmaxf(f0[2], f0[3]));
+    const float m1 = fmaxf(fmaxf(f1[0], f1[1]), fmaxf(f1[2], f1[3]));
+    const float tmax = xgroup_max(fmaxf(m0, m1)) * sl2;
+    const f32x4 sv = kh ? f1 : f0;
     const float mnew = (tmax > mref + kLazy) ? tmax : mref;
-    const float alpha = (mnew == mref) ? 1.f : exp2f(mref - mnew);
+    const float alpha = (mnew == mref) ? 1.f : __builtin_amdgcn_exp2f(mref - mnew);
     const float mbase = (mnew == -INFINITY) ? 0.f : mnew;
-    const float p0 = exp2f(sv[0] - mbase), p1 = exp2f(sv[1] - mbase);
-    const float p2 = exp2f(sv[2] - mbase), p3 = exp2f(sv[3] - mbase);
-    float psum = (p0 + p1) + (p2 + p3);
-    psum += shfl_xor(psum, 16);
-    psum += shfl_xor(psum, 32);
-    lrun = lrun * alpha + psum;
+    const float p0 = __builtin_amdgcn_exp2f(fmaf(sv[0], sl2, -mbase));
+    const float p1 = __builtin_amdgcn_exp2f(fmaf(sv[1], sl2, -mbase));
+    const float p2 = __builtin_amdgcn_exp2f(fmaf(sv[2], sl2, -mbase));
+    const float p3 = __builtin_amdgcn_exp2f(fmaf(sv[3], sl2, -mbase));
+    lrun = lrun * alpha + xgroup_sum((p0 + p1) + (p2 + p3));
     mref = mnew;
-    // P row of head hq; key 16*kh + 4g + j sits at position 8g + 4*kh + j
-    *reinterpret_cast<uint2*>(Ps + hq * kNK + 8 * g + 4 * kh) =
+    *reinterpret_cast<uint2*>(Ps + hq * kPS + 8 * g + 4 * kh) =
         make_uint2(pack2(p0, p1), pack2(p2, p3));
     if (kh == 0 && g == 0) alpha_s[hq] = alpha;
     if (kh == 0 && __ballot(alpha != 1.f) != 0ull && lane == 0) flags[par] = 1;
-    lds_barrier();
+  };
 
-    // ---- PV phase: O[all 64 heads][this wave's 64 columns] += P V
-    __builtin_amdgcn_sched_barrier(0);
+  // ---- PV phase of the tile in buffer J: O[all 64 heads][this wave's 64
+  // columns] += P V (after the rescale when some head raised its maximum),
+  // then, when WITH_S, the S phase of the tile in the next buffer.  The
+  // operand reads run ahead of the matrix instructions: the PV operands and
+  // the first K fragments are read before the PV products, and every group of
+  // S products is followed by the reads of the group after next.
+  auto pv_s = [&](auto JC, auto WITH_S, int par) __attribute__((always_inline)) {
+    constexpr bool kS = decltype(WITH_S)::value;
+    using JN = std::integral_constant<int, (decltype(JC)::value + 1) % NBUF>;
+    const unsigned char* kbuf = kbuf_of(JC);
     if (flags[par]) {
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb) {
@@ -486,10 +558,11 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(MfmaArgs args) {
         }
       }
     }
+    __builtin_amdgcn_sched_barrier(0);
     bf16x8 pa[4];
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb)
-      pa[mb] = as_bf16x8(*reinterpret_cast<const uint4*>(Ps + (16 * mb + c16) * kNK + 8 * g));
+      pa[mb] = as_bf16x8(*reinterpret_cast<const uint4*>(Ps + (16 * mb + c16) * kPS + 8 * g));
     // V: for key position q (key 16*(q/4) + 4g + q%4), this lane's 4 columns
     uint32_t vr[8][2];
     const unsigned char* vcol = kbuf + 4 * g * KT::ROWB + 2 * col0;
@@ -499,29 +572,86 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(MfmaArgs args) {
           vcol + (16 * (q >> 2) + (q & 3)) * KT::ROWB);
       vr[q][0] = u.x; vr[q][1] = u.y;
     }
+    uint4 kv[KH][2];
+    const unsigned char* krow = k_row(JN{});
+    // the first half of the K fragments now, the second half once the PV
+    // operands are consumed (bounds the registers held at once)
+    constexpr int KA = KH / 2;
+    auto k_reads = [&](int k_lo, int k_hi) __attribute__((always_inline)) {
+#pragma unroll
+      for (int ks = 0; ks < KH; ++ks)
+        if (ks >= k_lo && ks < k_hi) {
+          kv[ks][0] = *reinterpret_cast<const uint4*>(krow + 64 * ks);
+          kv[ks][1] = *reinterpret_cast<const uint4*>(krow + 16 * KT::ROWB + 64 * ks);
+        }
+    };
+    if constexpr (kS) k_reads(0, KA);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       const int dw = nb >> 1;
       uint32_t f[4];
 #pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        const uint32_t a = vr[2 * d][dw], bq = vr[2 * d + 1][dw];
-        f[d] = (nb & 1) ? ((a >> 16) | (bq & 0xffff0000u)) : ((a & 0xffffu) | (bq << 16));
-      }
+      for (int d = 0; d < 4; ++d)  // low halves (even nb) or high halves (odd nb) of two keys
+        f[d] = __builtin_amdgcn_perm(vr[2 * d + 1][dw], vr[2 * d][dw],
+                                     (nb & 1) ? 0x07060302u : 0x05040100u);
       const bf16x8 vb = as_bf16x8(make_uint4(f[0], f[1], f[2], f[3]));
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb) acc[mb][nb] = mfma16x16x32(pa[mb], vb, acc[mb][nb]);
     }
     __builtin_amdgcn_sched_barrier(0);
+    if constexpr (kS) {
+      k_reads(KA, KH);
+      f32x4 st0 = f32x4{0.f, 0.f, 0.f, 0.f}, st1 = st0;  // key blocks 0 / 1
+#pragma unroll
+      for (int ks = 0; ks < KH; ++ks) {
+        st0 = mfma16x16x32(as_bf16x8(kv[ks][0]), qf[ks], st0);
+        st1 = mfma16x16x32(as_bf16x8(kv[ks][1]), qf[ks], st1);
+      }
+      s_finish(JN{}, st0, st1);
+    }
   };
 
+  // ---- software pipeline over the tiles, two barriers per tile:
+  //   X(j): partials of tile j published; buffer (j-1) and P free
+  //         -> softmax of tile j, gather tile j+NBUF-1 into buffer (j-1)
+  //   Y(j): P(j) and the rescale factors visible; tile j+1 landed
+  //         -> PV of tile j, then S of tile j+1 (matrix cores back to back)
+  // Gathers are issued past the last tile as well (every row empty: the
+  // buffer is zero-filled), so that every iteration issues the same loads and
+  // the wait counts are exact; the row ids of the next gather are looked up
+  // an iteration ahead.
+  constexpr int kAhead = (NBUF - 2) * KT::G;   // loads still in flight at a wait
+  wait_vmcnt<kAhead>();
+  lds_barrier();  // tile0 landed
+  s_phase(std::integral_constant<int, 0>{});
+  int4 rid_next = rid4(tile0 + NBUF - 1);
+  auto iter = [&](auto JC, int j) __attribute__((always_inline)) {
+    constexpr int J = decltype(JC)::value;
+    const int par = (j - tile0) & 1;
+    const bool live = j < tile1;
+    lds_barrier();  // X(j)
+    if (live) softmax(JC, par);
+    issue(std::integral_constant<int, (J + NBUF - 1) % NBUF>{}, j + NBUF - 1, rid_next);
+    wait_vmcnt<kAhead>();  // this wave's loads of tile j+1 have landed
+    lds_barrier();  // Y(j)
+    if (tid == 0) flags[par ^ 1] = 0;  // the next tile's rescale flag starts clear
+    // the S phase runs after the last tile too, on a zero-filled buffer: one
+    // code path keeps the register allocation tight
+    if (live) pv_s(JC, std::true_type{}, par);
+    rid_next = rid4(j + NBUF);
+  };
+  // whole rounds of NBUF iterations: the ones past the last tile only keep the
+  // barriers and the (empty) gathers, so that the loads issued are the same
+  // on every path through the loop
   for (int tile = tile0; tile < tile1; tile += NBUF) {
-    step(std::integral_constant<int, 0>{}, tile);
-    if (tile + 1 < tile1) step(std::integral_constant<int, 1>{}, tile + 1);
-    if (tile + 2 < tile1) step(std::integral_constant<int, 2>{}, tile + 2);
-    if constexpr (NBUF == 4)
-      if (tile + 3 < tile1) step(std::integral_constant<int, 3>{}, tile + 3);
+    iter(std::integral_constant<int, 0>{}, tile);
+    iter(std::integral_constant<int, 1>{}, tile + 1);
+    iter(std::integral_constant<int, 2>{}, tile + 2);
+    if constexpr (NBUF == 4) iter(std::integral_constant<int, 3>{}, tile + 3);
   }
+  // no gather may still be writing this workgroup's LDS when it exits
+  wait_vmcnt<0>();
 
   // ---- epilogue: l = sum over both key halves
   if (kh == 1 && g == 0) l_s[hq] = lrun;
@@ -638,11 +768,10 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnParams p, const f
 // D = 512 (CSA / HCA) or 576 (DSA: 512 latent + 64 rope), dv = 512, rope 64.
 
 bool mfma_shape(int H, int D, int dv, int rope_dim, int k) {
-  return H % 64 == 0 && dv == 512 && rope_dim == 64 && (D == 512 || D == 576) &&
-         k <= kIdxCap;
+  (void)k;
+  return H % 64 == 0 && dv == 512 && rope_dim == 64 && (D == 512 || D == 576);
 }
 
-int mfma_nbuf(int) { return 3; }
 
 
 
@@ -711,10 +840,9 @@ hipError_t launch_attention(const AttnParams& p, const AttnPlan& plan, void* ws,
   a.nsplit = split ? plan.nsplit : 1;
   a.tiles_per_split = split ? plan.tiles_per_split : (1 << 30);
   a.rows_per_xcd = (int)((rows + 7) / 8);
-  a.idx_cap = p.dense ? 0 : p.k;
   dim3 grid((unsigned)(8 * (long)a.rows_per_xcd), a.nsplit, p.H / 64);
   if (p.D == 512)
-    hipLaunchKernelGGL((attn_mfma_kernel<512, 3>), grid, dim3(512), 0, s, a);
+    hipLaunchKernelGGL((attn_mfma_kernel<512, 4>), grid, dim3(512), 0, s, a);
   else
     hipLaunchKernelGGL((attn_mfma_kernel<576, 3>), grid, dim3(512), 0, s, a);
   hipError_t err = hipGetLastError();
