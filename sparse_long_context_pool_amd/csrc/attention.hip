@@ -180,37 +180,57 @@ __device__ __forceinline__ void wait_vmcnt() {
 // one instruction per row (plus an 8-lane one for the last 128 bytes when
 // D = 576); lanes whose row slot is empty read past the buffer bound, which
 // writes zeros.
+//
+// When D > 512 (a 512-wide latent part followed by the rope dims) the first 512
+// dims of each row are laid out as above and the rest goes to a tail area: one
+// block per wave of 8 rows, chunk-major ([16-byte chunk][row]), blocks 1152
+// bytes apart.  One 64-lane load then gathers the tails of a wave's 8 rows,
+// and the S-phase reads of the tail (16 rows, one chunk) still fall in
+// distinct banks.
 template <int D>
 struct KTile {
-  static constexpr int ROWB = D * 2 + 16;
+  static constexpr int MAIN = D > 512 ? 512 : D;    // dims in the row area
+  static constexpr int ROWB = MAIN * 2 + 16;
+  static constexpr int TAIL = D - MAIN;             // dims in the tail area
+  static constexpr int TBLK = 1152;                 // tail block stride (8 rows)
+  static_assert(TAIL == 0 || TAIL == 64, "tail of 64 dims");
   static constexpr int BYTES = kNK * ROWB;
-  static constexpr int G = (D > 512) ? 8 : 4;   // loads per wave per tile (8 waves)
+  static constexpr int TBYTES = TAIL ? 4 * TBLK : 16;
 };
 
 // Split workspace (fp32): [rows][nsplit][H][2] running (max, sum) in the log2
 // domain, then [rows][nsplit][H][dv] unnormalised partial outputs.
 //
-// One workgroup = one query row x one group of 64 heads, 8 waves (2 per SIMD).
-// S phase: wave w computes S^T for heads 16(w%4) .. +15 over keys 16(w/4) ..
-// +15 of the 32-key tile; the two key halves of a head exchange their tile
-// maxima through LDS.  PV phase: wave w owns output columns 64w .. 64w+63,
-// lane c16 the 4 consecutive columns 64w + 4*c16 .. (one 8-byte LDS read per
-// key, 8-byte output stores, lane-local de-rotation).  The gathers run
-// NBUF-1 tiles ahead of the compute.
+// One workgroup = one query row x one group of 64 heads, 8 waves in two roles,
+// one wave of each role per SIMD (so the hardware interleaves them):
+//   S waves (0..3): wave w owns heads 16w .. 16w+15 for the S products, the
+//     softmax (all keys of a tile, so a head's softmax state lives in one
+//     wave) and the gathers (rows 8w .. 8w+7 of each tile);
+//   PV waves (4..7): wave 4+w owns output columns 128w .. 128w+127 and their
+//     accumulators.
+// S phase: S^T[keys][heads] = K Q^T with 16x16x32 matrix instructions, the
+// query fragments held in registers; a lane ends with the logits of keys
+// 4g + r and 16 + 4g + r (g = lane / 16, r = 0..3) of its head, which are
+// exactly an A operand of the PV product in the key order position
+// 8g + e <-> key 16(e/4) + 4g + (e%4).  P goes through LDS in that order, and
+// V is read with the gfx950 transposing LDS load (ds_read_b64_tr_b16: 4 keys
+// x 1 column per lane) in the same key order.
 //
-// Softmax: a per-head reference max m (the sink logit to start with) is raised
-// only when a tile's max exceeds it by more than 8 (log2 units); otherwise the
-// probabilities exp2(s - m) may reach 2^8, which bf16 and fp32 carry exactly
-// in relative terms, and O / l is unchanged.  So the accumulators are rescaled
-// only in the rare tile that raises m.
+// Pipeline, one barrier per tile: between barriers B(j) and B(j+1) the S
+// waves gather tile j+NBUF-1 (into the buffer of tile j-1) and run S + softmax
+// of tile j+1 (P into the other P buffer) while the PV waves run PV of tile
+// j; the S waves then wait for their loads of tile j+2.
+//
 template <int D, int NBUF>
 __global__ __launch_bounds__(512) void attn_mfma_kernel(MfmaArgs args) {
-  constexpr int NW = 8, NT = 512, HG = 64, NB = 4;
+  constexpr int NW = 8, NT = 512, HG = 64, NB = 8;   // NB: 16-column blocks per PV wave
   constexpr int KS = D / 32;
-  constexpr int KH = KS / 2;  // k-steps per wave: the two waves of a head block split D
   constexpr int R = 64, half = R / 2, rbase = D - R;
-  constexpr float kLazy = 8.f;
+  constexpr float kRestart = 64.f;
+  constexpr int NS = 4;                              // S waves (and PV waves)
+  constexpr int RPW = kNK / NS;                      // gathered rows per S wave per tile
   using KT = KTile<D>;
+  constexpr int G = RPW + (KT::TAIL ? 1 : 0);         // gather loads per wave per tile
   static_assert(NBUF == 3 || NBUF == 4, "buffer count");
   // One static array per K buffer: with distinct objects the compiler can
   // tell that an in-flight gather into one buffer does not alias reads of
@@ -219,14 +239,17 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(MfmaArgs args) {
   __shared__ __attribute__((aligned(16))) unsigned char kb1[KT::BYTES];
   __shared__ __attribute__((aligned(16))) unsigned char kb2[KT::BYTES];
   __shared__ __attribute__((aligned(16))) unsigned char kb3[NBUF == 4 ? KT::BYTES : 16];
+  // tail areas (D > 512), one object per buffer as well
+  __shared__ __attribute__((aligned(16))) unsigned char tb0[KT::TBYTES];
+  __shared__ __attribute__((aligned(16))) unsigned char tb1[KT::TBYTES];
+  __shared__ __attribute__((aligned(16))) unsigned char tb2[KT::TBYTES];
+  __shared__ __attribute__((aligned(16))) unsigned char tb3[NBUF == 4 ? KT::TBYTES : 16];
   // every other LDS array is static as well, for the same reason
-  __shared__ __attribute__((aligned(16))) u16 Ps[HG * kPS];        // P, bf16
-  __shared__ __attribute__((aligned(16))) float spart[NW * 2 * 64 * 4];  // S^T partials
-  __shared__ __attribute__((aligned(16))) float alpha_s[HG];       // rescale factors
-  __shared__ __attribute__((aligned(16))) float fin_s[HG];         // 1/l
-  __shared__ __attribute__((aligned(16))) float l_s[HG];           // second half's sum
-  __shared__ __attribute__((aligned(16))) float bias_s[NBUF * kNK];  // 0 / -inf per key slot
-  __shared__ int flags[20];                                        // rescale, scan
+  __shared__ __attribute__((aligned(16))) u16 Ps[2 * HG * kPS];     // P, bf16, 2 tiles
+  __shared__ int rflag_s[2 * NS];                                   // restart requests
+  __shared__ __attribute__((aligned(16))) float bias_s[NBUF * kNK]; // 0 / -inf per slot
+  __shared__ __attribute__((aligned(16))) float fin_s[HG];          // 1/l
+  __shared__ int flags[20];                                         // scan
   const AttnParams& p = args.p;
   auto kbuf_of = [&](auto JC) __attribute__((always_inline)) -> unsigned char* {
     constexpr int J = decltype(JC)::value;
@@ -235,12 +258,22 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(MfmaArgs args) {
     else if constexpr (J == 2) return kb2;
     else return kb3;
   };
+  auto tbuf_of = [&](auto JC) __attribute__((always_inline)) -> unsigned char* {
+    constexpr int J = decltype(JC)::value;
+    if constexpr (J == 0) return tb0;
+    else if constexpr (J == 1) return tb1;
+    else if constexpr (J == 2) return tb2;
+    else return tb3;
+  };
 
   // the wave index is uniform: keep it (and everything derived from it) scalar
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int g = lane >> 4, c16 = lane & 15;
-  const int hgrp = wave & 3, kh = wave >> 2;   // head block; D half in S, key half in P
+  const bool s_role = wave < NS;                  // S wave, else PV wave
+  const int w4 = wave & (NS - 1);
+  const int hq = 16 * w4 + c16;                   // S phase / softmax head
+  const int cbase = 128 * w4;                     // PV phase columns
 
   // query row: consecutive rows stay on one XCD (workgroups go round-robin
   // over the 8 XCDs), so neighbouring rows share window rows in one L2
@@ -323,113 +356,121 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(MfmaArgs args) {
   const int pool_bytes = pool_base ? p.T * D * 2 : 0;
   const int lane_off = lane << 4;
 
-  // row ids of this wave's 4 rows (4w .. 4w+3) of a tile: kv_win / pool row of
+  // row ids of this S wave's rows (8w .. 8w+7) of a tile: kv_win / pool row of
   // this sequence, -1 = empty (or past the tile range).  Wave-uniform: the
   // index entries come in with scalar loads (read through the constant
   // address space: the index is never written while the kernel runs).
   typedef __attribute__((address_space(4))) const int cint;
-  cint* idx_row = p.idx ? (cint*)(p.idx + row * p.k) : nullptr;
   typedef int i32x4 __attribute__((ext_vector_type(4)));
   typedef __attribute__((address_space(4))) const i32x4 ci32x4;
-  auto rid4 = [=](int tile) __attribute__((always_inline)) -> int4 {
-    int4 r = make_int4(-1, -1, -1, -1);
-    if (tile >= tile1) return r;
+  cint* idx_row = p.idx ? (cint*)(p.idx + row * p.k) : nullptr;
+  struct Rid8 { int r[RPW]; };
+  auto rid8 = [=](int tile) __attribute__((always_inline)) -> Rid8 {
+    Rid8 o;
+#pragma unroll
+    for (int q = 0; q < RPW; ++q) o.r[q] = -1;
+    if (tile >= tile1) return o;
     if (tile < WT) {
-      const int jj = tile * kNK + wave * 4;
-      r.x = jj + 0 < n_win ? r_lo + jj + 0 : -1;
-      r.y = jj + 1 < n_win ? r_lo + jj + 1 : -1;
-      r.z = jj + 2 < n_win ? r_lo + jj + 2 : -1;
-      r.w = jj + 3 < n_win ? r_lo + jj + 3 : -1;
-      return r;
+      const int jj = tile * kNK + w4 * RPW;
+#pragma unroll
+      for (int q = 0; q < RPW; ++q) o.r[q] = jj + q < n_win ? r_lo + jj + q : -1;
+      return o;
     }
-    const int jj = (tile - WT) * kNK + wave * 4;
-    int4 w;
+    const int jj = (tile - WT) * kNK + w4 * RPW;
+    int w[RPW];
     if (p.dense) {
-      w = make_int4(jj, jj + 1, jj + 2, jj + 3);
-    } else if (jj + 4 <= p.k) {
-      const i32x4 v = *(ci32x4*)(idx_row + jj);  // one scalar load of the 4 entries
-      w = make_int4(v[0], v[1], v[2], v[3]);
+#pragma unroll
+      for (int q = 0; q < RPW; ++q) w[q] = jj + q;
+    } else if (jj + RPW <= p.k) {
+#pragma unroll
+      for (int q = 0; q < RPW; q += 4) {  // scalar loads of 4 entries
+        const i32x4 v = *(ci32x4*)(idx_row + jj + q);
+        w[q] = v[0]; w[q + 1] = v[1]; w[q + 2] = v[2]; w[q + 3] = v[3];
+      }
     } else {
-      w.x = jj + 0 < p.k ? idx_row[jj + 0] : -1;
-      w.y = jj + 1 < p.k ? idx_row[jj + 1] : -1;
-      w.z = jj + 2 < p.k ? idx_row[jj + 2] : -1;
-      w.w = jj + 3 < p.k ? idx_row[jj + 3] : -1;
+#pragma unroll
+      for (int q = 0; q < RPW; ++q) w[q] = jj + q < p.k ? idx_row[jj + q] : -1;
     }
-    r.x = (jj + 0 < npool && w.x >= 0 && w.x < p.T) ? w.x : -1;
-    r.y = (jj + 1 < npool && w.y >= 0 && w.y < p.T) ? w.y : -1;
-    r.z = (jj + 2 < npool && w.z >= 0 && w.z < p.T) ? w.z : -1;
-    r.w = (jj + 3 < npool && w.w >= 0 && w.w < p.T) ? w.w : -1;
-    return r;
+#pragma unroll
+    for (int q = 0; q < RPW; ++q)
+      o.r[q] = (jj + q < npool && w[q] >= 0 && w[q] < p.T) ? w[q] : -1;
+    return o;
   };
 
-  // this wave's share of a tile's gather into buffer J: rows 4*wave ..
-  // 4*wave+3, one 1 KiB load per row (and one 8-lane load of the last 128
-  // bytes when D = 576)
-  // An empty slot gathers a stand-in row of the same tensor (finite data that
-  // the -inf bias of the slot cancels: its probability is exactly 0); a tile
-  // past the range gathers through a zero-size descriptor (zero fill).  The
-  // row is wave-uniform: its offset goes in the scalar operand, so the
-  // per-lane operand is the loop-invariant lane_off (the compiler's wait-count
-  // model treats a register that fed a gather as pending until the gather
-  // lands, so a per-gather temporary reused later for other data would cost a
-  // wait).
-  auto issue = [=](auto JC, int tile, const int4 rids) __attribute__((always_inline)) {
+  // This wave's share of a tile's gather into buffer J: rows 8w .. 8w+7, one
+  // 1 KiB load per row (and one 8-lane load of the last 128 bytes when D =
+  // 576).  An empty slot gathers a stand-in row of the same tensor (finite
+  // data that the -inf bias of the slot cancels: its probability is exactly
+  // 0); a tile past the range gathers through a zero-size descriptor (zero
+  // fill).  The row is wave-uniform: its offset goes in the scalar operand, so
+  // the per-lane operand is the loop-invariant lane_off (the compiler's
+  // wait-count model treats a register that fed a gather as pending until the
+  // gather lands, so a per-gather temporary reused later for other data would
+  // cost a wait).
+  auto issue = [=](auto JC, int tile, const Rid8 rids) __attribute__((always_inline)) {
     constexpr int J = decltype(JC)::value;
     unsigned char* kbuf = kbuf_of(JC);
-    const int rl = lane == 0 ? rids.x : lane == 1 ? rids.y : lane == 2 ? rids.z : rids.w;
-    if (lane < 4) bias_s[J * kNK + wave * 4 + lane] = rl >= 0 ? 0.f : -INFINITY;
+    int rl = -1;
+#pragma unroll
+    for (int q = 0; q < RPW; ++q) rl = lane == q ? rids.r[q] : rl;
+    if (lane < RPW) bias_s[J * kNK + w4 * RPW + lane] = rl >= 0 ? 0.f : -INFINITY;
     const bool win = tile < WT;
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<u16*>(win ? win_base : pool_base), 0,
         tile >= tile1 ? 0 : win ? win_bytes : pool_bytes, 0x00020000);
     const int stand_in = win ? r_lo : pool_stand_in;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int r = wave * 4 + q;
-      const int rid = q == 0 ? rids.x : q == 1 ? rids.y : q == 2 ? rids.z : rids.w;
-      const int soff = (rid >= 0 ? rid : stand_in) * (D * 2);
+    for (int q = 0; q < RPW; ++q) {
+      const int r = w4 * RPW + q;
+      const int soff = (rids.r[q] >= 0 ? rids.r[q] : stand_in) * (D * 2);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(kbuf + r * KT::ROWB), 16,
                                                lane_off, soff, 0, 0);
-      if constexpr (D > 512) {
-        // (the immediate offset would move the LDS address too: the extra
-        // 1024 bytes go in the scalar offset, which addresses memory only)
-        if (lane < (D - 512) / 8)
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(kbuf + r * KT::ROWB + 1024),
-                                                   16, lane_off, soff + 1024, 0, 0);
-      }
+    }
+    if constexpr (KT::TAIL > 0) {
+      // the tails of this wave's 8 rows: lane l takes row l%8, chunk l/8
+      int rid_l = stand_in;
+#pragma unroll
+      for (int q = 0; q < RPW; ++q)
+        if ((lane & 7) == q && rids.r[q] >= 0) rid_l = rids.r[q];
+      unsigned char* tbuf = tbuf_of(JC) + w4 * KT::TBLK;
+      // (the offset goes through a named value: written inline in the call,
+      // the host pass of this template drops the kernel's launch stub)
+      const int tvoff = rid_l * (D * 2) + 2 * KT::MAIN + 16 * (lane >> 3);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)tbuf, 16, tvoff, 0, 0, 0);
     }
   };
 
-  // ---- Q fragments (B operand of S^T = K Q^T): head hq, this wave's half of
-  // the k-steps, dims 32ks + 8g .. +7
-  const int hq = 16 * hgrp + c16;
-  const int ks0 = KH * kh;                       // first k-step of this wave
-  uint4 qraw[KH];
-  {
+  // ---- Q fragments (B operand of S^T = K Q^T): head hq, dims 32ks + 8g .. +7
+  // (S waves)
+  uint4 qraw[KS];
+  const bool use_sink = p.sink && !split_mode;
+  float sink_l2 = -INFINITY;
+  auto prologue_issue = [&]() __attribute__((always_inline)) {
+    // the first NBUF-1 gathers (issued whether or not the tiles exist, as in
+    // the loop, so that the wait counts are the same on every path)
+    issue(std::integral_constant<int, 0>{}, tile0, rid8(tile0));
+    issue(std::integral_constant<int, 1>{}, tile0 + 1, rid8(tile0 + 1));
+    if constexpr (NBUF == 4) issue(std::integral_constant<int, 2>{}, tile0 + 2, rid8(tile0 + 2));
+  };
+  if (s_role) {
     const u16* qrow = reinterpret_cast<const u16*>(p.q) + (row * H + h0 + hq) * D;
 #pragma unroll
-    for (int ks = 0; ks < KH; ++ks)
-      qraw[ks] = *reinterpret_cast<const uint4*>(qrow + 32 * (ks0 + ks) + 8 * g);
+    for (int ks = 0; ks < KS; ++ks)
+      qraw[ks] = *reinterpret_cast<const uint4*>(qrow + 32 * ks + 8 * g);
+    // the sink logit, loaded before the gathers so that waiting for it does
+    // not wait for them
+    if (use_sink) sink_l2 = p.sink[h0 + hq] * kLog2e;
+    prologue_issue();
   }
-  // the sink logit, loaded before the gathers so that waiting for it does not
-  // wait for them
-  const bool use_sink = p.sink && !split_mode;
-  const float sink_l2 = use_sink ? p.sink[h0 + hq] * kLog2e : -INFINITY;
-  if (tid == 0) { flags[0] = 1; flags[1] = 1; }
-  // the first NBUF-1 gathers (issued whether or not the tiles exist, as in the
-  // loop, so that the wait counts are the same on every path)
-  issue(std::integral_constant<int, 0>{}, tile0, rid4(tile0));
-  issue(std::integral_constant<int, 1>{}, tile0 + 1, rid4(tile0 + 1));
-  if constexpr (NBUF == 4) issue(std::integral_constant<int, 2>{}, tile0 + 2, rid4(tile0 + 2));
 
-  // rotate the rope slice of q at +t, round to bf16
-  bf16x8 qf[KH];
+  // rotate the rope slice of q at +t, round to bf16 (S waves; the PV waves
+  // never read these)
+  bf16x8 qf[KS];
 #pragma unroll
-  for (int ks = 0; ks < KH; ++ks) {
-    // the rope slice is the last R dims: the last R/32 k-steps of the upper half
-    const int d0 = 32 * (ks0 + ks) + 8 * g;
+  for (int ks = 0; ks < KS; ++ks) {
+    const int d0 = 32 * ks + 8 * g;
     uint4 u = qraw[ks];
-    if (ks >= KH - R / 32 && kh == 1) {
+    if (32 * ks >= rbase && s_role) {
       float v[8] = {bf_lo(u.x), bf_hi(u.x), bf_lo(u.y), bf_hi(u.y),
                     bf_lo(u.z), bf_hi(u.z), bf_lo(u.w), bf_hi(u.w)};
 #pragma unroll
@@ -445,264 +486,282 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(MfmaArgs args) {
     qf[ks] = as_bf16x8(u);
   }
 
-  // ---- softmax state of head hq (replicated over the 4 lane groups, and the
-  // same in both waves of the head block), log2 domain; lrun sums the keys of
-  // this wave's key half only
+  // ---- softmax state of head hq (replicated over the 4 lane groups), log2
+  // domain
   const float sl2 = p.scale * kLog2e;
-  float mref = sink_l2, lrun = (use_sink && kh == 0) ? 1.f : 0.f;
+  float mref = sink_l2, lrun = use_sink ? 1.f : 0.f, mseen = -INFINITY;
 
+  // ---- S phase pieces.  S^T for keys 16kb + c16 (kb = 0, 1) and the 16
+  // heads of this wave, in groups of 4 k-steps; lane supplies K row
+  // 16kb + c16, 16-byte chunk 4ks + g.  Four accumulation chains (key block x
+  // even/odd k-step).
+  constexpr int NG = (KS + 3) / 4;
+  auto k_group = [&](auto JC, int grp, uint4 (&kv)[4][2]) __attribute__((always_inline)) {
+    const unsigned char* krow = kbuf_of(JC) + c16 * KT::ROWB + 16 * g;
+    // tail area: rows c16 and 16 + c16 sit in wave blocks c16/8 and 2 + c16/8
+    const unsigned char* ktail = tbuf_of(JC) + (c16 >> 3) * KT::TBLK + (c16 & 7) * 16 + 128 * g;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const int ks = 4 * grp + kk;
+      if (ks < KT::MAIN / 32) {
+        kv[kk][0] = *reinterpret_cast<const uint4*>(krow + 64 * ks);
+        kv[kk][1] = *reinterpret_cast<const uint4*>(krow + 16 * KT::ROWB + 64 * ks);
+      } else if (ks < KS) {
+        const int u = ks - KT::MAIN / 32;   // tail chunk 4u + g
+        kv[kk][0] = *reinterpret_cast<const uint4*>(ktail + 512 * u);
+        kv[kk][1] = *reinterpret_cast<const uint4*>(ktail + 2 * KT::TBLK + 512 * u);
+      }
+    }
+  };
+  auto s_group = [&](int grp, const uint4 (&kv)[4][2], f32x4 (&sa)[4])
+      __attribute__((always_inline)) {
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const int ks = 4 * grp + kk;
+      if (ks < KS) {
+        sa[(kk & 1) * 2 + 0] = mfma16x16x32(as_bf16x8(kv[kk][0]), qf[ks], sa[(kk & 1) * 2 + 0]);
+        sa[(kk & 1) * 2 + 1] = mfma16x16x32(as_bf16x8(kv[kk][1]), qf[ks], sa[(kk & 1) * 2 + 1]);
+      }
+    }
+  };
+  // V: column block nb, keys 4g + e (first read) and 16 + 4g + e (second):
+  // lane (g, s) of a 16-lane block reads row 4g + s/4, columns 4(s%4) ..
+  typedef short s16x4 __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  auto v_read = [&](auto JC, int nb) __attribute__((always_inline)) -> bf16x8 {
+    const unsigned char* vrow =
+        kbuf_of(JC) + (4 * g + (c16 >> 2)) * KT::ROWB + 2 * cbase + 8 * (c16 & 3) + 32 * nb;
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)vrow);
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vrow + 16 * KT::ROWB));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+
+  // ---- softmax of a tile (buffer J) from its logits: P to P buffer par (key
+  // position 8g + e <-> key 16(e/4) + 4g + (e%4)).  On the first tile of the
+  // range the reference max is set (the accumulators are still zero, only the
+  // running sum is rescaled); afterwards a tile far above it requests a
+  // restart.
+  auto bias_of = [&](auto JC, int kb) __attribute__((always_inline)) -> f32x4 {
+    return *reinterpret_cast<const f32x4*>(bias_s + decltype(JC)::value * kNK + 16 * kb + 4 * g);
+  };
+  auto softmax = [&](int par, const f32x4 x0, const f32x4 x1, bool first)
+      __attribute__((always_inline)) {
+    // raw logits; the scale (> 0) commutes with the max and goes into the
+    // exponent's fused multiply-add
+    const float m0 = fmaxf(fmaxf(x0[0], x0[1]), fmaxf(x0[2], x0[3]));
+    const float m1 = fmaxf(fmaxf(x1[0], x1[1]), fmaxf(x1[2], x1[3]));
+    const float tmax = xgroup_max(fmaxf(m0, m1)) * sl2;
+    mseen = fmaxf(mseen, tmax);
+    float alpha = 1.f;
+    if (first) {
+      const float mnew = fmaxf(mref, tmax);
+      if (mnew != mref) alpha = __builtin_amdgcn_exp2f(mref - mnew);
+      mref = mnew;
+    } else {
+      // every lane writes the wave's verdict (no branch: this chain is
+      // interleaved with matrix instructions)
+      rflag_s[par * NS + w4] = __ballot(tmax > mref + kRestart) != 0ull ? 1 : 0;
+    }
+    const float mbase = (mref == -INFINITY) ? 0.f : mref;
+    float pv[8];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      pv[r] = __builtin_amdgcn_exp2f(fmaf(x0[r], sl2, -mbase));
+      pv[4 + r] = __builtin_amdgcn_exp2f(fmaf(x1[r], sl2, -mbase));
+    }
+    const float ps = ((pv[0] + pv[1]) + (pv[2] + pv[3])) + ((pv[4] + pv[5]) + (pv[6] + pv[7]));
+    lrun = lrun * alpha + xgroup_sum(ps);
+    *reinterpret_cast<uint4*>(Ps + (par * HG + hq) * kPS + 8 * g) =
+        make_uint4(pack2(pv[0], pv[1]), pack2(pv[2], pv[3]), pack2(pv[4], pv[5]),
+                   pack2(pv[6], pv[7]));
+  };
+
+  // ---- S-wave step: S + softmax of the tile in buffer JN (P buffer par),
+  // the K groups read one group ahead of their products
+  auto s_step = [&](auto JN, int par, bool first) __attribute__((always_inline)) {
+    uint4 kv[2][4][2];
+    k_group(JN, 0, kv[0]);
+    const f32x4 bias0 = bias_of(JN, 0), bias1 = bias_of(JN, 1);
+    f32x4 sa[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sa[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int grp = 0; grp < NG; ++grp) {
+      __builtin_amdgcn_sched_barrier(0);
+      if (grp + 1 < NG) k_group(JN, grp + 1, kv[(grp + 1) & 1]);
+      s_group(grp, kv[grp & 1], sa);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    softmax(par, sa[0] + sa[2] + bias0, sa[1] + sa[3] + bias1, first);
+  };
+  constexpr int kAhead = (NBUF - 2) * G;   // loads still in flight at a wait
+  if (tid < 2 * NS) rflag_s[tid] = 0;
+  // restart requests for tile j+1 (written by the S waves in step j)
+  auto again_of = [&](int par) __attribute__((always_inline)) -> bool {
+    const int4 rf = *reinterpret_cast<const int4*>(rflag_s + (par ^ 1) * NS);
+    return __builtin_amdgcn_readfirstlane(rf.x | rf.y | rf.z | rf.w) != 0;
+  };
+  // Both roles run the same barriers: two in the prologue, one per iteration
+  // (whole rounds of NBUF iterations; the ones past the last tile keep only
+  // the barrier and, in the S waves, the empty gathers, so that the loads
+  // issued are the same on every path through the loop), one per restart and
+  // one before the output.
+  if (s_role) {
+    for (;;) {
+      // ---- prologue: S + softmax of the first tile
+      wait_vmcnt<kAhead>();
+      lds_barrier();  // tile0 landed
+      s_step(std::integral_constant<int, 0>{}, 0, true);
+      Rid8 rid_next = rid8(tile0 + NBUF - 1);
+      wait_vmcnt<(NBUF - 3) * G>();  // tile0+1 landed
+      lds_barrier();  // B(tile0)
+      bool again = false;
+      auto iter = [&](auto JC, int j) __attribute__((always_inline)) {
+        constexpr int J = decltype(JC)::value;
+        const int par = (j - tile0) & 1;
+        issue(std::integral_constant<int, (J + NBUF - 1) % NBUF>{}, j + NBUF - 1, rid_next);
+        if (j < tile1 && !again)
+          s_step(std::integral_constant<int, (J + 1) % NBUF>{}, par ^ 1, false);
+        rid_next = rid8(j + NBUF);
+        // this wave's loads of tile j+2 have landed (those of j+3 may be in
+        // flight)
+        wait_vmcnt<(NBUF - 3) * G>();
+        lds_barrier();  // B(j+1)
+        again = again_of(par);
+      };
+      for (int tile = tile0; tile < tile1 && !again; tile += NBUF) {
+        iter(std::integral_constant<int, 0>{}, tile);
+        iter(std::integral_constant<int, 1>{}, tile + 1);
+        iter(std::integral_constant<int, 2>{}, tile + 2);
+        if constexpr (NBUF == 4) iter(std::integral_constant<int, 3>{}, tile + 3);
+      }
+      // no gather may still be writing this workgroup's LDS when it exits or
+      // starts over
+      wait_vmcnt<0>();
+      if (!again) break;
+      // ---- restart with the reference max raised to the largest one seen
+      lds_barrier();
+      mref = mseen;
+      lrun = use_sink ? __builtin_amdgcn_exp2f(sink_l2 - mref) : 0.f;
+      if (tid < 2 * NS) rflag_s[tid] = 0;
+      prologue_issue();
+    }
+    // ---- running max and sum of each head, for the PV waves / the merge
+    if (g == 0) {
+      if (split_mode) {
+        float* ml = args.ws + ((size_t)row * args.nsplit + split) * H * 2;
+        ml[2 * (h0 + hq)] = mref;
+        ml[2 * (h0 + hq) + 1] = lrun;
+      } else {
+        fin_s[hq] = lrun > 0.f ? 1.f / lrun : 0.f;
+      }
+    }
+    lds_barrier();
+    return;
+  }
+
+  // ---- PV waves
   f32x4 acc[4][NB];
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const int col0 = 64 * wave + 4 * c16;          // this lane's first output column
-
-  // this wave's partial S^T of the pending tile (its half of the k-steps),
-  // key blocks 0 and 1; empty key slots hold -inf
-  f32x4 sp[2];
-
-  // ---- S phase pieces.  Lane supplies K row 16kb + c16, 16-byte chunk
-  // 4(ks0 + ks) + g for key block kb and k-step ks of this wave's half.
-  auto k_row = [&](auto JC) __attribute__((always_inline)) -> const unsigned char* {
-    return kbuf_of(JC) + c16 * KT::ROWB + 16 * g + 64 * ks0;
-  };
-  // bias the partials (0 / -inf per key slot; the lower D-half wave adds it,
-  // so the sum of the two partials carries it once) and publish them for the
-  // other wave of the head block
-  auto s_finish = [&](auto JC, const f32x4 st0, const f32x4 st1) __attribute__((always_inline)) {
-    constexpr int J = decltype(JC)::value;
-    sp[0] = st0;
-    sp[1] = st1;
-    if (kh == 0) {
-      sp[0] += *reinterpret_cast<const f32x4*>(bias_s + J * kNK + 4 * g);
-      sp[1] += *reinterpret_cast<const f32x4*>(bias_s + J * kNK + 16 + 4 * g);
-    }
-    *reinterpret_cast<f32x4*>(spart + (wave * 2 + 0) * 64 * 4 + 4 * lane) = sp[0];
-    *reinterpret_cast<f32x4*>(spart + (wave * 2 + 1) * 64 * 4 + 4 * lane) = sp[1];
-  };
-  // the S phase on its own (first tile): groups of 2 k-steps x 2 key blocks,
-  // the fence bounds the K fragments held in registers at once
-  auto s_phase = [&](auto JC) __attribute__((always_inline)) {
-    const unsigned char* krow = k_row(JC);
-    f32x4 st0 = f32x4{0.f, 0.f, 0.f, 0.f}, st1 = st0;  // key blocks 0 / 1
-#pragma unroll
-    for (int k2 = 0; k2 < KH; k2 += 2) {
-      uint4 kv[2][2];
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk)
-        if (k2 + kk < KH) {
-          kv[kk][0] = *reinterpret_cast<const uint4*>(krow + 64 * (k2 + kk));
-          kv[kk][1] = *reinterpret_cast<const uint4*>(krow + 16 * KT::ROWB + 64 * (k2 + kk));
-        }
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk)
-        if (k2 + kk < KH) {
-          st0 = mfma16x16x32(as_bf16x8(kv[kk][0]), qf[k2 + kk], st0);
-          st1 = mfma16x16x32(as_bf16x8(kv[kk][1]), qf[k2 + kk], st1);
-        }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    s_finish(JC, st0, st1);
-  };
-
-  // ---- softmax of the pending tile, once both waves' partials are in LDS:
-  // the full logits of the 32 keys of head hq (identical in both waves: the
-  // two partials are added in either order), the new reference max, P of this
-  // wave's key half to LDS (key 16kh + 4g + j at position 8g + 4kh + j), the
-  // rescale factor of head hq, and the rescale flag of parity par
-  auto softmax = [&](auto JC, int par) __attribute__((always_inline)) {
-    const int pw = wave ^ 4;
-    const f32x4 o0 = *reinterpret_cast<const f32x4*>(spart + (pw * 2 + 0) * 64 * 4 + 4 * lane);
-    const f32x4 o1 = *reinterpret_cast<const f32x4*>(spart + (pw * 2 + 1) * 64 * 4 + 4 * lane);
-    // raw logits; the scale (> 0) commutes with the max and goes into the
-    // exponent's fused multiply-add
-    const f32x4 f0 = sp[0] + o0, f1 = sp[1] + o1;
-    const float m0 = fmaxf(fmaxf(f0[0], f0[1]), fmaxf(f0[2], f0[3]));
-    const float m1 = fmaxf(fmaxf(f1[0], f1[1]), fmaxf(f1[2], f1[3]));
-    const float tmax = xgroup_max(fmaxf(m0, m1)) * sl2;
-    const f32x4 sv = kh ? f1 : f0;
-    const float mnew = (tmax > mref + kLazy) ? tmax : mref;
-    const float alpha = (mnew == mref) ? 1.f : __builtin_amdgcn_exp2f(mref - mnew);
-    const float mbase = (mnew == -INFINITY) ? 0.f : mnew;
-    const float p0 = __builtin_amdgcn_exp2f(fmaf(sv[0], sl2, -mbase));
-    const float p1 = __builtin_amdgcn_exp2f(fmaf(sv[1], sl2, -mbase));
-    const float p2 = __builtin_amdgcn_exp2f(fmaf(sv[2], sl2, -mbase));
-    const float p3 = __builtin_amdgcn_exp2f(fmaf(sv[3], sl2, -mbase));
-    lrun = lrun * alpha + xgroup_sum((p0 + p1) + (p2 + p3));
-    mref = mnew;
-    *reinterpret_cast<uint2*>(Ps + hq * kPS + 8 * g + 4 * kh) =
-        make_uint2(pack2(p0, p1), pack2(p2, p3));
-    if (kh == 0 && g == 0) alpha_s[hq] = alpha;
-    if (kh == 0 && __ballot(alpha != 1.f) != 0ull && lane == 0) flags[par] = 1;
-  };
-
-  // ---- PV phase of the tile in buffer J: O[all 64 heads][this wave's 64
-  // columns] += P V (after the rescale when some head raised its maximum),
-  // then, when WITH_S, the S phase of the tile in the next buffer.  The
-  // operand reads run ahead of the matrix instructions: the PV operands and
-  // the first K fragments are read before the PV products, and every group of
-  // S products is followed by the reads of the group after next.
-  auto pv_s = [&](auto JC, auto WITH_S, int par) __attribute__((always_inline)) {
-    constexpr bool kS = decltype(WITH_S)::value;
-    using JN = std::integral_constant<int, (decltype(JC)::value + 1) % NBUF>;
-    const unsigned char* kbuf = kbuf_of(JC);
-    if (flags[par]) {
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb) {
-        const float4 al = *reinterpret_cast<const float4*>(alpha_s + 16 * mb + 4 * g);
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-          acc[mb][nb][0] *= al.x; acc[mb][nb][1] *= al.y;
-          acc[mb][nb][2] *= al.z; acc[mb][nb][3] *= al.w;
-        }
-      }
-    }
-    __builtin_amdgcn_sched_barrier(0);
+  // ---- PV-wave step: PV of the tile in buffer J (P buffer par)
+  auto pv_step = [&](auto JC, int par) __attribute__((always_inline)) {
     bf16x8 pa[4];
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb)
-      pa[mb] = as_bf16x8(*reinterpret_cast<const uint4*>(Ps + (16 * mb + c16) * kPS + 8 * g));
-    // V: for key position q (key 16*(q/4) + 4g + q%4), this lane's 4 columns
-    uint32_t vr[8][2];
-    const unsigned char* vcol = kbuf + 4 * g * KT::ROWB + 2 * col0;
+      pa[mb] = as_bf16x8(
+          *reinterpret_cast<const uint4*>(Ps + (par * HG + 16 * mb + c16) * kPS + 8 * g));
+    bf16x8 vb[NB];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const uint2 u = *reinterpret_cast<const uint2*>(
-          vcol + (16 * (q >> 2) + (q & 3)) * KT::ROWB);
-      vr[q][0] = u.x; vr[q][1] = u.y;
-    }
-    uint4 kv[KH][2];
-    const unsigned char* krow = k_row(JN{});
-    // the first half of the K fragments now, the second half once the PV
-    // operands are consumed (bounds the registers held at once)
-    constexpr int KA = KH / 2;
-    auto k_reads = [&](int k_lo, int k_hi) __attribute__((always_inline)) {
+    for (int nb = 0; nb < NB; ++nb) vb[nb] = v_read(JC, nb);
 #pragma unroll
-      for (int ks = 0; ks < KH; ++ks)
-        if (ks >= k_lo && ks < k_hi) {
-          kv[ks][0] = *reinterpret_cast<const uint4*>(krow + 64 * ks);
-          kv[ks][1] = *reinterpret_cast<const uint4*>(krow + 16 * KT::ROWB + 64 * ks);
-        }
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) acc[mb][nb] = mfma16x16x32(pa[mb], vb[nb], acc[mb][nb]);
+  };
+
+  for (;;) {
+    lds_barrier();  // tile0 landed
+    lds_barrier();  // B(tile0)
+    bool again = false;
+    auto iter = [&](auto JC, int j) __attribute__((always_inline)) {
+      const int par = (j - tile0) & 1;
+      if (j < tile1 && !again) pv_step(JC, par);
+      lds_barrier();  // B(j+1)
+      again = again_of(par);
     };
-    if constexpr (kS) k_reads(0, KA);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      const int dw = nb >> 1;
-      uint32_t f[4];
-#pragma unroll
-      for (int d = 0; d < 4; ++d)  // low halves (even nb) or high halves (odd nb) of two keys
-        f[d] = __builtin_amdgcn_perm(vr[2 * d + 1][dw], vr[2 * d][dw],
-                                     (nb & 1) ? 0x07060302u : 0x05040100u);
-      const bf16x8 vb = as_bf16x8(make_uint4(f[0], f[1], f[2], f[3]));
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb) acc[mb][nb] = mfma16x16x32(pa[mb], vb, acc[mb][nb]);
+    for (int tile = tile0; tile < tile1 && !again; tile += NBUF) {
+      iter(std::integral_constant<int, 0>{}, tile);
+      iter(std::integral_constant<int, 1>{}, tile + 1);
+      iter(std::integral_constant<int, 2>{}, tile + 2);
+      if constexpr (NBUF == 4) iter(std::integral_constant<int, 3>{}, tile + 3);
     }
-    __builtin_amdgcn_sched_barrier(0);
-    if constexpr (kS) {
-      k_reads(KA, KH);
-      f32x4 st0 = f32x4{0.f, 0.f, 0.f, 0.f}, st1 = st0;  // key blocks 0 / 1
-#pragma unroll
-      for (int ks = 0; ks < KH; ++ks) {
-        st0 = mfma16x16x32(as_bf16x8(kv[ks][0]), qf[ks], st0);
-        st1 = mfma16x16x32(as_bf16x8(kv[ks][1]), qf[ks], st1);
-      }
-      s_finish(JN{}, st0, st1);
-    }
-  };
-
-  // ---- software pipeline over the tiles, two barriers per tile:
-  //   X(j): partials of tile j published; buffer (j-1) and P free
-  //         -> softmax of tile j, gather tile j+NBUF-1 into buffer (j-1)
-  //   Y(j): P(j) and the rescale factors visible; tile j+1 landed
-  //         -> PV of tile j, then S of tile j+1 (matrix cores back to back)
-  // Gathers are issued past the last tile as well (every row empty: the
-  // buffer is zero-filled), so that every iteration issues the same loads and
-  // the wait counts are exact; the row ids of the next gather are looked up
-  // an iteration ahead.
-  constexpr int kAhead = (NBUF - 2) * KT::G;   // loads still in flight at a wait
-  wait_vmcnt<kAhead>();
-  lds_barrier();  // tile0 landed
-  s_phase(std::integral_constant<int, 0>{});
-  int4 rid_next = rid4(tile0 + NBUF - 1);
-  auto iter = [&](auto JC, int j) __attribute__((always_inline)) {
-    constexpr int J = decltype(JC)::value;
-    const int par = (j - tile0) & 1;
-    const bool live = j < tile1;
-    lds_barrier();  // X(j)
-    if (live) softmax(JC, par);
-    issue(std::integral_constant<int, (J + NBUF - 1) % NBUF>{}, j + NBUF - 1, rid_next);
-    wait_vmcnt<kAhead>();  // this wave's loads of tile j+1 have landed
-    lds_barrier();  // Y(j)
-    if (tid == 0) flags[par ^ 1] = 0;  // the next tile's rescale flag starts clear
-    // the S phase runs after the last tile too, on a zero-filled buffer: one
-    // code path keeps the register allocation tight
-    if (live) pv_s(JC, std::true_type{}, par);
-    rid_next = rid4(j + NBUF);
-  };
-  // whole rounds of NBUF iterations: the ones past the last tile only keep the
-  // barriers and the (empty) gathers, so that the loads issued are the same
-  // on every path through the loop
-  for (int tile = tile0; tile < tile1; tile += NBUF) {
-    iter(std::integral_constant<int, 0>{}, tile);
-    iter(std::integral_constant<int, 1>{}, tile + 1);
-    iter(std::integral_constant<int, 2>{}, tile + 2);
-    if constexpr (NBUF == 4) iter(std::integral_constant<int, 3>{}, tile + 3);
-  }
-  // no gather may still be writing this workgroup's LDS when it exits
-  wait_vmcnt<0>();
-
-  // ---- epilogue: l = sum over both key halves
-  if (kh == 1 && g == 0) l_s[hq] = lrun;
-  lds_barrier();
-  if (kh == 0 && g == 0) {
-    const float l = lrun + l_s[hq];
-    if (split_mode) {
-      float* ml = args.ws + ((size_t)row * args.nsplit + split) * H * 2;
-      ml[2 * (h0 + hq)] = mref;
-      ml[2 * (h0 + hq) + 1] = l;
-    } else {
-      fin_s[hq] = l > 0.f ? 1.f / l : 0.f;
-    }
-  }
-  if (split_mode) {
-    float* po = args.ws + (size_t)((long)p.B * p.S) * args.nsplit * H * 2 +
-                ((size_t)row * args.nsplit + split) * H * dv;
+    if (!again) break;
+    lds_barrier();  // restart
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        *reinterpret_cast<float4*>(po + (size_t)(h0 + 16 * mb + 4 * g + j) * dv + col0) =
-            make_float4(acc[mb][0][j], acc[mb][1][j], acc[mb][2][j], acc[mb][3][j]);
+      for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  lds_barrier();  // the S waves' max and sum are in place
+
+  // ---- output.  Lane (g, c16) holds, for head block mb and column block nb,
+  // O[head 16mb + 4g + j][column cbase + 16nb + c16], j = 0..3.  Stores go out
+  // as column pairs: adjacent lanes trade one value (even lane: row j, columns
+  // c, c+1; odd lane: row j+1, columns c-1, c).
+  const bool odd = (c16 & 1) != 0;
+  auto partner = [&](float v) __attribute__((always_inline)) -> float {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true));
+  };
+  if (split_mode) {
+    float* po = args.ws + (size_t)((long)p.B * p.S) * args.nsplit * H * 2 +
+                ((size_t)row * args.nsplit + split) * H * dv + (size_t)h0 * dv;
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const int col = cbase + 16 * nb + c16;
+#pragma unroll
+        for (int j = 0; j < 4; j += 2) {
+          const float v0 = acc[mb][nb][j], v1 = acc[mb][nb][j + 1];
+          const float r = partner(odd ? v0 : v1);
+          const int hr = 16 * mb + 4 * g + j + (odd ? 1 : 0);
+          *reinterpret_cast<float2*>(po + (size_t)hr * dv + col - (odd ? 1 : 0)) =
+              odd ? make_float2(r, v1) : make_float2(v0, r);
+        }
+      }
     return;
   }
-  lds_barrier();
   u16* out = reinterpret_cast<u16*>(p.out) + (row * H + h0) * dv;
-  const bool derot = (dv == D) && col0 + NB > rbase;
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb) {
     const float4 li = *reinterpret_cast<const float4*>(fin_s + 16 * mb + 4 * g);
     const float lv[4] = {li.x, li.y, li.z, li.w};
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      float v[NB];
+    for (int nb = 0; nb < NB; ++nb) {
+      const int col = cbase + 16 * nb + c16;
+      float v[4];
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) v[nb] = acc[mb][nb][j] * lv[j];
-      if (derot) {
+      for (int j = 0; j < 4; ++j) v[j] = acc[mb][nb][j] * lv[j];
+      if (dv == D && cbase + 16 * nb + 16 > rbase) {
+        // de-rotate the rope slice at -t: pairs (even column, odd column)
+        // sit in adjacent lanes
+        const float2 rr = cs[t * half + (((col & ~1) - rbase) >> 1)];
 #pragma unroll
-        for (int nb = 0; nb < NB; nb += 2) {
-          const int col = col0 + nb;
-          if (col >= rbase) {
-            const float2 rr = cs[t * half + ((col - rbase) >> 1)];
-            const float a = v[nb], bb = v[nb + 1];
-            v[nb] = a * rr.x + bb * rr.y;
-            v[nb + 1] = -a * rr.y + bb * rr.x;
-          }
+        for (int j = 0; j < 4; ++j) {
+          const float o = partner(v[j]);
+          v[j] = odd ? (-o * rr.y + v[j] * rr.x) : (v[j] * rr.x + o * rr.y);
         }
       }
-      *reinterpret_cast<uint2*>(out + (16 * mb + 4 * g + j) * dv + col0) =
-          make_uint2(pack2(v[0], v[1]), pack2(v[2], v[3]));
+#pragma unroll
+      for (int j = 0; j < 4; j += 2) {
+        const float r = partner(odd ? v[j] : v[j + 1]);
+        const int hr = 16 * mb + 4 * g + j + (odd ? 1 : 0);
+        *reinterpret_cast<uint32_t*>(out + hr * dv + col - (odd ? 1 : 0)) =
+            odd ? pack2(r, v[j + 1]) : pack2(v[j], r);
+      }
     }
   }
 }

@@ -30,6 +30,13 @@ def test_header_declares_the_hot_path():
         assert n in names
 
 
+def test_library_resolves_every_symbol():
+    # immediate binding: a kernel whose launch stub the compiler failed to emit
+    # shows up here as an undefined symbol rather than at first use on a GPU
+    from sparse_long_context_pool_amd import csa
+    ctypes.CDLL(csa._LIB_PATH, mode=os.RTLD_NOW | os.RTLD_LOCAL)
+
+
 def test_library_exports_every_declared_symbol(L):
     for name in declared_functions():
         assert hasattr(L, name), name
