@@ -5,14 +5,22 @@
 
 Prints ONE JSON line.  ``value`` is CSA prefill tokens/s (8192-token sequence,
 64 heads x 512, top-512 of 2048 pool entries, window 128): one step is every
-stage of the path over that batch -- RoPE table, window-row rotation, K=V pool
-and indexer-key compression, index scores, top-k, sparse attention -- with the
-inputs already resident in HBM.  Each stage is timed with HIP events on the
+stage of the path over that batch -- window-row rotation, K=V pool and
+indexer-key compression, index scores, top-k, sparse attention -- with the
+inputs already resident in HBM (the RoPE table is model set-up: built once,
+timed on its own and reported beside the step).  Each stage is timed with HIP events on the
 stream its kernels run on; ``roofline`` reports the dominant kernel's
 algorithmic FLOP/s or bytes/s against the MI355X peak.  CSA decode (64 x 1
 token after 131072 cached tokens) is reported in us/step, and the HCA and DSA
 workloads in tokens/s.  ``cpu_baseline`` times the CPU oracle on a stratified
 sample of the prefill rows.
+
+HBM traffic of the dominant kernels (``roofline.traffic``) comes from two
+rocprofv3 counter runs (FETCH_SIZE, then WRITE_SIZE) of one workload each,
+with ``--calib-copy`` so that a plain device copy of known size is profiled in
+the same run; ``--traffic FETCH_DB WRITE_DB`` (no GPU) turns the two counter
+databases into profiles/hbm_traffic.json, tagged with a hash of the kernel
+sources so that a stale file is ignored.
 """
 from __future__ import annotations
 
@@ -310,6 +318,88 @@ def cpu_baseline(WORKLOADS, synth, n_rows=8192):
             "seconds_measured": round(t2 - t0, 2)}
 
 
+# ------------------------------------------------------------------ HBM traffic
+CALIB_BYTES = 1 << 30       # the calibration copy reads and writes this many bytes
+DOMINANT = {                # stage -> kernels that make it (name prefixes)
+    "attention": ("csa::(anonymous namespace)::attn_mfma_kernel",
+                  "csa::(anonymous namespace)::attn_combine_kernel",
+                  "csa::(anonymous namespace)::attn_generic_kernel"),
+    "index_scores": ("csa::(anonymous namespace)::index_scores",),
+    "topk": ("csa::(anonymous namespace)::topk_kernel",),
+}
+
+
+def calib_copy(torch):
+    """A plain device-to-device copy of CALIB_BYTES (4x the last-level cache, so
+    that it streams from and to HBM), three times, so that a counter run sees
+    what FETCH_SIZE / WRITE_SIZE report for known traffic."""
+    src = torch.empty(CALIB_BYTES, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    evict = torch.empty_like(src)
+    for _ in range(3):
+        evict.fill_(2)
+        dst.copy_(src)
+    torch.cuda.synchronize()
+
+
+def _counter_values(db_path, counter):
+    """kernel name -> the counter's value (KiB) of every dispatch"""
+    import sqlite3
+    c = sqlite3.connect(db_path).cursor()
+    vals = {}
+    for name, value in c.execute("select kernel_name, value from counters_collection "
+                                 "where counter_name = ? order by dispatch_id", (counter,)):
+        name = name[5:] if name.startswith("void ") else name
+        vals.setdefault(name, []).append(value)
+    return vals
+
+
+def write_traffic(fetch_db, write_db, workload, out=None):
+    """profiles/hbm_traffic.json from a FETCH_SIZE and a WRITE_SIZE run of one
+    workload (both with --calib-copy): bytes per launch of each stage's
+    kernels, each counter scaled by (known copy bytes) / (what it read for the
+    copy)."""
+    fetch = _counter_values(fetch_db, "FETCH_SIZE")
+    write = _counter_values(write_db, "WRITE_SIZE")
+
+    def copy_kib(d):
+        # the calibration copies: the large dispatches of the copy kernel
+        big = sorted(v for n, vs in d.items() if "copyBuffer" in n for v in vs
+                     if v > CALIB_BYTES / 1024 / 16)
+        if not big:
+            raise RuntimeError("no calibration copy in the counter database")
+        return big[len(big) // 2]
+
+    def mean(vs):
+        return sum(vs) / len(vs)
+
+    f_scale = (CALIB_BYTES / 1024) / copy_kib(fetch)
+    w_scale = (CALIB_BYTES / 1024) / copy_kib(write)
+    out = out or os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    try:
+        doc = json.load(open(out))
+        if doc.get("kernel_sources") != kernel_source_hash():
+            doc = {}
+    except (OSError, ValueError):
+        doc = {}
+    doc["kernel_sources"] = kernel_source_hash()
+    doc.setdefault("bytes_per_launch", {})
+    doc.setdefault("calibration", {})
+    doc["calibration"][workload] = {"copy_bytes": CALIB_BYTES, "fetch_scale": round(f_scale, 4),
+                                    "write_scale": round(w_scale, 4)}
+    for stage, prefixes in DOMINANT.items():
+        kib_f = sum(mean(v) for n, v in fetch.items() if n.startswith(prefixes))
+        kib_w = sum(mean(v) for n, v in write.items() if n.startswith(prefixes))
+        if kib_f or kib_w:
+            doc["bytes_per_launch"][f"{workload}/{stage}"] = int(
+                round((kib_f * f_scale + kib_w * w_scale) * 1024))
+    os.makedirs(os.path.dirname(out), exist_ok=True)
+    with open(out, "w") as fh:
+        json.dump(doc, fh, indent=1, sort_keys=True)
+        fh.write("\n")
+    return doc
+
+
 # ------------------------------------------------------------------ main
 def main():
     ap = argparse.ArgumentParser()
@@ -318,7 +408,18 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workloads", default="csa_prefill_bf16,csa_decode_bf16,hca_bf16,dsa_bf16")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="also run a plain copy of known size (for counter calibration)")
+    ap.add_argument("--traffic", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
+                    help="write profiles/hbm_traffic.json from two counter databases of "
+                         "one --workloads run, then exit (no GPU)")
     args = ap.parse_args()
+    if args.traffic:
+        names = [n for n in args.workloads.split(",") if n]
+        if len(names) != 1:
+            sys.exit("--traffic takes the one workload the counter runs covered")
+        print(json.dumps(write_traffic(args.traffic[0], args.traffic[1], names[0])))
+        return
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU (asked for --gpus {args.gpus}); the path is "
               "single-GPU by design and multi-GPU scaling is not part of this benchmark",
@@ -362,6 +463,8 @@ def main():
         else:
             entry["tokens_per_s"] = r2["tokens_per_s"]
         line[key] = entry
+    if args.calib_copy:
+        calib_copy(torch)
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(WORKLOADS, synth)
     print(json.dumps(line))
