@@ -251,10 +251,15 @@ def run_workload(name, steps, warmup, csa, torch, synth, WORKLOADS):
     torch.cuda.synchronize()
     flush = None
     if wl.decode:
-        # the decode working set fits the 256 MB last-level cache: flush it
-        # between steps so the gather reads HBM, not the cache
-        junk = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
-        flush = lambda: junk.fill_(1)
+        # the decode working set is comparable to the 256 MB last-level cache:
+        # flush it between steps so every step reads HBM, not the cache.  The
+        # flush READS 1 GiB (a write would leave dirty lines whose write-back
+        # then competes with the timed kernels) and completes before the step.
+        junk = torch.ones(1 << 28, dtype=torch.int32, device="cuda")
+
+        def flush():
+            junk.sum()
+            torch.cuda.synchronize()
     ms_step, avg = r.run(steps, warmup, flush)
     work, keys = work_counts(wl)
     stages = stage_report(wl, avg, work)

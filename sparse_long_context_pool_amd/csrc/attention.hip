@@ -10,21 +10,17 @@
 // Page "DeepSeek-V3.2", section "DeepSeek Sparse Attention": attention over
 // the selected tokens only (the m = 1 case, value = the latent part).
 //
-// Matrix-core kernel (bf16).  One workgroup = one query row, all H heads
-// (H/16 wavefronts).  The key list (window slots, then pool slots) is walked in
-// tiles of 32 rows.  Each tile's rows are gathered from HBM with 16-byte loads
-// into ONE LDS tile that serves as both K and V, so a selected row is read from
-// HBM once per query row for all heads:
-//   S-phase: each wave computes S^T = K * Q^T for its 16 heads with
-//     v_mfma_f32_16x16x32_bf16 (keys on M, heads on N; Q stays in registers as
-//     the B operand).  That layout leaves each lane one head and 8 keys, i.e.
-//     exactly the A-operand layout of the P*V product, so the online softmax
-//     (seeded with the sink logit) runs in registers and P goes to LDS once.
-//   PV-phase: the waves split the value columns: each computes O[all heads]
-//     [its dv/NW columns] += P * V, reusing every V fragment for all heads.
-// Rows whose keys exceed one workgroup's share (decode: few query rows, 2176
-// keys each) are split over workgroups; partial (max, sum, O) go to the
-// caller's workspace and a combine kernel merges them with the sink.
+// Matrix-core kernel (bf16).  One workgroup = one query row x 64 heads.  The
+// key list (window slots, then pool slots) is walked in tiles of 32 rows; each
+// tile's rows are gathered from HBM straight into LDS (16-byte direct-to-LDS
+// buffer loads, several tiles in flight) into ONE tile that serves as both K
+// and V, so a selected row is read once per query row for all heads.  Half of
+// the waves compute S^T = K Q^T (v_mfma_f32_16x16x32_bf16, Q in registers) and
+// the softmax (seeded with the sink logit), the other half P V with the value
+// columns split between them; the two halves work one tile apart.  Rows whose
+// keys exceed one workgroup's share (decode: few query rows, 2176 keys each)
+// are split over workgroups; partial (max, sum, O) go to the caller's
+// workspace and a combine kernel merges them with the sink.
 // Generic kernel: one wave per (row, head), any dtype and shape.
 #include "csa_device.hpp"
 
@@ -151,7 +147,6 @@ __global__ __launch_bounds__(256) void attn_generic_kernel(AttnParams p) {
 }
 
 // ------------------------------------------------------------------ matrix-core
-typedef __attribute__((address_space(3))) void lds_void;
 
 struct MfmaArgs {
   AttnParams p;
@@ -161,15 +156,6 @@ struct MfmaArgs {
   int rows_per_xcd;       // query-row remap: consecutive rows on one XCD
 };
 
-// LDS barrier that waits only for this wave's LDS traffic, not for global
-// loads still in flight (the gathers of later tiles must stay in flight).
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
 
 // K=V tile of 32 rows in LDS, each row padded by 16 bytes (row stride
 // 2D+16 bytes = 4 or 36 dwords mod 64 banks), so that the S-phase reads (16

@@ -94,6 +94,20 @@ __device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast
 // ---------------------------------------------------------------- misc
 __device__ __forceinline__ float shfl_xor(float v, int mask) { return __shfl_xor(v, mask, 64); }
 
+// LDS barrier that waits only for this wave's LDS traffic, not for global
+// loads still in flight (the gathers of later tiles must stay in flight).
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+// Wait until at most N of this wave's vector memory operations (loads, stores
+// and direct-to-LDS loads, retired in issue order) are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+// LDS pointer type of the direct-to-LDS buffer loads
+typedef __attribute__((address_space(3))) void lds_void;
+
 // Reductions over the four lanes l, l^16, l^32, l^48 of a wave with the gfx950
 // lane-swap instructions (VALU, no LDS round trip).  v_permlane16_swap(x, x)
 // returns, in its two results, x of lanes l and l^16 (in an order that depends

@@ -12,42 +12,57 @@
 // dimension and pool entries on N (K = c^I).  v_mfma_f32_32x32x16_bf16 leaves
 // each lane 16 heads of one entry, so the ReLU-and-weight epilogue reduces over
 // heads inside the lane and one cross-half swap finishes the head sum: no LDS
-// round trip for the reduction.  Query fragments stay in registers for the
-// whole row; 128-entry key tiles are staged in LDS (16-byte padded rows, so the
-// 32 rows a B-fragment read touches fall in distinct banks) and shared by the
-// four wavefronts of a workgroup:
-//   prefill (QR = 4): four consecutive query rows per workgroup, one per wave,
-//     all sharing each key tile; causal row blocks are launched heaviest first.
-//   decode  (QR = 1): one query row per workgroup; the four waves take the four
-//     32-entry blocks of each tile, and the pool is split over workgroups so the
-//     whole chip streams the key pool (HBM-bound).
+// round trip for the reduction.  Query fragments (the A operand) stay in
+// registers; pool rows come in through direct-to-LDS loads of whole cache
+// lines, their 16-byte chunks swizzled by row so that B-fragment reads fall in
+// distinct banks.  Two kernels:
+//   many query rows (prefill, token-level indexer): 8 rows per workgroup share
+//     each 128-entry tile of the pool (MFMA-bound);
+//   few query rows (decode): a pool entry meets one query row only, so each
+//     wave streams its own blocks and the pool is split over workgroups so
+//     that the whole chip streams it (HBM-bound).
 // fp32 (and unusual shapes): a plain kernel, one thread per (row, entry).
 #include "csa_device.hpp"
+
+#include <type_traits>
 
 namespace csa {
 namespace {
 
 constexpr int kIdxTile = 128;  // pool entries per LDS tile
 
-template <int NI, int CI, int QR>
-__global__ __launch_bounds__(256) void index_scores_mfma(
+// Many query rows (prefill, token-level indexer): workgroup = 8 consecutive
+// query rows (one per wave) x one chunk of the pool.  The pool is walked in
+// 128-entry tiles (32 KiB), triple-buffered in LDS and shared by the 8 rows:
+// each wave fills four 1 KiB slices of every tile, two tiles ahead of the
+// products, with one barrier per tile.  Each wave keeps its row's
+// query fragments (the A operand, 64 heads x 128) in registers and, per
+// 32-entry block, runs 16 matrix instructions, the ReLU-and-weight epilogue
+// and one 128-byte store.  Row blocks are launched heaviest first.
+template <int NI, int CI>
+__global__ __launch_bounds__(512) void index_scores_mfma(
     const u16* __restrict__ q_idx, const float* __restrict__ w_idx,
     const u16* __restrict__ k_pool, float* __restrict__ scores,
     const int* __restrict__ q_pos, int S, int T, int m, int chunk) {
+  constexpr int QR = 8;            // query rows = waves per workgroup
   constexpr int MB = NI / 32;      // 32-head blocks
   constexpr int KS = CI / 16;      // k-steps of 16
-  constexpr int ROWB = CI * 2 + 16;
-  constexpr int CPR = CI / 8;      // 16-byte chunks per key row
-  __shared__ __attribute__((aligned(16))) unsigned char tile[kIdxTile * ROWB];
+  constexpr int NT = 128;          // entries per tile
+  constexpr int TB = NT * CI * 2;  // bytes per tile
+  static_assert(CI == 128, "a key row is 16 chunks of 16 bytes");
+  static_assert(NI <= 64, "one head weight per lane");
+  // one static array per buffer (a load in flight into one buffer then does
+  // not look like it aliases reads of another)
+  __shared__ __attribute__((aligned(16))) unsigned char kb0[TB];
+  __shared__ __attribute__((aligned(16))) unsigned char kb1[TB];
+  __shared__ __attribute__((aligned(16))) unsigned char kb2[TB];
+  __shared__ __attribute__((aligned(16))) float wsh[QR][64];
 
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int b = blockIdx.z;
   const int rb = gridDim.x - 1 - blockIdx.x;  // heaviest (latest) rows first
   const int i0 = rb * QR;
-  const int my_i = (QR == 4) ? i0 + wave : i0;
-  const bool valid = my_i < S;
   const long qp = q_pos[b];
-
   int r_wg = 0;
 #pragma unroll
   for (int r = 0; r < QR; ++r)
@@ -55,68 +70,276 @@ __global__ __launch_bounds__(256) void index_scores_mfma(
   const int lo = blockIdx.y * chunk;
   const int hi = min(r_wg, lo + chunk);
   if (lo >= hi) return;  // uniform over the workgroup
-  const int r_my = valid ? ready_count(qp + my_i, m, T) : 0;
-  const long row = (long)b * S + my_i;
+  const int my_i = i0 + wave;
+  const bool valid = my_i < S;
+  const int hi_my = valid ? min(ready_count(qp + my_i, m, T), lo + chunk) : lo;
+  const long row = (long)b * S + (valid ? my_i : 0);
 
   // A fragments: a[mb][ks] = q_idx[row][32mb + lane%32][16ks + 8(lane/32) .. +7]
   bf16x8 a[MB][KS];
-  float wv[MB][16];
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb) {
-    const int head = 32 * mb + (lane & 31);
+  for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      uint4 u = make_uint4(0, 0, 0, 0);
-      if (valid)
-        u = *reinterpret_cast<const uint4*>(q_idx + (row * NI + head) * CI + 16 * ks +
-                                            8 * (lane >> 5));
-      a[mb][ks] = as_bf16x8(u);
+    for (int ks = 0; ks < KS; ++ks)
+      a[mb][ks] = as_bf16x8(*reinterpret_cast<const uint4*>(
+          q_idx + (row * NI + 32 * mb + (lane & 31)) * CI + 16 * ks + 8 * (lane >> 5)));
+  wsh[wave][lane] = w_idx[row * NI + min(lane, NI - 1)];
+
+  // pool rows lo .. hi-1 of this sequence; tiles past hi read zeros
+  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<u16*>(k_pool + ((long)b * T + lo) * CI), 0, (hi - lo) * CI * 2, 0x00020000);
+  // this wave's slices of a tile: 1 KiB slice g = 4 wave + q (rows 4g .. 4g+3);
+  // lane l fills LDS slot l of the slice with chunk (l % 16) ^ (row % 16) of
+  // row 4g + l / 16 (row % 16 depends on q only)
+  int loff[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    loff[q] = (lane >> 4) * 256 + 16 * ((lane & 15) ^ ((4 * q + (lane >> 4)) & 15));
+  auto issue = [&](auto JC, int tile) __attribute__((always_inline)) {
+    constexpr int J = decltype(JC)::value;
+    unsigned char* buf = J == 0 ? kb0 : J == 1 ? kb1 : kb2;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int g = 4 * wave + q;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)(buf + g * 1024), 16, loff[q],
+                                               tile * TB + g * 1024, 0, 0);
     }
-    // accumulator register r holds head 32mb + 8(r/4) + 4(lane/32) + r%4
+  };
+  // B-fragment read address: row 32nb + lane%32, chunk 2ks + lane/32
+  int roff[KS];
 #pragma unroll
-    for (int r = 0; r < 16; ++r)
-      wv[mb][r] = valid ? w_idx[row * NI + 32 * mb + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)]
-                        : 0.f;
+  for (int ks = 0; ks < KS; ++ks)
+    roff[ks] = (lane & 31) * 256 + 16 * ((2 * ks + (lane >> 5)) ^ (lane & 15));
+
+  // scores of this row within the chunk: a bounded buffer store drops lanes
+  // past the row's ready entries (and the upper half, which holds copies)
+  const __amdgpu_buffer_rsrc_t out_rs = __builtin_amdgcn_make_buffer_rsrc(
+      scores + row * T + lo, 0, (hi_my - lo) * 4, 0x00020000);
+
+  // tile j: the products of the 8 rows on buffer J; exactly four stores per
+  // wave and tile (past the row's entries they are dropped), which keeps the
+  // wait counts below exact
+  auto compute = [&](auto JC, int tile) __attribute__((always_inline)) {
+    constexpr int J = decltype(JC)::value;
+    const unsigned char* buf = J == 0 ? kb0 : J == 1 ? kb1 : kb2;
+#pragma unroll
+    for (int nb = 0; nb < NT / 32; ++nb) {
+      const int e0 = tile * NT + 32 * nb;  // first entry of the block, from lo
+      float part = 0.f;
+      if (lo + e0 < hi_my) {               // uniform over the wave
+        f32x16 acc[MB];
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[mb][r] = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const uint4 bv = *reinterpret_cast<const uint4*>(buf + nb * 8192 + roff[ks]);
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb)
+            acc[mb] = mfma32x32x16(a[mb][ks], as_bf16x8(bv), acc[mb]);
+        }
+        // accumulator register r holds head 32mb + 8(r/4) + 4(lane/32) + r%4
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const float4 w4 = *reinterpret_cast<const float4*>(
+                &wsh[wave][32 * mb + 8 * q + 4 * (lane >> 5)]);
+            part += w4.x * fmaxf(acc[mb][4 * q], 0.f);
+            part += w4.y * fmaxf(acc[mb][4 * q + 1], 0.f);
+            part += w4.z * fmaxf(acc[mb][4 * q + 2], 0.f);
+            part += w4.w * fmaxf(acc[mb][4 * q + 3], 0.f);
+          }
+        // the other half of the heads sits in lane l ^ 32
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part),
+                                                         __float_as_uint(part), false, false);
+        part = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+      }
+      const int off = (lane < 32) ? (e0 + lane) * 4 : 0x40000000;
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint((part == 0.f) ? 0.f : part), out_rs,
+                                            off, 0, 0);
+    }
+  };
+
+  // Tile j: wait for this wave's slices of tile j, barrier (then every slice
+  // of tile j has landed and every wave is done with tile j-1, whose buffer
+  // takes tile j+2), refill, products.  After the loads of tile j a wave has
+  // issued at most: 4 stores (tile j-2), 4 loads (tile j+1), 4 stores (tile
+  // j-1).
+  const int ntiles = (hi - lo + NT - 1) / NT;
+  issue(std::integral_constant<int, 0>{}, 0);
+  issue(std::integral_constant<int, 1>{}, 1);
+  wait_vmcnt<4>();
+  lds_barrier();
+  issue(std::integral_constant<int, 2>{}, 2);
+  compute(std::integral_constant<int, 0>{}, 0);
+  wait_vmcnt<8>();
+  lds_barrier();
+  issue(std::integral_constant<int, 0>{}, 3);
+  compute(std::integral_constant<int, 1>{}, 1);
+  for (int j = 2; j < ntiles; j += 3) {  // whole rounds: every wave, every path
+    wait_vmcnt<12>();
+    lds_barrier();
+    issue(std::integral_constant<int, 1>{}, j + 2);
+    compute(std::integral_constant<int, 2>{}, j);
+    wait_vmcnt<12>();
+    lds_barrier();
+    issue(std::integral_constant<int, 2>{}, j + 3);
+    compute(std::integral_constant<int, 0>{}, j + 1);
+    wait_vmcnt<12>();
+    lds_barrier();
+    issue(std::integral_constant<int, 0>{}, j + 4);
+    compute(std::integral_constant<int, 1>{}, j + 2);
+  }
+  wait_vmcnt<0>();  // no load into LDS outlives the workgroup
+}
+
+// Streaming kernel for few query rows.  Workgroup (x = query row, y = pool
+// chunk); wave w scores 32-entry blocks w, w + 4, w + 8, ... of the chunk.
+// A block (32 rows x 256 bytes, contiguous in HBM) comes in with eight
+// direct-to-LDS 16-byte buffer loads, each reading 1 KiB contiguous (whole
+// cache lines, once); lane l of load i fills LDS slot l of rows 4i .. 4i+3
+// with the 16-byte chunk (l % 16) ^ (row % 16) of its row, so that the
+// B-fragment reads (32 rows, one chunk each) fall in distinct banks.  Two
+// buffers per wave: a block's fragments are read into registers as soon as it
+// lands, and its buffer is refilled at once, so two blocks stay in flight per
+// wave.  Query fragments (the A operand) stay in registers.  A wave with no
+// block leaves at once; the chunk is covered in whole rounds of two blocks
+// (blocks past the end read zeros and their scores are dropped).
+template <int NI, int CI>
+__global__ __launch_bounds__(256, 2) void index_scores_stream(
+    const u16* __restrict__ q_idx, const float* __restrict__ w_idx,
+    const u16* __restrict__ k_pool, float* __restrict__ scores,
+    const int* __restrict__ q_pos, int S, int T, int m, int chunk) {
+  constexpr int MB = NI / 32;      // 32-head blocks
+  constexpr int KS = CI / 16;      // k-steps of 16
+  constexpr int BLK = 32 * CI * 2;  // bytes per block
+  static_assert(CI == 128, "a key row is 16 chunks of 16 bytes");
+  static_assert(NI <= 64, "one head weight per lane");
+  // one static array per buffer: the compiler then sees that a load in flight
+  // into one buffer does not alias reads of the other
+  __shared__ __attribute__((aligned(16))) unsigned char kb0[4][BLK];
+  __shared__ __attribute__((aligned(16))) unsigned char kb1[4][BLK];
+  __shared__ __attribute__((aligned(16))) float wsh[4][64];
+  // the wave index is uniform: keep it (and the block loop) scalar
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const long row = blockIdx.x;
+  const int b = (int)(row / S), i = (int)(row - (long)b * S);
+  const int R = ready_count((long)q_pos[b] + i, m, T);
+  const int lo = blockIdx.y * chunk;
+  const int hi = min(R, lo + chunk);
+  const int nblk = (hi - lo + 31) >> 5;
+  int blk = wave;
+  if (blk >= nblk) return;  // wave-uniform
+
+  // key rows lo .. hi-1 of this sequence; reads past hi return zeros
+  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<u16*>(k_pool + ((long)b * T + lo) * CI), 0, (hi - lo) * CI * 2, 0x00020000);
+  // per-lane source offset of load i within its 1 KiB (rows 4i .. 4i+3; the
+  // scalar offset adds the 1 KiB steps); it depends on i % 4 only
+  int loff[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int r = 4 * q + (lane >> 4);  // row within the block, mod 16
+    loff[q] = (lane >> 4) * 256 + 16 * ((lane & 15) ^ (r & 15));
+  }
+  auto issue = [&](auto JC, int bk) __attribute__((always_inline)) {
+    unsigned char* buf = decltype(JC)::value ? kb1[wave] : kb0[wave];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int soff = bk * BLK + q * 1024;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)(buf + q * 1024), 16,
+                                               loff[q & 3], soff, 0, 0);
+    }
+  };
+  // head weights to LDS (lane l: 4 bytes at +4l), A fragments to registers:
+  // a[mb][ks] = q_idx[row][32mb + lane%32][16ks + 8(lane/32) .. +7]
+  {
+    const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float*>(w_idx + row * NI), 0, NI * 4, 0x00020000);
+    const int woff = lane * 4;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(wrs, (lds_void*)&wsh[wave][0], 4, woff, 0, 0, 0);
+  }
+  bf16x8 a[MB][KS];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      a[mb][ks] = as_bf16x8(*reinterpret_cast<const uint4*>(
+          q_idx + (row * NI + 32 * mb + (lane & 31)) * CI + 16 * ks + 8 * (lane >> 5)));
+
+  // query loads first, then the key blocks: waits count loads in issue order
+  __builtin_amdgcn_sched_barrier(0);
+  issue(std::integral_constant<int, 0>{}, blk);
+  issue(std::integral_constant<int, 1>{}, blk + 4);
+  __builtin_amdgcn_sched_barrier(0);
+
+  // B-fragment read addresses: row lane%32, chunk 2ks + lane/32 (swizzled)
+  int roff[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    const int r = lane & 31, c = 2 * ks + (lane >> 5);
+    roff[ks] = r * 256 + 16 * (c ^ (r & 15));
   }
 
-  const long kbase = (long)b * T;
-  for (int t0 = lo; t0 < hi; t0 += kIdxTile) {
-    __syncthreads();
-    for (int c = threadIdx.x; c < kIdxTile * CPR; c += 256) {
-      const int r = c / CPR, col = c - (c / CPR) * CPR;
-      const int w = t0 + r;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (w < hi) v = *reinterpret_cast<const uint4*>(k_pool + (kbase + w) * CI + col * 8);
-      *reinterpret_cast<uint4*>(tile + r * ROWB + col * 16) = v;
-    }
-    __syncthreads();
-    const int nb0 = (QR == 4) ? 0 : wave;
-    const int nb1 = (QR == 4) ? kIdxTile / 32 : wave + 1;
-    for (int nb = nb0; nb < nb1; ++nb) {
-      const int wb = t0 + nb * 32;
-      if (wb >= min(hi, r_my)) continue;  // uniform over the wave
-      f32x16 acc[MB];
+  // scores of this row and chunk go out through a bounded buffer store: lanes
+  // past the chunk (and the upper half, which holds copies) are dropped by the
+  // hardware, so the store needs no branch
+  const __amdgpu_buffer_rsrc_t out_rs = __builtin_amdgcn_make_buffer_rsrc(
+      scores + row * T + lo, 0, (hi - lo) * 4, 0x00020000);
+
+  auto step = [&](auto JC, int bk) __attribute__((always_inline)) {
+    const unsigned char* buf = decltype(JC)::value ? kb1[wave] : kb0[wave];
+    uint4 bv[KS];
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
+    for (int ks = 0; ks < KS; ++ks) bv[ks] = *reinterpret_cast<const uint4*>(buf + roff[ks]);
+    // the fragments are in registers once these reads are done: refill (the
+    // scheduling barriers keep one block's reads, refill and products
+    // together, in this order)
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    __builtin_amdgcn_sched_barrier(0);
+    issue(JC, bk + 8);
+    __builtin_amdgcn_sched_barrier(0);
+    f32x16 acc[MB];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[mb][r] = 0.f;
+    for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const uint4 bv = *reinterpret_cast<const uint4*>(
-            tile + (nb * 32 + (lane & 31)) * ROWB + (16 * ks + 8 * (lane >> 5)) * 2);
+      for (int r = 0; r < 16; ++r) acc[mb][r] = 0.f;
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) acc[mb] = mfma32x32x16(a[mb][ks], as_bf16x8(bv), acc[mb]);
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) acc[mb] = mfma32x32x16(a[mb][ks], as_bf16x8(bv[ks]), acc[mb]);
+    // accumulator register r holds head 32mb + 8(r/4) + 4(lane/32) + r%4
+    float part = 0.f;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float4 w4 = *reinterpret_cast<const float4*>(
+            &wsh[wave][32 * mb + 8 * q + 4 * (lane >> 5)]);
+        part += w4.x * fmaxf(acc[mb][4 * q], 0.f);
+        part += w4.y * fmaxf(acc[mb][4 * q + 1], 0.f);
+        part += w4.z * fmaxf(acc[mb][4 * q + 2], 0.f);
+        part += w4.w * fmaxf(acc[mb][4 * q + 3], 0.f);
       }
-      float part = 0.f;
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) part += wv[mb][r] * fmaxf(acc[mb][r], 0.f);
-      part += shfl_xor(part, 32);
-      const int w = wb + lane;
-      if (lane < 32 && w < hi && w < r_my) scores[row * T + w] = (part == 0.f) ? 0.f : part;
-    }
-  }
+    // the other half of the heads sits in lane l ^ 32
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part),
+                                                     __float_as_uint(part), false, false);
+    part = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+    const int off = (lane < 32) ? (32 * bk + lane) * 4 : 0x40000000;
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint((part == 0.f) ? 0.f : part), out_rs,
+                                          off, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  const int rounds = ((nblk - wave + 3) / 4 + 1) / 2;  // >= 1
+  int it = 0;
+  do {
+    step(std::integral_constant<int, 0>{}, blk);
+    step(std::integral_constant<int, 1>{}, blk + 4);
+    blk += 8;
+  } while (++it < rounds);
 }
 
 template <bool BF16>
@@ -159,26 +382,33 @@ hipError_t launch_index_scores(const void* q_idx, const float* w_idx, const void
                                hipStream_t s) {
   if (B == 0 || S == 0 || T == 0) return hipSuccess;
   if (bf16 && n_heads == 64 && head_dim == 128) {
-    const int QR = (S >= 16) ? 4 : 1;
+    const int tiles = (T + kIdxTile - 1) / kIdxTile;
+    if (S < 16) {
+      // about two workgroups per compute unit over all rows, each a whole
+      // number of 128-entry tiles
+      const long rows = (long)B * S;
+      const int nchunk = (int)std::min<long>(tiles, std::max<long>(1, (512 + rows - 1) / rows));
+      const int chunk_tiles = (tiles + nchunk - 1) / nchunk;
+      const int chunk = chunk_tiles * kIdxTile;
+      dim3 grid((unsigned)rows, (tiles + chunk_tiles - 1) / chunk_tiles);
+      hipLaunchKernelGGL((index_scores_stream<64, 128>), grid, dim3(256), 0, s,
+                         reinterpret_cast<const u16*>(q_idx), w_idx,
+                         reinterpret_cast<const u16*>(k_pool), scores, q_pos, S, T, m, chunk);
+      return hipGetLastError();
+    }
+    constexpr int QR = 8;
     const int nrb = (S + QR - 1) / QR;
     // split the pool over workgroups until the chip has enough of them
-    int tiles = (T + kIdxTile - 1) / kIdxTile;
-    long wgs = (long)nrb * B;
+    const long wgs = (long)nrb * B;
     int nchunk = 1;
-    if (QR == 1) nchunk = tiles < 8 ? 1 : tiles / 8;             // ~1024 entries each
-    else if (wgs < 1024) nchunk = (int)std::min<long>(tiles, (1024 + wgs - 1) / wgs);
+    if (wgs < 1024) nchunk = (int)std::min<long>(tiles, (1024 + wgs - 1) / wgs);
     int chunk_tiles = (tiles + nchunk - 1) / nchunk;
     nchunk = (tiles + chunk_tiles - 1) / chunk_tiles;
     const int chunk = chunk_tiles * kIdxTile;
     dim3 grid(nrb, nchunk, B);
-    if (QR == 4)
-      hipLaunchKernelGGL((index_scores_mfma<64, 128, 4>), grid, dim3(256), 0, s,
-                         reinterpret_cast<const u16*>(q_idx), w_idx,
-                         reinterpret_cast<const u16*>(k_pool), scores, q_pos, S, T, m, chunk);
-    else
-      hipLaunchKernelGGL((index_scores_mfma<64, 128, 1>), grid, dim3(256), 0, s,
-                         reinterpret_cast<const u16*>(q_idx), w_idx,
-                         reinterpret_cast<const u16*>(k_pool), scores, q_pos, S, T, m, chunk);
+    hipLaunchKernelGGL((index_scores_mfma<64, 128>), grid, dim3(512), 0, s,
+                       reinterpret_cast<const u16*>(q_idx), w_idx,
+                       reinterpret_cast<const u16*>(k_pool), scores, q_pos, S, T, m, chunk);
     return hipGetLastError();
   }
   const size_t lds = (size_t)(n_heads * head_dim + n_heads) * sizeof(float);

@@ -8,14 +8,14 @@
 // kernel is deterministic and matches any correct implementation bit for bit.
 //
 // One workgroup (8 wavefronts) per query row.  Scores become order-preserving
-// 32-bit keys (-0 folded onto +0); the row is kept in LDS when it fits (up to
-// 32768 entries = 128 KiB of the 160 KiB LDS), otherwise re-read from global
-// memory on every pass.  A most-significant-digit-first radix select (four
-// 8-bit digits, per-wave LDS histograms to cut atomic contention, a one-wave
-// suffix scan to pick the digit) finds the k-th largest key K and how many
-// copies of K to keep.  A final pass in index order keeps every key > K and the
-// first copies of K; positions come from wave ballots and popcounts, so the
-// output is written in ascending index order without any sort.
+// 32-bit keys (-0 folded onto +0).  A most-significant-digit-first radix
+// select finds the k-th largest key K and how many copies of K to keep; a
+// final pass in index order keeps every key > K and the first copies of K,
+// with output positions from wave ballots and popcounts, so the result is
+// written in ascending index order without any sort.  Rows of up to 32768
+// entries keep their keys in registers for the whole selection (three passes
+// over 11 + 11 + 10 bits); longer rows re-read the scores from global memory
+// on each of four 8-bit passes.
 #include "csa_device.hpp"
 
 namespace csa {
@@ -23,7 +23,6 @@ namespace {
 
 constexpr int kTopkThreads = 512;
 constexpr int kTopkWaves = kTopkThreads / 64;
-constexpr int kTopkLdsCap = 32768;
 constexpr int kHistWords = kTopkWaves * 256;
 constexpr int kMetaWords = 64;
 
@@ -37,14 +36,12 @@ __device__ __forceinline__ uint64_t lanemask_lt(int lane) {
   return lane == 0 ? 0ull : (~0ull >> (64 - lane));
 }
 
-template <bool IN_LDS>
-__global__ __launch_bounds__(kTopkThreads) void topk_kernel(
+__global__ __launch_bounds__(kTopkThreads) void topk_global(
     const float* __restrict__ scores, int* __restrict__ idx, const int* __restrict__ q_pos,
     int S, int T, int k, int m) {
-  extern __shared__ uint32_t sm[];
+  __shared__ uint32_t sm[kHistWords + kMetaWords];
   uint32_t* hist = sm;                            // [waves][256]
   int* meta = reinterpret_cast<int*>(sm + kHistWords);  // selection + per-wave counts
-  uint32_t* keys = sm + kHistWords + kMetaWords;  // [R] when IN_LDS
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const long row = blockIdx.x;
@@ -57,16 +54,13 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
     for (int j = tid; j < k; j += kTopkThreads) out[j] = j < R ? j : -1;
     return;
   }
-  if (IN_LDS)
-    for (int j = tid; j < R; j += kTopkThreads) keys[j] = score_key(src[j]);
-
   uint32_t prefix = 0u, pmask = 0u;
   int kk = k;  // rank still to find among keys matching prefix
   for (int shift = 24; shift >= 0; shift -= 8) {
     for (int j = tid; j < kHistWords; j += kTopkThreads) hist[j] = 0u;
     __syncthreads();
     for (int j = tid; j < R; j += kTopkThreads) {
-      const uint32_t key = IN_LDS ? keys[j] : score_key(src[j]);
+      const uint32_t key = score_key(src[j]);
       if ((key & pmask) == prefix) atomicAdd(&hist[wave * 256 + ((key >> shift) & 255u)], 1u);
     }
     __syncthreads();
@@ -115,7 +109,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
   for (int base = 0; base < R && sel_base < k; base += kTopkThreads, ++it) {
     const int j = base + tid;
     uint32_t key = 0u;
-    if (j < R) key = IN_LDS ? keys[j] : score_key(src[j]);
+    if (j < R) key = score_key(src[j]);
     const bool gt = j < R && key > K;
     const bool eq = j < R && key == K;
     const uint64_t mgt = __ballot(gt), meq = __ballot(eq);
@@ -145,20 +139,159 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
   }
 }
 
+// Register path (rows of up to 512 * KPT entries): thread t keeps the keys
+// of entries 512 j + t (j < KPT) in registers for the whole selection.  Radix
+// select over 11 + 11 + 10 bits with one shared LDS histogram (2048 bins, two
+// copies so that clearing the next one needs no extra barrier), each pass a
+// block-wide suffix scan of the bins.  Final pass: for each 512-entry slice,
+// wave ballots of (key > K) and (key == K) give every entry its rank among the
+// earlier ones; the per-(slice, wave) totals are prefix-summed once, so the
+// ordered compaction needs a single barrier.
+template <int KPT>
+__global__ __launch_bounds__(kTopkThreads) void topk_reg(
+    const float* __restrict__ scores, int* __restrict__ idx, const int* __restrict__ q_pos,
+    int S, int T, int k, int m) {
+  constexpr int NW = kTopkWaves;
+  __shared__ uint32_t hist[2][2048];
+  __shared__ int wtot[NW];
+  __shared__ int meta[2];
+  __shared__ int gtot[KPT * NW], etot[KPT * NW];  // per (slice, wave) counts, then prefixes
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const long row = blockIdx.x;
+  const int b = (int)(row / S), i = (int)(row - (long)b * S);
+  const int R = ready_count((long)q_pos[b] + i, m, T);
+  int* out = idx + row * k;
+  const float* src = scores + row * T;
+
+  if (R <= k) {  // every ready entry is kept
+    for (int j = tid; j < k; j += kTopkThreads) out[j] = j < R ? j : -1;
+    return;
+  }
+  // keys of entries 512 j + tid.  Entries past R get key 0, below the key of
+  // any score that is not NaN (-inf maps to 0x007fffff), so they fall in the
+  // lowest bin of the first pass, never match a later prefix and are never
+  // kept: no separate validity test is needed.
+  // (the loads are unconditional, clamped into the row, so that all of them
+  // are in flight together)
+  float sv[KPT];
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) sv[j] = src[min(j * kTopkThreads + tid, R - 1)];
+  uint32_t key[KPT];
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) key[j] = j * kTopkThreads + tid < R ? score_key(sv[j]) : 0u;
+
+  uint32_t prefix = 0u, pmask = 0u;
+  int kk = k;
+  int buf = 0;
+  for (int j = tid; j < 2048; j += kTopkThreads) hist[0][j] = 0u;
+#pragma unroll
+  for (int pass = 0; pass < 3; ++pass) {
+    const int shift = pass == 0 ? 21 : pass == 1 ? 10 : 0;
+    const uint32_t dmask = pass == 2 ? 1023u : 2047u;
+    uint32_t* h = hist[buf];
+    __syncthreads();  // h cleared, meta of the last pass read
+#pragma unroll
+    for (int j = 0; j < KPT; ++j)
+      if ((key[j] & pmask) == prefix) atomicAdd(&h[(key[j] >> shift) & dmask], 1u);
+    // clear the other copy for the next pass meanwhile
+    for (int j = tid; j < 2048; j += kTopkThreads) hist[buf ^ 1][j] = 0u;
+    __syncthreads();
+    // thread t owns bins 4t .. 4t+3; suffix sums over the bins above
+    const uint4 hb = *reinterpret_cast<const uint4*>(&h[4 * tid]);
+    const int loc = (int)(hb.x + hb.y + hb.z + hb.w);
+    int suf = loc;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int v = __shfl_down(suf, off, 64);
+      if (lane + off < 64) suf += v;
+    }
+    if (lane == 0) wtot[wave] = suf;
+    __syncthreads();
+    int above = suf - loc;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) above += w > wave ? wtot[w] : 0;
+    const int cnt[4] = {(int)hb.x, (int)hb.y, (int)hb.z, (int)hb.w};
+#pragma unroll
+    for (int u = 3; u >= 0; --u) {
+      if (above < kk && above + cnt[u] >= kk) {
+        meta[0] = 4 * tid + u;
+        meta[1] = above;
+      }
+      above += cnt[u];
+    }
+    __syncthreads();
+    const uint32_t digit = (uint32_t)meta[0];
+    kk -= meta[1];
+    prefix |= digit << shift;
+    pmask |= dmask << shift;
+    buf ^= 1;
+  }
+
+  // prefix is the k-th largest key K: keep every key > K and the first kk
+  // copies of K, in index order
+  const uint32_t K = prefix;
+  const uint64_t lt = lanemask_lt(lane);
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) {
+    const uint64_t mg = __ballot(key[j] > K);
+    const uint64_t me = __ballot(key[j] == K);
+    if (lane == 0) {
+      gtot[j * NW + wave] = __popcll(mg);
+      etot[j * NW + wave] = __popcll(me);
+    }
+    __builtin_amdgcn_sched_barrier(0);  // one slice at a time (scalar registers)
+  }
+  __syncthreads();
+  // exclusive prefix over (slice, wave) in index order, by wave 0
+  if (wave == 0) {
+    int rg = 0, re = 0;
+    for (int base = 0; base < KPT * NW; base += 64) {
+      const int s = base + lane;
+      int g = s < KPT * NW ? gtot[s] : 0, e = s < KPT * NW ? etot[s] : 0;
+      int ig = g, ie = e;  // inclusive scans over the 64 lanes
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int vg = __shfl_up(ig, off, 64), ve = __shfl_up(ie, off, 64);
+        if (lane >= off) { ig += vg; ie += ve; }
+      }
+      if (s < KPT * NW) { gtot[s] = rg + ig - g; etot[s] = re + ie - e; }
+      rg += __shfl(ig, 63, 64);
+      re += __shfl(ie, 63, 64);
+    }
+  }
+  __syncthreads();
+  // the ballots are recomputed rather than kept (64 of them would not fit the
+  // scalar registers): opaque keys stop the compiler from reusing the first
+  // ones
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) asm volatile("" : "+v"(key[j]));
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) {
+    const bool gt = key[j] > K, eq = key[j] == K;
+    const uint64_t mg = __ballot(gt), me = __ballot(eq);
+    const int gb = gtot[j * NW + wave] + __popcll(mg & lt);
+    const int eb = etot[j * NW + wave] + __popcll(me & lt);
+    if (gt || (eq && eb < kk)) out[gb + min(eb, kk)] = j * kTopkThreads + tid;
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
 }  // namespace
 
 hipError_t launch_topk(const float* scores, int* idx, const int* q_pos, int B, int S,
                        int T, int k, int m, hipStream_t s) {
   const long rows = (long)B * S;
   if (rows == 0) return hipSuccess;
-  const bool in_lds = T <= kTopkLdsCap;
-  const size_t lds = (size_t)(kHistWords + kMetaWords + (in_lds ? T : 0)) * sizeof(uint32_t);
-  if (in_lds)
-    hipLaunchKernelGGL(topk_kernel<true>, dim3((unsigned)rows), dim3(kTopkThreads), lds, s,
-                       scores, idx, q_pos, S, T, k, m);
+  const dim3 grid((unsigned)rows), block(kTopkThreads);
+  if (T <= 4 * kTopkThreads)
+    hipLaunchKernelGGL(topk_reg<4>, grid, block, 0, s, scores, idx, q_pos, S, T, k, m);
+  else if (T <= 16 * kTopkThreads)
+    hipLaunchKernelGGL(topk_reg<16>, grid, block, 0, s, scores, idx, q_pos, S, T, k, m);
+  else if (T <= 64 * kTopkThreads)
+    hipLaunchKernelGGL(topk_reg<64>, grid, block, 0, s, scores, idx, q_pos, S, T, k, m);
   else
-    hipLaunchKernelGGL(topk_kernel<false>, dim3((unsigned)rows), dim3(kTopkThreads), lds, s,
-                       scores, idx, q_pos, S, T, k, m);
+    hipLaunchKernelGGL(topk_global, grid, block, 0, s, scores, idx, q_pos, S, T, k, m);
   return hipGetLastError();
 }
 

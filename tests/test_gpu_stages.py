@@ -77,6 +77,8 @@ def _score_bound(q, w, k):
     # (dtype, B, S, nI, cI, T, m, q_pos): the 64x128 bf16 shape runs on matrix cores
     ("bf16", 2, 61, 64, 128, 300, 4, [0, 700]),     # prefill mode, ragged rows
     ("bf16", 5, 1, 64, 128, 3000, 4, [12000, 11999, 3, 0, 40000]),  # decode mode
+    # few rows per sequence, many blocks per wave (several rounds, ragged ends)
+    ("bf16", 16, 8, 64, 128, 3000, 4, [11990 + 13 * b - 4000 * (b % 3) for b in range(16)]),
     ("bf16", 1, 200, 64, 128, 200, 1, [0]),         # token level (m=1)
     ("f32", 2, 33, 2, 32, 64, 4, [0, 100]),         # generic kernel
     ("bf16", 1, 20, 4, 64, 50, 4, [150]),           # generic kernel, bf16
