@@ -31,6 +31,14 @@ namespace {
 
 constexpr int kIdxTile = 128;  // pool entries per LDS tile
 
+// max(x, 0) as one integer max on the bit pattern: a negative float (sign bit
+// set) is a negative integer, so it becomes +0; everything else is unchanged.
+// (fmaxf would cost a second instruction per value: the compiler first quiets
+// a possible signalling NaN coming out of the matrix core.)
+__device__ __forceinline__ float relu_bits(float x) {
+  return __int_as_float(max(__float_as_int(x), 0));
+}
+
 // Many query rows (prefill, token-level indexer): workgroup = 8 consecutive
 // query rows (one per wave) x one chunk of the pool.  The pool is walked in
 // 128-entry tiles (32 KiB), triple-buffered in LDS and shared by the 8 rows:
@@ -56,7 +64,6 @@ __global__ __launch_bounds__(512) void index_scores_mfma(
   __shared__ __attribute__((aligned(16))) unsigned char kb0[TB];
   __shared__ __attribute__((aligned(16))) unsigned char kb1[TB];
   __shared__ __attribute__((aligned(16))) unsigned char kb2[TB];
-  __shared__ __attribute__((aligned(16))) float wsh[QR][64];
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int b = blockIdx.z;
@@ -83,7 +90,15 @@ __global__ __launch_bounds__(512) void index_scores_mfma(
     for (int ks = 0; ks < KS; ++ks)
       a[mb][ks] = as_bf16x8(*reinterpret_cast<const uint4*>(
           q_idx + (row * NI + 32 * mb + (lane & 31)) * CI + 16 * ks + 8 * (lane >> 5)));
-  wsh[wave][lane] = w_idx[row * NI + min(lane, NI - 1)];
+  // head weights in accumulator order: wreg[mb][q] = w_idx[row][32mb + 8q +
+  // 4(lane/32) .. +3]
+  float4 wreg[MB][4];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      wreg[mb][q] = *reinterpret_cast<const float4*>(w_idx + row * NI + 32 * mb + 8 * q +
+                                                     4 * (lane >> 5));
 
   // pool rows lo .. hi-1 of this sequence; tiles past hi read zeros
   const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
@@ -116,9 +131,10 @@ __global__ __launch_bounds__(512) void index_scores_mfma(
   const __amdgpu_buffer_rsrc_t out_rs = __builtin_amdgcn_make_buffer_rsrc(
       scores + row * T + lo, 0, (hi_my - lo) * 4, 0x00020000);
 
-  // tile j: the products of the 8 rows on buffer J; exactly four stores per
-  // wave and tile (past the row's entries they are dropped), which keeps the
-  // wait counts below exact
+  // tile j: the products of the 8 rows on buffer J, four 32-entry blocks per
+  // wave; blocks past the row's entries are skipped, but every block issues
+  // exactly one store (dropped past the row's entries), which keeps the wait
+  // counts below exact.  The epilogue sums in four independent chains.
   auto compute = [&](auto JC, int tile) __attribute__((always_inline)) {
     constexpr int J = decltype(JC)::value;
     const unsigned char* buf = J == 0 ? kb0 : J == 1 ? kb1 : kb2;
@@ -126,7 +142,7 @@ __global__ __launch_bounds__(512) void index_scores_mfma(
     for (int nb = 0; nb < NT / 32; ++nb) {
       const int e0 = tile * NT + 32 * nb;  // first entry of the block, from lo
       float part = 0.f;
-      if (lo + e0 < hi_my) {               // uniform over the wave
+      if (lo + e0 < hi_my) {
         f32x16 acc[MB];
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
@@ -140,17 +156,18 @@ __global__ __launch_bounds__(512) void index_scores_mfma(
             acc[mb] = mfma32x32x16(a[mb][ks], as_bf16x8(bv), acc[mb]);
         }
         // accumulator register r holds head 32mb + 8(r/4) + 4(lane/32) + r%4
+        float p4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            const float4 w4 = *reinterpret_cast<const float4*>(
-                &wsh[wave][32 * mb + 8 * q + 4 * (lane >> 5)]);
-            part += w4.x * fmaxf(acc[mb][4 * q], 0.f);
-            part += w4.y * fmaxf(acc[mb][4 * q + 1], 0.f);
-            part += w4.z * fmaxf(acc[mb][4 * q + 2], 0.f);
-            part += w4.w * fmaxf(acc[mb][4 * q + 3], 0.f);
+            const float4 w4 = wreg[mb][q];
+            p4[0] += w4.x * relu_bits(acc[mb][4 * q]);
+            p4[1] += w4.y * relu_bits(acc[mb][4 * q + 1]);
+            p4[2] += w4.z * relu_bits(acc[mb][4 * q + 2]);
+            p4[3] += w4.w * relu_bits(acc[mb][4 * q + 3]);
           }
+        part = (p4[0] + p4[1]) + (p4[2] + p4[3]);
         // the other half of the heads sits in lane l ^ 32
         const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part),
                                                          __float_as_uint(part), false, false);
@@ -318,10 +335,10 @@ __global__ __launch_bounds__(256, 2) void index_scores_stream(
       for (int q = 0; q < 4; ++q) {
         const float4 w4 = *reinterpret_cast<const float4*>(
             &wsh[wave][32 * mb + 8 * q + 4 * (lane >> 5)]);
-        part += w4.x * fmaxf(acc[mb][4 * q], 0.f);
-        part += w4.y * fmaxf(acc[mb][4 * q + 1], 0.f);
-        part += w4.z * fmaxf(acc[mb][4 * q + 2], 0.f);
-        part += w4.w * fmaxf(acc[mb][4 * q + 3], 0.f);
+        part += w4.x * relu_bits(acc[mb][4 * q]);
+        part += w4.y * relu_bits(acc[mb][4 * q + 1]);
+        part += w4.z * relu_bits(acc[mb][4 * q + 2]);
+        part += w4.w * relu_bits(acc[mb][4 * q + 3]);
       }
     // the other half of the heads sits in lane l ^ 32
     const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part),
