@@ -342,45 +342,30 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(MfmaArgs args) {
   const int pool_bytes = pool_base ? p.T * D * 2 : 0;
   const int lane_off = lane << 4;
 
-  // row ids of this S wave's rows (8w .. 8w+7) of a tile: kv_win / pool row of
-  // this sequence, -1 = empty (or past the tile range).  Wave-uniform: the
-  // index entries come in with scalar loads (read through the constant
-  // address space: the index is never written while the kernel runs).
-  typedef __attribute__((address_space(4))) const int cint;
-  typedef int i32x4 __attribute__((ext_vector_type(4)));
-  typedef __attribute__((address_space(4))) const i32x4 ci32x4;
-  cint* idx_row = p.idx ? (cint*)(p.idx + row * p.k) : nullptr;
-  struct Rid8 { int r[RPW]; };
-  auto rid8 = [=](int tile) __attribute__((always_inline)) -> Rid8 {
-    Rid8 o;
-#pragma unroll
-    for (int q = 0; q < RPW; ++q) o.r[q] = -1;
-    if (tile >= tile1) return o;
+  // Row ids of a tile's rows 8w .. 8w+7 (w = the wave's index in its role):
+  // kv_win / pool row of this sequence, -1 = empty (or past the tile range).
+  // The pool index entries come in with ONE vector load per tile (lane l:
+  // entry of row 8w + l % 8), through a bounded descriptor, so that a window
+  // tile or a tile past the range reads nothing; vector loads keep the scalar
+  // data counter free for LDS waits, and retire in order with the gathers.
+  const __amdgpu_buffer_rsrc_t idx_rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<int*>(p.idx ? p.idx + row * p.k : p.q_pos), 0, p.idx ? p.k * 4 : 0,
+      0x00020000);
+  auto rid_load = [=](int tile) __attribute__((always_inline)) -> int {
+    const int jj = (tile - WT) * kNK + w4 * RPW + (lane & 7);  // < 0 for window tiles
+    const int off = jj * 4;  // a negative offset is out of range: reads 0
+    return (int)__builtin_amdgcn_raw_buffer_load_b32(idx_rs, off, 0, 0);
+  };
+  // row id of row 8w + lane % 8 of a tile, from its loaded index entry
+  auto rid_of = [=](int tile, int raw) __attribute__((always_inline)) -> int {
+    if (tile >= tile1) return -1;
     if (tile < WT) {
-      const int jj = tile * kNK + w4 * RPW;
-#pragma unroll
-      for (int q = 0; q < RPW; ++q) o.r[q] = jj + q < n_win ? r_lo + jj + q : -1;
-      return o;
+      const int jj = tile * kNK + w4 * RPW + (lane & 7);
+      return jj < n_win ? r_lo + jj : -1;
     }
-    const int jj = (tile - WT) * kNK + w4 * RPW;
-    int w[RPW];
-    if (p.dense) {
-#pragma unroll
-      for (int q = 0; q < RPW; ++q) w[q] = jj + q;
-    } else if (jj + RPW <= p.k) {
-#pragma unroll
-      for (int q = 0; q < RPW; q += 4) {  // scalar loads of 4 entries
-        const i32x4 v = *(ci32x4*)(idx_row + jj + q);
-        w[q] = v[0]; w[q + 1] = v[1]; w[q + 2] = v[2]; w[q + 3] = v[3];
-      }
-    } else {
-#pragma unroll
-      for (int q = 0; q < RPW; ++q) w[q] = jj + q < p.k ? idx_row[jj + q] : -1;
-    }
-#pragma unroll
-    for (int q = 0; q < RPW; ++q)
-      o.r[q] = (jj + q < npool && w[q] >= 0 && w[q] < p.T) ? w[q] : -1;
-    return o;
+    const int jj = (tile - WT) * kNK + w4 * RPW + (lane & 7);
+    const int w = p.dense ? jj : raw;
+    return (jj < npool && w >= 0 && w < p.T) ? w : -1;
   };
 
   // This wave's share of a tile's gather into buffer J: rows 8w .. 8w+7, one
@@ -393,13 +378,10 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(MfmaArgs args) {
   // wait-count model treats a register that fed a gather as pending until the
   // gather lands, so a per-gather temporary reused later for other data would
   // cost a wait).
-  auto issue = [=](auto JC, int tile, const Rid8 rids) __attribute__((always_inline)) {
+  auto issue = [=](auto JC, int tile, int rid) __attribute__((always_inline)) {
     constexpr int J = decltype(JC)::value;
     unsigned char* kbuf = kbuf_of(JC);
-    int rl = -1;
-#pragma unroll
-    for (int q = 0; q < RPW; ++q) rl = lane == q ? rids.r[q] : rl;
-    if (lane < RPW) bias_s[J * kNK + w4 * RPW + lane] = rl >= 0 ? 0.f : -INFINITY;
+    if (lane < RPW) bias_s[J * kNK + w4 * RPW + lane] = rid >= 0 ? 0.f : -INFINITY;
     const bool win = tile < WT;
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<u16*>(win ? win_base : pool_base), 0,
@@ -408,16 +390,14 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(MfmaArgs args) {
 #pragma unroll
     for (int q = 0; q < RPW; ++q) {
       const int r = w4 * RPW + q;
-      const int soff = (rids.r[q] >= 0 ? rids.r[q] : stand_in) * (D * 2);
+      const int rq = __builtin_amdgcn_readlane(rid, q);
+      const int soff = (rq >= 0 ? rq : stand_in) * (D * 2);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(kbuf + r * KT::ROWB), 16,
                                                lane_off, soff, 0, 0);
     }
     if constexpr (KT::TAIL > 0) {
       // the tails of this wave's 8 rows: lane l takes row l%8, chunk l/8
-      int rid_l = stand_in;
-#pragma unroll
-      for (int q = 0; q < RPW; ++q)
-        if ((lane & 7) == q && rids.r[q] >= 0) rid_l = rids.r[q];
+      const int rid_l = rid >= 0 ? rid : stand_in;
       unsigned char* tbuf = tbuf_of(JC) + w4 * KT::TBLK;
       // (the offset goes through a named value: written inline in the call,
       // the host pass of this template drops the kernel's launch stub)
@@ -431,21 +411,26 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(MfmaArgs args) {
   uint4 qraw[KS];
   const bool use_sink = p.sink && !split_mode;
   float sink_l2 = -INFINITY;
+  // PV waves: index entries of the first NBUF tiles, then the first NBUF-1
+  // gathers (issued whether or not the tiles exist, as in the loop, so that
+  // the wait counts are the same on every path)
+  int rid_raw_next = 0;
   auto prologue_issue = [&]() __attribute__((always_inline)) {
-    // the first NBUF-1 gathers (issued whether or not the tiles exist, as in
-    // the loop, so that the wait counts are the same on every path)
-    issue(std::integral_constant<int, 0>{}, tile0, rid8(tile0));
-    issue(std::integral_constant<int, 1>{}, tile0 + 1, rid8(tile0 + 1));
-    if constexpr (NBUF == 4) issue(std::integral_constant<int, 2>{}, tile0 + 2, rid8(tile0 + 2));
+    int raw[NBUF];
+#pragma unroll
+    for (int u = 0; u < NBUF; ++u) raw[u] = rid_load(tile0 + u);
+    issue(std::integral_constant<int, 0>{}, tile0, rid_of(tile0, raw[0]));
+    issue(std::integral_constant<int, 1>{}, tile0 + 1, rid_of(tile0 + 1, raw[1]));
+    if constexpr (NBUF == 4) issue(std::integral_constant<int, 2>{}, tile0 + 2, rid_of(tile0 + 2, raw[2]));
+    rid_raw_next = raw[NBUF - 1];
   };
   if (s_role) {
     const u16* qrow = reinterpret_cast<const u16*>(p.q) + (row * H + h0 + hq) * D;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
       qraw[ks] = *reinterpret_cast<const uint4*>(qrow + 32 * ks + 8 * g);
-    // the sink logit, loaded before the gathers so that waiting for it does
-    // not wait for them
     if (use_sink) sink_l2 = p.sink[h0 + hq] * kLog2e;
+  } else {
     prologue_issue();
   }
 
@@ -580,7 +565,6 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(MfmaArgs args) {
     __builtin_amdgcn_sched_barrier(0);
     softmax(par, sa[0] + sa[2] + bias0, sa[1] + sa[3] + bias1, first);
   };
-  constexpr int kAhead = (NBUF - 2) * G;   // loads still in flight at a wait
   if (tid < 2 * NS) rflag_s[tid] = 0;
   // restart requests for tile j+1 (written by the S waves in step j)
   auto again_of = [&](int par) __attribute__((always_inline)) -> bool {
@@ -588,30 +572,25 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(MfmaArgs args) {
     return __builtin_amdgcn_readfirstlane(rf.x | rf.y | rf.z | rf.w) != 0;
   };
   // Both roles run the same barriers: two in the prologue, one per iteration
-  // (whole rounds of NBUF iterations; the ones past the last tile keep only
-  // the barrier and, in the S waves, the empty gathers, so that the loads
-  // issued are the same on every path through the loop), one per restart and
-  // one before the output.
+  // (whole rounds of NBUF iterations), one per restart and one before the
+  // output.  Between barriers B(j) and B(j+1) the S waves run S + softmax of
+  // tile j+1 while the PV waves run PV of tile j and gather tile j+NBUF-1
+  // (into the buffer of tile j-1).  The PV waves alone touch global memory in
+  // the loop, so they alone wait for it: before B(j+1) their loads of tile
+  // j+2 must have landed.  Their vector memory operations per iteration, in
+  // order: the index load of tile j+NBUF, the G gathers of tile j+NBUF-1.
   if (s_role) {
     for (;;) {
       // ---- prologue: S + softmax of the first tile
-      wait_vmcnt<kAhead>();
       lds_barrier();  // tile0 landed
       s_step(std::integral_constant<int, 0>{}, 0, true);
-      Rid8 rid_next = rid8(tile0 + NBUF - 1);
-      wait_vmcnt<(NBUF - 3) * G>();  // tile0+1 landed
       lds_barrier();  // B(tile0)
       bool again = false;
       auto iter = [&](auto JC, int j) __attribute__((always_inline)) {
         constexpr int J = decltype(JC)::value;
         const int par = (j - tile0) & 1;
-        issue(std::integral_constant<int, (J + NBUF - 1) % NBUF>{}, j + NBUF - 1, rid_next);
         if (j < tile1 && !again)
           s_step(std::integral_constant<int, (J + 1) % NBUF>{}, par ^ 1, false);
-        rid_next = rid8(j + NBUF);
-        // this wave's loads of tile j+2 have landed (those of j+3 may be in
-        // flight)
-        wait_vmcnt<(NBUF - 3) * G>();
         lds_barrier();  // B(j+1)
         again = again_of(par);
       };
@@ -621,16 +600,12 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(MfmaArgs args) {
         iter(std::integral_constant<int, 2>{}, tile + 2);
         if constexpr (NBUF == 4) iter(std::integral_constant<int, 3>{}, tile + 3);
       }
-      // no gather may still be writing this workgroup's LDS when it exits or
-      // starts over
-      wait_vmcnt<0>();
       if (!again) break;
       // ---- restart with the reference max raised to the largest one seen
       lds_barrier();
       mref = mseen;
       lrun = use_sink ? __builtin_amdgcn_exp2f(sink_l2 - mref) : 0.f;
       if (tid < 2 * NS) rflag_s[tid] = 0;
-      prologue_issue();
     }
     // ---- running max and sum of each head, for the PV waves / the merge
     if (g == 0) {
@@ -669,12 +644,22 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(MfmaArgs args) {
   };
 
   for (;;) {
+    wait_vmcnt<(NBUF - 2) * G>();
     lds_barrier();  // tile0 landed
+    wait_vmcnt<(NBUF - 3) * G>();
     lds_barrier();  // B(tile0)
     bool again = false;
     auto iter = [&](auto JC, int j) __attribute__((always_inline)) {
+      constexpr int J = decltype(JC)::value;
       const int par = (j - tile0) & 1;
+      const int raw = rid_load(j + NBUF);
+      issue(std::integral_constant<int, (J + NBUF - 1) % NBUF>{}, j + NBUF - 1,
+            rid_of(j + NBUF - 1, rid_raw_next));
+      rid_raw_next = raw;
       if (j < tile1 && !again) pv_step(JC, par);
+      // this wave's loads of tile j+2 have landed (NBUF = 4: the index load
+      // of tile j+4 and the gathers of tile j+3 may be in flight)
+      wait_vmcnt<(NBUF - 3) * (G + 1)>();
       lds_barrier();  // B(j+1)
       again = again_of(par);
     };
@@ -684,12 +669,16 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(MfmaArgs args) {
       iter(std::integral_constant<int, 2>{}, tile + 2);
       if constexpr (NBUF == 4) iter(std::integral_constant<int, 3>{}, tile + 3);
     }
+    // no gather may still be writing this workgroup's LDS when it exits or
+    // starts over
+    wait_vmcnt<0>();
     if (!again) break;
     lds_barrier();  // restart
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    prologue_issue();
   }
   lds_barrier();  // the S waves' max and sum are in place
 
