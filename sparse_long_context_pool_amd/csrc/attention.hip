@@ -157,15 +157,19 @@ struct MfmaArgs {
 };
 
 
-// K=V tile of 32 rows in LDS, each row padded by 16 bytes (row stride
-// 2D+16 bytes = 4 or 36 dwords mod 64 banks), so that the S-phase reads (16
-// rows, one 16-byte chunk) and the PV-phase reads (4 rows x 8 consecutive
-// chunks) fall in distinct banks, while every address is a per-lane base plus
-// an immediate offset.  Rows are filled by direct global->LDS 16-byte buffer
-// loads: one wave instruction writes up to 1 KiB contiguous (lane l at +16*l),
-// one instruction per row (plus an 8-lane one for the last 128 bytes when
-// D = 576); lanes whose row slot is empty read past the buffer bound, which
-// writes zeros.
+// K=V tile of 32 rows in LDS, 1 KiB per row, the 16-byte chunks of row r
+// stored XOR-swizzled: logical chunk c sits at chunk c ^ f(r), with
+// f(r) = 2 ((r + 4 h) % 8) + h, h = (r / 8) % 2 (rows r and r + 16 alike).
+// The PV-phase transposing reads (8-byte, served 32 lanes at a time: eight
+// consecutive rows x two adjacent chunks {2i, 2i + 1}) need f / 2 distinct
+// over eight consecutive rows, which any such f gives; among those, this one
+// was measured (with the LDS bank-conflict counter, over candidate swizzles)
+// to leave the S-phase reads (16-byte, sixteen rows x one chunk, four chunks
+// per wave instruction) free of bank conflicts as well.  Rows are filled by
+// direct global->LDS 16-byte buffer loads: one wave instruction per row writes
+// 1 KiB contiguous (lane l at +16 l), lane l reading logical chunk l ^ f(r)
+// from memory; lanes whose row slot is past the tile range read past the
+// buffer bound, which writes zeros.
 //
 // When D > 512 (a 512-wide latent part followed by the rope dims) the first 512
 // dims of each row are laid out as above and the rest goes to a tail area: one
@@ -173,10 +177,17 @@ struct MfmaArgs {
 // bytes apart.  One 64-lane load then gathers the tails of a wave's 8 rows,
 // and the S-phase reads of the tail (16 rows, one chunk) still fall in
 // distinct banks.
+// chunk swizzle of tile row r (see above); rows r and r + 16 share it
+__device__ __forceinline__ int swz(int r) {
+  const int h = (r >> 3) & 1;
+  return ((((r & 7) + 4 * h) & 7) << 1) | h;
+}
+
 template <int D>
 struct KTile {
   static constexpr int MAIN = D > 512 ? 512 : D;    // dims in the row area
-  static constexpr int ROWB = MAIN * 2 + 16;
+  static constexpr int ROWB = MAIN * 2;
+  static_assert(MAIN == 512, "the chunk swizzle assumes 64 chunks per row");
   static constexpr int TAIL = D - MAIN;             // dims in the tail area
   static constexpr int TBLK = 1152;                 // tail block stride (8 rows)
   static_assert(TAIL == 0 || TAIL == 64, "tail of 64 dims");
@@ -340,7 +351,11 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(MfmaArgs args) {
   // tile range: the loads then fill zeros)
   const int win_bytes = win_base ? p.L_win * D * 2 : 0;
   const int pool_bytes = pool_base ? p.T * D * 2 : 0;
-  const int lane_off = lane << 4;
+  // gather source offset of lane l for tile row 8w + q: logical chunk
+  // l ^ f(8w + q) (loop-invariant registers)
+  int lane_off[RPW];
+#pragma unroll
+  for (int q = 0; q < RPW; ++q) lane_off[q] = (lane ^ swz(RPW * w4 + q)) << 4;
 
   // Row ids of a tile's rows 8w .. 8w+7 (w = the wave's index in its role):
   // kv_win / pool row of this sequence, -1 = empty (or past the tile range).
@@ -374,7 +389,7 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(MfmaArgs args) {
   // data that the -inf bias of the slot cancels: its probability is exactly
   // 0); a tile past the range gathers through a zero-size descriptor (zero
   // fill).  The row is wave-uniform: its offset goes in the scalar operand, so
-  // the per-lane operand is the loop-invariant lane_off (the compiler's
+  // the per-lane operands are the loop-invariant lane_off[q] (the compiler's
   // wait-count model treats a register that fed a gather as pending until the
   // gather lands, so a per-gather temporary reused later for other data would
   // cost a wait).
@@ -393,7 +408,7 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(MfmaArgs args) {
       const int rq = __builtin_amdgcn_readlane(rid, q);
       const int soff = (rq >= 0 ? rq : stand_in) * (D * 2);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(kbuf + r * KT::ROWB), 16,
-                                               lane_off, soff, 0, 0);
+                                               lane_off[q], soff, 0, 0);
     }
     if constexpr (KT::TAIL > 0) {
       // the tails of this wave's 8 rows: lane l takes row l%8, chunk l/8
@@ -467,16 +482,23 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(MfmaArgs args) {
   // 16kb + c16, 16-byte chunk 4ks + g.  Four accumulation chains (key block x
   // even/odd k-step).
   constexpr int NG = (KS + 3) / 4;
+  // K row c16 (and 16 + c16, same swizzle), logical chunk 4ks + g: physical
+  // chunk ((4 (ks % 4) + g) ^ f(c16)) + 16 (ks / 4)
+  const int fk = swz(c16);
+  int koff[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) koff[u] = c16 * KT::ROWB + 16 * ((4 * u + g) ^ fk);
   auto k_group = [&](auto JC, int grp, uint4 (&kv)[4][2]) __attribute__((always_inline)) {
-    const unsigned char* krow = kbuf_of(JC) + c16 * KT::ROWB + 16 * g;
+    const unsigned char* kbase = kbuf_of(JC);
     // tail area: rows c16 and 16 + c16 sit in wave blocks c16/8 and 2 + c16/8
     const unsigned char* ktail = tbuf_of(JC) + (c16 >> 3) * KT::TBLK + (c16 & 7) * 16 + 128 * g;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       const int ks = 4 * grp + kk;
       if (ks < KT::MAIN / 32) {
-        kv[kk][0] = *reinterpret_cast<const uint4*>(krow + 64 * ks);
-        kv[kk][1] = *reinterpret_cast<const uint4*>(krow + 16 * KT::ROWB + 64 * ks);
+        const unsigned char* kp = kbase + koff[ks & 3] + 256 * (ks >> 2);
+        kv[kk][0] = *reinterpret_cast<const uint4*>(kp);
+        kv[kk][1] = *reinterpret_cast<const uint4*>(kp + 16 * KT::ROWB);
       } else if (ks < KS) {
         const int u = ks - KT::MAIN / 32;   // tail chunk 4u + g
         kv[kk][0] = *reinterpret_cast<const uint4*>(ktail + 512 * u);
@@ -499,9 +521,14 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(MfmaArgs args) {
   // lane (g, s) of a 16-lane block reads row 4g + s/4, columns 4(s%4) ..
   typedef short s16x4 __attribute__((ext_vector_type(4)));
   typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  // (row r = 4g + s/4 and 16 + r share the swizzle f(r); logical chunk
+  // cbase/8 + 2nb + (s/2) % 2, byte 8 (s % 2) within it)
+  const int rv = 4 * g + (c16 >> 2);
+  const int fv = swz(rv);
+  const int voff0 = rv * KT::ROWB + 2 * cbase + 8 * (c16 & 1);
   auto v_read = [&](auto JC, int nb) __attribute__((always_inline)) -> bf16x8 {
     const unsigned char* vrow =
-        kbuf_of(JC) + (4 * g + (c16 >> 2)) * KT::ROWB + 2 * cbase + 8 * (c16 & 3) + 32 * nb;
+        kbuf_of(JC) + voff0 + 16 * ((2 * nb + ((c16 >> 1) & 1)) ^ fv);
     const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)vrow);
     const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vrow + 16 * KT::ROWB));
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
