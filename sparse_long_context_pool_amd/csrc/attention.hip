@@ -246,7 +246,7 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(MfmaArgs args) {
   __shared__ int rflag_s[2 * NS];                                   // restart requests
   __shared__ __attribute__((aligned(16))) float bias_s[NBUF * kNK]; // 0 / -inf per slot
   __shared__ __attribute__((aligned(16))) float fin_s[HG];          // 1/l
-  __shared__ int flags[20];                                         // scan
+  __shared__ int flags[NS];                                         // scan
   const AttnParams& p = args.p;
   auto kbuf_of = [&](auto JC) __attribute__((always_inline)) -> unsigned char* {
     constexpr int J = decltype(JC)::value;
@@ -309,39 +309,8 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(MfmaArgs args) {
     const long hi = min(t, wp0 + (long)p.L_win - 1);
     if (hi >= lo) { n_win = (int)(hi - lo + 1); r_lo = (int)(lo - wp0); }
   }
-  int npool = 0, pool_stand_in = 0;
-  if (p.dense) {
-    npool = p.pool ? ready_count(t, p.m, p.T) : 0;
-  } else if (p.k > 0 && p.pool) {
-    // the last non-empty slot of the index row bounds the list; the row of the
-    // first non-empty one stands in for the empty slots
-    const int* idx_row = p.idx + row * p.k;
-    int last = -1, first = p.k;
-    for (int j = tid; j < p.k; j += NT) {
-      const int w = idx_row[j];
-      if (w >= 0 && w < p.T) { last = j; first = min(first, j); }
-    }
-#pragma unroll
-    for (int sh = 32; sh > 0; sh >>= 1) {
-      last = max(last, __shfl_xor(last, sh, 64));
-      first = min(first, __shfl_xor(first, sh, 64));
-    }
-    if (lane == 0) { flags[2 + wave] = last; flags[10 + wave] = first; }
-    __syncthreads();
-#pragma unroll
-    for (int q = 0; q < NW; ++q) {
-      npool = max(npool, flags[2 + q] + 1);
-      first = min(first, flags[10 + q]);
-    }
-    // (values read back from LDS or memory: made wave-uniform explicitly so
-    // that they stay in scalar registers)
-    npool = __builtin_amdgcn_readfirstlane(npool);
-    if (npool > 0) pool_stand_in = __builtin_amdgcn_readfirstlane(idx_row[first]);
-  }
   const int WT = (n_win + kNK - 1) / kNK;
-  const int ntiles = WT + (npool + kNK - 1) / kNK;
   const int tile0 = split * args.tiles_per_split;
-  const int tile1 = min(ntiles, tile0 + args.tiles_per_split);
 
   const u16* win_base = p.kv_win ? reinterpret_cast<const u16*>(p.kv_win) + (size_t)b * p.L_win * D
                                  : nullptr;
@@ -371,25 +340,14 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(MfmaArgs args) {
     const int off = jj * 4;  // a negative offset is out of range: reads 0
     return (int)__builtin_amdgcn_raw_buffer_load_b32(idx_rs, off, 0, 0);
   };
-  // row id of row 8w + lane % 8 of a tile, from its loaded index entry
-  auto rid_of = [=](int tile, int raw) __attribute__((always_inline)) -> int {
-    if (tile >= tile1) return -1;
-    if (tile < WT) {
-      const int jj = tile * kNK + w4 * RPW + (lane & 7);
-      return jj < n_win ? r_lo + jj : -1;
-    }
-    const int jj = (tile - WT) * kNK + w4 * RPW + (lane & 7);
-    const int w = p.dense ? jj : raw;
-    return (jj < npool && w >= 0 && w < p.T) ? w : -1;
-  };
-
   // This wave's share of a tile's gather into buffer J: rows 8w .. 8w+7, one
   // 1 KiB load per row (and one 8-lane load of the last 128 bytes when D =
-  // 576).  An empty slot gathers a stand-in row of the same tensor (finite
-  // data that the -inf bias of the slot cancels: its probability is exactly
-  // 0); a tile past the range gathers through a zero-size descriptor (zero
-  // fill).  The row is wave-uniform: its offset goes in the scalar operand, so
-  // the per-lane operands are the loop-invariant lane_off[q] (the compiler's
+  // 576).  An empty slot gathers a stand-in row, the first non-empty one of
+  // the 8 (finite data that the -inf bias of the slot cancels: its
+  // probability is exactly 0); when all 8 are empty (or the tile is past the
+  // range) the loads go through a zero-size descriptor (zero fill).
+  // The row is wave-uniform: its offset goes in the scalar operand, so the
+  // per-lane operands are the loop-invariant lane_off[q] (the compiler's
   // wait-count model treats a register that fed a gather as pending until the
   // gather lands, so a per-gather temporary reused later for other data would
   // cost a wait).
@@ -397,11 +355,13 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(MfmaArgs args) {
     constexpr int J = decltype(JC)::value;
     unsigned char* kbuf = kbuf_of(JC);
     if (lane < RPW) bias_s[J * kNK + w4 * RPW + lane] = rid >= 0 ? 0.f : -INFINITY;
+    const uint64_t live = __ballot(lane < RPW && rid >= 0);
     const bool win = tile < WT;
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<u16*>(win ? win_base : pool_base), 0,
-        tile >= tile1 ? 0 : win ? win_bytes : pool_bytes, 0x00020000);
-    const int stand_in = win ? r_lo : pool_stand_in;
+        live == 0ull ? 0 : win ? win_bytes : pool_bytes, 0x00020000);
+    const int stand_in =
+        live == 0ull ? 0 : __builtin_amdgcn_readlane(rid, (int)__builtin_ctzll(live));
 #pragma unroll
     for (int q = 0; q < RPW; ++q) {
       const int r = w4 * RPW + q;
@@ -421,61 +381,135 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(MfmaArgs args) {
     }
   };
 
-  // ---- Q fragments (B operand of S^T = K Q^T): head hq, dims 32ks + 8g .. +7
-  // (S waves)
-  uint4 qraw[KS];
-  const bool use_sink = p.sink && !split_mode;
-  float sink_l2 = -INFINITY;
-  // PV waves: index entries of the first NBUF tiles, then the first NBUF-1
-  // gathers (issued whether or not the tiles exist, as in the loop, so that
-  // the wait counts are the same on every path)
-  int rid_raw_next = 0;
-  auto prologue_issue = [&]() __attribute__((always_inline)) {
-    int raw[NBUF];
+  // PV waves: the first NBUF-1 gathers and the index entries of the first
+  // NBUF tiles (issued whether or not the tiles exist, as in the loop, so that
+  // the wait counts are the same on every path).  When those gathers are all
+  // window tiles inside this split's range they need neither the index row
+  // nor the list length, so they go out first, before the length is known
+  // (the waits hold for either order).
+  const bool win_first = tile0 + NBUF - 2 < WT && NBUF - 2 < args.tiles_per_split;
+  auto win_rid = [=](int tile) __attribute__((always_inline)) -> int {
+    const int jj = tile * kNK + w4 * RPW + (lane & 7);
+    return jj < n_win ? r_lo + jj : -1;
+  };
+  auto win_issue = [&]() __attribute__((always_inline)) {
+    issue(std::integral_constant<int, 0>{}, tile0, win_rid(tile0));
+    issue(std::integral_constant<int, 1>{}, tile0 + 1, win_rid(tile0 + 1));
+    if constexpr (NBUF == 4) issue(std::integral_constant<int, 2>{}, tile0 + 2, win_rid(tile0 + 2));
+  };
+
+  // ---- length of the key list: every ready entry (dense), else up to the
+  // last non-empty slot of the index row, found by the S waves and passed on
+  // through LDS (both roles call this after their first loads)
+  const bool scan = !p.dense && p.k > 0 && p.pool;
+  int npool = 0, tile1 = 0;
+  auto list_length = [&]() __attribute__((always_inline)) {
+    if (p.dense) {
+      npool = p.pool ? ready_count(t, p.m, p.T) : 0;
+    } else if (scan) {
+      lds_barrier();
 #pragma unroll
-    for (int u = 0; u < NBUF; ++u) raw[u] = rid_load(tile0 + u);
-    issue(std::integral_constant<int, 0>{}, tile0, rid_of(tile0, raw[0]));
-    issue(std::integral_constant<int, 1>{}, tile0 + 1, rid_of(tile0 + 1, raw[1]));
-    if constexpr (NBUF == 4) issue(std::integral_constant<int, 2>{}, tile0 + 2, rid_of(tile0 + 2, raw[2]));
+      for (int q = 0; q < NS; ++q) npool = max(npool, flags[q] + 1);
+      // (read back from LDS: made wave-uniform explicitly so that it stays in
+      // a scalar register)
+      npool = __builtin_amdgcn_readfirstlane(npool);
+    }
+    tile1 = min(WT + (npool + kNK - 1) / kNK, tile0 + args.tiles_per_split);
+  };
+
+  // row id of row 8w + lane % 8 of a tile, from its loaded index entry
+  auto rid_of = [&](int tile, int raw) __attribute__((always_inline)) -> int {
+    if (tile >= tile1) return -1;
+    if (tile < WT) return win_rid(tile);
+    const int jj = (tile - WT) * kNK + w4 * RPW + (lane & 7);
+    const int w = p.dense ? jj : raw;
+    return (jj < npool && w >= 0 && w < p.T) ? w : -1;
+  };
+
+  int rid_raw_next = 0;
+  auto prologue_issue = [&](bool win_done) __attribute__((always_inline)) {
+    int raw[NBUF];
+    if (win_first) {
+      if (!win_done) win_issue();
+#pragma unroll
+      for (int u = 0; u < NBUF; ++u) raw[u] = rid_load(tile0 + u);
+    } else {
+#pragma unroll
+      for (int u = 0; u < NBUF; ++u) raw[u] = rid_load(tile0 + u);
+      issue(std::integral_constant<int, 0>{}, tile0, rid_of(tile0, raw[0]));
+      issue(std::integral_constant<int, 1>{}, tile0 + 1, rid_of(tile0 + 1, raw[1]));
+      if constexpr (NBUF == 4) issue(std::integral_constant<int, 2>{}, tile0 + 2, rid_of(tile0 + 2, raw[2]));
+    }
     rid_raw_next = raw[NBUF - 1];
   };
-  if (s_role) {
+
+  // ---- S waves' first loads: the first index entries of the scan (bounded:
+  // nothing is read without an index row), the sink of head hq, then the Q
+  // fragments (B operand of S^T = K Q^T: head hq, dims 32ks + 8g .. +7), so
+  // that the scan waits for its own loads only.  Every S-wave path issues the
+  // same loads, and the PV waves' code joins none of them, so the compiler's
+  // wait counts never merge paths of different load histories.
+  const bool use_sink = p.sink && !split_mode;
+  const __amdgpu_buffer_rsrc_t sink_rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float*>(use_sink ? p.sink : p.cs), 0, use_sink ? H * 4 : 0, 0x00020000);
+  bf16x8 qf[KS];
+  auto s_first_loads = [&]() __attribute__((always_inline)) -> float {
+    constexpr int NSCAN = 8;   // first scan loads per lane: 2048 index slots
+    int w[NSCAN];
+#pragma unroll
+    for (int u = 0; u < NSCAN; ++u)
+      w[u] = (int)__builtin_amdgcn_raw_buffer_load_b32(idx_rs, 4 * (NS * 64 * u + tid), 0, 0);
+    const float sinkv = __builtin_bit_cast(
+        float, (int)__builtin_amdgcn_raw_buffer_load_b32(sink_rs, 4 * (h0 + hq), 0, 0));
+    __builtin_amdgcn_sched_barrier(0);
+    uint4 qraw[KS];
     const u16* qrow = reinterpret_cast<const u16*>(p.q) + (row * H + h0 + hq) * D;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
       qraw[ks] = *reinterpret_cast<const uint4*>(qrow + 32 * ks + 8 * g);
-    if (use_sink) sink_l2 = p.sink[h0 + hq] * kLog2e;
-  } else {
-    prologue_issue();
-  }
-
-  // rotate the rope slice of q at +t, round to bf16 (S waves; the PV waves
-  // never read these)
-  bf16x8 qf[KS];
+    __builtin_amdgcn_sched_barrier(0);
+    if (scan) {
+      int last = -1;
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    const int d0 = 32 * ks + 8 * g;
-    uint4 u = qraw[ks];
-    if (32 * ks >= rbase && s_role) {
-      float v[8] = {bf_lo(u.x), bf_hi(u.x), bf_lo(u.y), bf_hi(u.y),
-                    bf_lo(u.z), bf_hi(u.z), bf_lo(u.w), bf_hi(u.w)};
-#pragma unroll
-      for (int e = 0; e < 8; e += 2) {
-        const float2 r = cs[t * half + ((d0 + e - rbase) >> 1)];
-        const float a = v[e], bb = v[e + 1];
-        v[e] = a * r.x - bb * r.y;
-        v[e + 1] = a * r.y + bb * r.x;
+      for (int u = 0; u < NSCAN; ++u) {
+        const int jj = NS * 64 * u + tid;
+        if (jj < p.k && w[u] >= 0 && w[u] < p.T) last = jj;
       }
-      u.x = pack2(v[0], v[1]); u.y = pack2(v[2], v[3]);
-      u.z = pack2(v[4], v[5]); u.w = pack2(v[6], v[7]);
+      for (int j = NSCAN * NS * 64 + tid; j < p.k; j += NS * 64) {
+        const int v = (int)__builtin_amdgcn_raw_buffer_load_b32(idx_rs, 4 * j, 0, 0);
+        if (v >= 0 && v < p.T) last = j;
+      }
+#pragma unroll
+      for (int sh = 32; sh > 0; sh >>= 1) last = max(last, __shfl_xor(last, sh, 64));
+      if (lane == 0) flags[w4] = last;
     }
-    qf[ks] = as_bf16x8(u);
-  }
+    // rotate the rope slice of q at +t, round to bf16
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int d0 = 32 * ks + 8 * g;
+      uint4 u = qraw[ks];
+      if (32 * ks >= rbase) {
+        float v[8] = {bf_lo(u.x), bf_hi(u.x), bf_lo(u.y), bf_hi(u.y),
+                      bf_lo(u.z), bf_hi(u.z), bf_lo(u.w), bf_hi(u.w)};
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          const float2 r = cs[t * half + ((d0 + e - rbase) >> 1)];
+          const float a = v[e], bb = v[e + 1];
+          v[e] = a * r.x - bb * r.y;
+          v[e + 1] = a * r.y + bb * r.x;
+        }
+        u.x = pack2(v[0], v[1]); u.y = pack2(v[2], v[3]);
+        u.z = pack2(v[4], v[5]); u.w = pack2(v[6], v[7]);
+      }
+      qf[ks] = as_bf16x8(u);
+    }
+    return sinkv;
+  };
 
   // ---- softmax state of head hq (replicated over the 4 lane groups), log2
-  // domain
+  // domain (set by the S waves once the sink is in)
   const float sl2 = p.scale * kLog2e;
-  float mref = sink_l2, lrun = use_sink ? 1.f : 0.f, mseen = -INFINITY;
+  float sink_l2 = -INFINITY, mref = -INFINITY, lrun = 0.f, mseen = -INFINITY;
 
   // ---- S phase pieces.  S^T for keys 16kb + c16 (kb = 0, 1) and the 16
   // heads of this wave, in groups of 4 k-steps; lane supplies K row
@@ -607,6 +641,11 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(MfmaArgs args) {
   // j+2 must have landed.  Their vector memory operations per iteration, in
   // order: the index load of tile j+NBUF, the G gathers of tile j+NBUF-1.
   if (s_role) {
+    const float sinkv = s_first_loads();
+    list_length();
+    if (use_sink) sink_l2 = sinkv * kLog2e;
+    mref = sink_l2;
+    lrun = use_sink ? 1.f : 0.f;
     for (;;) {
       // ---- prologue: S + softmax of the first tile
       lds_barrier();  // tile0 landed
@@ -616,7 +655,7 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(MfmaArgs args) {
       auto iter = [&](auto JC, int j) __attribute__((always_inline)) {
         constexpr int J = decltype(JC)::value;
         const int par = (j - tile0) & 1;
-        if (j < tile1 && !again)
+        if (j + 1 < tile1 && !again)
           s_step(std::integral_constant<int, (J + 1) % NBUF>{}, par ^ 1, false);
         lds_barrier();  // B(j+1)
         again = again_of(par);
@@ -649,6 +688,9 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(MfmaArgs args) {
   }
 
   // ---- PV waves
+  if (win_first) win_issue();
+  list_length();
+  prologue_issue(true);
   f32x4 acc[4][NB];
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb)
@@ -705,7 +747,7 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(MfmaArgs args) {
     for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    prologue_issue();
+    prologue_issue(false);
   }
   lds_barrier();  // the S waves' max and sum are in place
 
