@@ -32,6 +32,7 @@ namespace {
 
 constexpr int kNK = 32;     // keys per tile
 constexpr int kPS = kNK + 8;  // P row stride (u16): 80 bytes keeps P reads conflict-free
+constexpr int kMaxK = 2048;   // index slots per query the matrix-core kernel keeps in LDS
 
 struct RowInfo {
   int b;
@@ -151,11 +152,12 @@ __global__ __launch_bounds__(256) void attn_generic_kernel(AttnParams p) {
 struct MfmaArgs {
   AttnParams p;
   float* ws;              // split partials, or nullptr
-  int nsplit;
-  int tiles_per_split;
-  int rows_per_xcd;       // query-row remap: consecutive rows on one XCD
+  int nsplit;             // splits of a row's key list (1: none)
+  int tiles_per_split;    // tiles of a split (huge: no split)
+  int nhg;                // groups of 64 heads
+  int rows;               // query rows B * S
+  long n_items;           // work items: rows rounded up to 8, x splits x head groups
 };
-
 
 // K=V tile of 32 rows in LDS, 1 KiB per row, the 16-byte chunks of row r
 // stored XOR-swizzled: logical chunk c sits at chunk c ^ f(r), with
@@ -198,13 +200,26 @@ struct KTile {
 // Split workspace (fp32): [rows][nsplit][H][2] running (max, sum) in the log2
 // domain, then [rows][nsplit][H][dv] unnormalised partial outputs.
 //
-// One workgroup = one query row x one group of 64 heads, 8 waves in two roles,
-// one wave of each role per SIMD (so the hardware interleaves them):
-//   S waves (0..3): wave w owns heads 16w .. 16w+15 for the S products, the
-//     softmax (all keys of a tile, so a head's softmax state lives in one
-//     wave) and the gathers (rows 8w .. 8w+7 of each tile);
+// Work items: (query row, split of its key list, group of 64 heads).  The
+// grid is persistent (one workgroup per compute unit) and workgroup w takes
+// items w, w + grid, w + 2 grid, ...; item i stands for row 8 (i / 8 / (splits
+// x groups)) + i % 8 with its group and split from the middle digits, so the
+// workgroups of one XCD (which gets every 8th workgroup) run the head groups
+// and splits of the same rows side by side and share their gathers in the
+// XCD's L2.  The tiles of a workgroup's items form ONE stream: each item's
+// tile count is padded to whole rounds of NBUF tiles (the padding tiles are
+// skipped), and the gathers, index entries, query fragments and list length
+// of the next item are fetched while the current one is still running, so
+// a row costs no pipeline fill or drain.
+//
+// 8 waves in two roles, one wave of each role per SIMD (so the hardware
+// interleaves them):
+//   S waves (0..3): wave w owns heads 16w .. 16w+15 for the S products and
+//     the softmax (all keys of a tile, so a head's softmax state lives in one
+//     wave), and reads each item's metadata, index-row length and queries;
 //   PV waves (4..7): wave 4+w owns output columns 128w .. 128w+127 and their
-//     accumulators.
+//     accumulators, and loads the index entries and gathers rows 8w .. 8w+7
+//     of each tile.
 // S phase: S^T[keys][heads] = K Q^T with 16x16x32 matrix instructions, the
 // query fragments held in registers; a lane ends with the logits of keys
 // 4g + r and 16 + 4g + r (g = lane / 16, r = 0..3) of its head, which are
@@ -213,19 +228,27 @@ struct KTile {
 // V is read with the gfx950 transposing LDS load (ds_read_b64_tr_b16: 4 keys
 // x 1 column per lane) in the same key order.
 //
-// Pipeline, one barrier per tile: between barriers B(j) and B(j+1) the S
-// waves gather tile j+NBUF-1 (into the buffer of tile j-1) and run S + softmax
-// of tile j+1 (P into the other P buffer) while the PV waves run PV of tile
-// j; the S waves then wait for their loads of tile j+2.
+// Pipeline, one barrier per tile: between barriers B(j) and B(j+1) (stream
+// positions) the S waves run S + softmax of tile j+1 while the PV waves run
+// PV of tile j, load the index entries of tile j+NBUF and gather tile
+// j+NBUF-1 into the buffer of tile j-1; before B(j+1) the PV waves wait for
+// their loads of tile j+2.
 //
+// Softmax: per head a reference max m (log2 domain) that only ever rises:
+// the first tile of an item sets it (from the sink logit and the tile), and a
+// later tile whose max exceeds it by more than 64 raises it to that max, the
+// running sum and the accumulators being scaled by 2^(m_old - m_new) (the S
+// waves publish the factors with the tile's P, the PV waves apply them before
+// adding the tile's P V).  So P <= 2^64 and the rescale is rare.
 template <int D, int NBUF>
 __global__ __launch_bounds__(512) void attn_mfma_kernel(MfmaArgs args) {
-  constexpr int NW = 8, NT = 512, HG = 64, NB = 8;   // NB: 16-column blocks per PV wave
+  constexpr int HG = 64, NB = 8;                     // NB: 16-column blocks per PV wave
   constexpr int KS = D / 32;
   constexpr int R = 64, half = R / 2, rbase = D - R;
-  constexpr float kRestart = 64.f;
+  constexpr float kRescale = 64.f;
   constexpr int NS = 4;                              // S waves (and PV waves)
-  constexpr int RPW = kNK / NS;                      // gathered rows per S wave per tile
+  constexpr int RPW = kNK / NS;                      // gathered rows per PV wave per tile
+  constexpr int NSCAN = kMaxK / (NS * 64);           // index-row loads per S lane
   using KT = KTile<D>;
   constexpr int G = RPW + (KT::TAIL ? 1 : 0);         // gather loads per wave per tile
   static_assert(NBUF == 3 || NBUF == 4, "buffer count");
@@ -243,10 +266,14 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(MfmaArgs args) {
   __shared__ __attribute__((aligned(16))) unsigned char tb3[NBUF == 4 ? KT::TBYTES : 16];
   // every other LDS array is static as well, for the same reason
   __shared__ __attribute__((aligned(16))) u16 Ps[2 * HG * kPS];     // P, bf16, 2 tiles
-  __shared__ int rflag_s[2 * NS];                                   // restart requests
   __shared__ __attribute__((aligned(16))) float bias_s[NBUF * kNK]; // 0 / -inf per slot
-  __shared__ __attribute__((aligned(16))) float fin_s[HG];          // 1/l
-  __shared__ int flags[NS];                                         // scan
+  __shared__ __attribute__((aligned(16))) float alpha_s[2][HG];     // rescale factors
+  __shared__ __attribute__((aligned(16))) int rfl_s[2][NS];         // rescale flags
+  __shared__ __attribute__((aligned(16))) float fin_s[2][HG];       // 1/l per item parity
+  __shared__ __attribute__((aligned(16))) int scan_s[2][NS];        // last live slot, per wave
+  __shared__ __attribute__((aligned(16))) int meta_s[2][4];         // t, n_win, r_lo, bad
+  __shared__ __attribute__((aligned(16))) float2 cs_s[2][R / 2];    // RoPE factors at t
+  __shared__ __attribute__((aligned(16))) int idx_s[2][kMaxK];      // index rows of 2 items
   const AttnParams& p = args.p;
   auto kbuf_of = [&](auto JC) __attribute__((always_inline)) -> unsigned char* {
     constexpr int J = decltype(JC)::value;
@@ -271,95 +298,456 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(MfmaArgs args) {
   const int w4 = wave & (NS - 1);
   const int hq = 16 * w4 + c16;                   // S phase / softmax head
   const int cbase = 128 * w4;                     // PV phase columns
-
-  // query row: consecutive rows stay on one XCD (workgroups go round-robin
-  // over the 8 XCDs), so neighbouring rows share window rows in one L2
-  const long bid = blockIdx.x;
-  const long row = (bid & 7) * (long)args.rows_per_xcd + (bid >> 3);
-  if (row >= (long)p.B * p.S) return;
-  const int split = blockIdx.y;
-  const int h0 = blockIdx.z * HG;
   const int H = p.H, dv = p.dv;
-  const int b = (int)(row / p.S);
-  const long t = (long)p.q_pos[b] + (row - (long)b * p.S);
   const float2* cs = reinterpret_cast<const float2*>(p.cs);
   const bool split_mode = args.nsplit > 1;
+  const bool use_sink = p.sink && !split_mode;
+  const bool scan = !p.dense && p.k > 0 && p.pool;
 
-  if (t < 0 || t >= p.n_pos) {
-    // position outside the RoPE table: the row is written as NaN
-    if (split_mode) {
-      float* ml = args.ws + ((size_t)row * args.nsplit + split) * H * 2;
-      for (int e = tid; e < HG; e += NT) {
-        ml[2 * (h0 + e)] = __int_as_float(0x7fc00000);
-        ml[2 * (h0 + e) + 1] = 0.f;
+  // ---- work items (wave-uniform)
+  struct Item {
+    int row;              // query row, -1: past the end of this workgroup's list
+    int split, h0, b;
+  };
+  auto item_at = [&](int i) __attribute__((always_inline)) -> Item {
+    Item it;
+    it.row = -1; it.split = 0; it.h0 = 0; it.b = 0;
+    const long n = (long)blockIdx.x + (long)i * gridDim.x;
+    if (n >= args.n_items) return it;
+    const int x = (int)(n & 7);
+    const int rest = (int)(n >> 3);
+    const int hg = rest % args.nhg;
+    const int rest2 = rest / args.nhg;
+    it.split = rest2 % args.nsplit;
+    const int row = (rest2 / args.nsplit) * 8 + x;
+    if (row >= args.rows) return it;
+    it.row = row;
+    it.h0 = hg * HG;
+    it.b = row / p.S;
+    return it;
+  };
+  // what the gathers of an item need (t, the window range and the validity
+  // come from the S waves through LDS)
+  struct Meta {
+    int row, split, h0, b, t, bad, n_win, r_lo, WT, tile0, tlim, bound;
+  };
+  auto meta_of = [&](const Item& it, int t, int n_win, int r_lo, int bad)
+      __attribute__((always_inline)) -> Meta {
+    Meta m;
+    m.row = it.row; m.split = it.split; m.h0 = it.h0; m.b = it.b;
+    m.t = t; m.bad = it.row < 0 ? 1 : bad; m.n_win = n_win; m.r_lo = r_lo;
+    m.WT = (n_win + kNK - 1) / kNK;
+    m.tile0 = it.split * args.tiles_per_split;
+    m.tlim = m.tile0 + args.tiles_per_split;
+    // pool slots a gather may read: every ready entry (dense) or the k slots
+    m.bound = m.bad ? 0 : p.dense ? (p.pool ? ready_count(t, p.m, p.T) : 0) : p.k;
+    return m;
+  };
+  // tiles of an item's slice of the key list (at least one, so that every
+  // item has a first tile; the list length npool comes from the scan) and
+  // that count padded to whole rounds
+  auto tiles_of = [&](const Meta& m, int npool) __attribute__((always_inline)) -> int {
+    if (m.bad) return 1;
+    const int nt = min(m.WT + (npool + kNK - 1) / kNK, m.tlim) - m.tile0;
+    return max(nt, 1);
+  };
+  auto padded = [&](int nt) __attribute__((always_inline)) -> int {
+    return (nt + NBUF - 1) / NBUF * NBUF;
+  };
+
+  // ======================================================================
+  // S waves
+  // ======================================================================
+  if (s_role) {
+    // per-sequence values through bounded descriptors (no branch, zero when
+    // absent)
+    const __amdgpu_buffer_rsrc_t qpos_rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<int*>(p.q_pos), 0, p.B * 4, 0x00020000);
+    const bool has_win = p.window > 0 && p.kv_win != nullptr;
+    const __amdgpu_buffer_rsrc_t wpos_rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<int*>(has_win ? p.win_pos0 : p.q_pos), 0, has_win ? p.B * 4 : 0,
+        0x00020000);
+    const __amdgpu_buffer_rsrc_t sink_rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float*>(use_sink ? p.sink : p.cs), 0, use_sink ? H * 4 : 0, 0x00020000);
+    auto load_pos = [&](const Item& it, int& qp, int& wp) __attribute__((always_inline)) {
+      qp = (int)__builtin_amdgcn_raw_buffer_load_b32(qpos_rs, 4 * it.b, 0, 0);
+      wp = (int)__builtin_amdgcn_raw_buffer_load_b32(wpos_rs, 4 * it.b, 0, 0);
+    };
+    // t, window range and validity of an item from its sequence's values
+    auto pos_meta = [&](const Item& it, int qp, int wp, int (&mt)[4])
+        __attribute__((always_inline)) {
+      qp = __builtin_amdgcn_readfirstlane(qp);
+      wp = __builtin_amdgcn_readfirstlane(wp);
+      const long t = (long)qp + (it.row - (long)it.b * p.S);
+      const int bad = (it.row < 0 || t < 0 || t >= p.n_pos) ? 1 : 0;
+      int n_win = 0, r_lo = 0;
+      if (!bad && has_win) {
+        const long lo = max(t - p.window + 1, max(0L, (long)wp));
+        const long hi = min(t, (long)wp + (long)p.L_win - 1);
+        if (hi >= lo) { n_win = (int)(hi - lo + 1); r_lo = (int)(lo - wp); }
       }
-      return;
+      mt[0] = bad ? 0 : (int)t; mt[1] = n_win; mt[2] = r_lo; mt[3] = bad;
+    };
+    // index-row scan of an item: NSCAN loads per lane (through a descriptor
+    // bounded by the row, so nothing is read without one), reduced later
+    auto scan_load = [&](const Item& it, int (&w)[NSCAN]) __attribute__((always_inline)) {
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<int*>(scan && it.row >= 0 ? p.idx + (long)it.row * p.k : p.q_pos), 0,
+          scan && it.row >= 0 ? p.k * 4 : 0, 0x00020000);
+#pragma unroll
+      for (int u = 0; u < NSCAN; ++u)
+        w[u] = (int)__builtin_amdgcn_raw_buffer_load_b32(rs, 4 * (NS * 64 * u + tid), 0, 0);
+    };
+    // an item's index row into LDS (slot = item parity) for the gathers, and
+    // this wave's last live slot of it (-1: none) for the list length
+    auto scan_publish = [&](const int (&w)[NSCAN], int slot) __attribute__((always_inline)) {
+      int last = -1;
+#pragma unroll
+      for (int u = 0; u < NSCAN; ++u) {
+        const int jj = NS * 64 * u + tid;
+        idx_s[slot][jj] = w[u];
+        if (jj < p.k && w[u] >= 0 && w[u] < p.T) last = jj;
+      }
+#pragma unroll
+      for (int sh = 32; sh > 0; sh >>= 1) last = max(last, __shfl_xor(last, sh, 64));
+      if (lane == 0) scan_s[slot][w4] = last;
+    };
+    auto npool_of = [&](const int (&mt)[4], int slot) __attribute__((always_inline)) -> int {
+      if (p.dense) return p.pool ? ready_count(mt[0], p.m, p.T) : 0;
+      if (!scan) return 0;
+      const int4 s4 = *reinterpret_cast<const int4*>(scan_s[slot]);
+      return __builtin_amdgcn_readfirstlane(max(max(s4.x, s4.y), max(s4.z, s4.w)) + 1);
+    };
+
+    // query fragments of an item (B operand of S^T = K Q^T): head h0 + hq,
+    // dims 32ks + 8g .. +7, loaded raw with the RoPE factors of the rope
+    // slice, rotated at +t and rounded to bf16 once they are in
+    bf16x8 qf[KS];
+    constexpr int KR = R / 32;                      // rope k-steps
+    float2 csr[KR][4];
+    float sink_raw = 0.f;
+    auto q_load = [&](const Item& it, int t) __attribute__((always_inline)) {
+      const long row = it.row < 0 ? 0 : it.row;
+      const u16* qrow = reinterpret_cast<const u16*>(p.q) + (row * H + it.h0 + hq) * D;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        qf[ks] = as_bf16x8(*reinterpret_cast<const uint4*>(qrow + 32 * ks + 8 * g));
+#pragma unroll
+      for (int kr = 0; kr < KR; ++kr) {
+        const float4* c4 = reinterpret_cast<const float4*>(cs + (long)t * half + 16 * kr + 4 * g);
+        const float4 a = c4[0], bq = c4[1];
+        csr[kr][0] = make_float2(a.x, a.y); csr[kr][1] = make_float2(a.z, a.w);
+        csr[kr][2] = make_float2(bq.x, bq.y); csr[kr][3] = make_float2(bq.z, bq.w);
+      }
+      sink_raw = __builtin_bit_cast(
+          float, (int)__builtin_amdgcn_raw_buffer_load_b32(sink_rs, 4 * (it.h0 + hq), 0, 0));
+    };
+    // the RoPE factors of the item's position, for the PV waves' output
+    auto cs_publish = [&](int slot) __attribute__((always_inline)) {
+      if (w4 == 0 && c16 == 0) {
+#pragma unroll
+        for (int kr = 0; kr < KR; ++kr)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) cs_s[slot][16 * kr + 4 * g + e] = csr[kr][e];
+      }
+    };
+    auto q_rotate = [&]() __attribute__((always_inline)) {
+#pragma unroll
+      for (int kr = 0; kr < KR; ++kr) {
+        uint4 u = __builtin_bit_cast(uint4, qf[rbase / 32 + kr]);
+        float v[8] = {bf_lo(u.x), bf_hi(u.x), bf_lo(u.y), bf_hi(u.y),
+                      bf_lo(u.z), bf_hi(u.z), bf_lo(u.w), bf_hi(u.w)};
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          const float2 r = csr[kr][e >> 1];
+          const float a = v[e], bb = v[e + 1];
+          v[e] = a * r.x - bb * r.y;
+          v[e + 1] = a * r.y + bb * r.x;
+        }
+        u.x = pack2(v[0], v[1]); u.y = pack2(v[2], v[3]);
+        u.z = pack2(v[4], v[5]); u.w = pack2(v[6], v[7]);
+        qf[rbase / 32 + kr] = as_bf16x8(u);
+      }
+    };
+
+    // ---- softmax state of head hq (replicated over the 4 lane groups), log2
+    // domain
+    const float sl2 = p.scale * kLog2e;
+    float mref = -INFINITY, lrun = 0.f;
+    auto state_reset = [&]() __attribute__((always_inline)) {
+      mref = use_sink ? sink_raw * kLog2e : -INFINITY;
+      lrun = use_sink ? 1.f : 0.f;
+    };
+
+    // ---- S phase pieces.  S^T for keys 16kb + c16 (kb = 0, 1) and the 16
+    // heads of this wave, in groups of 4 k-steps; lane supplies K row
+    // 16kb + c16, 16-byte chunk 4ks + g.  Four accumulation chains (key block x
+    // even/odd k-step).
+    constexpr int NG = (KS + 3) / 4;
+    // K row c16 (and 16 + c16, same swizzle), logical chunk 4ks + g: physical
+    // chunk ((4 (ks % 4) + g) ^ f(c16)) + 16 (ks / 4)
+    const int fk = swz(c16);
+    int koff[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) koff[u] = c16 * KT::ROWB + 16 * ((4 * u + g) ^ fk);
+    auto k_group = [&](auto JC, int grp, uint4 (&kv)[4][2]) __attribute__((always_inline)) {
+      const unsigned char* kbase = kbuf_of(JC);
+      // tail area: rows c16 and 16 + c16 sit in wave blocks c16/8 and 2 + c16/8
+      const unsigned char* ktail = tbuf_of(JC) + (c16 >> 3) * KT::TBLK + (c16 & 7) * 16 + 128 * g;
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const int ks = 4 * grp + kk;
+        if (ks < KT::MAIN / 32) {
+          const unsigned char* kp = kbase + koff[ks & 3] + 256 * (ks >> 2);
+          kv[kk][0] = *reinterpret_cast<const uint4*>(kp);
+          kv[kk][1] = *reinterpret_cast<const uint4*>(kp + 16 * KT::ROWB);
+        } else if (ks < KS) {
+          const int u = ks - KT::MAIN / 32;   // tail chunk 4u + g
+          kv[kk][0] = *reinterpret_cast<const uint4*>(ktail + 512 * u);
+          kv[kk][1] = *reinterpret_cast<const uint4*>(ktail + 2 * KT::TBLK + 512 * u);
+        }
+      }
+    };
+    auto s_group = [&](int grp, const uint4 (&kv)[4][2], f32x4 (&sa)[4])
+        __attribute__((always_inline)) {
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const int ks = 4 * grp + kk;
+        if (ks < KS) {
+          sa[(kk & 1) * 2 + 0] = mfma16x16x32(as_bf16x8(kv[kk][0]), qf[ks], sa[(kk & 1) * 2 + 0]);
+          sa[(kk & 1) * 2 + 1] = mfma16x16x32(as_bf16x8(kv[kk][1]), qf[ks], sa[(kk & 1) * 2 + 1]);
+        }
+      }
+    };
+    // ---- softmax of a tile (buffer J) from its logits: P to P buffer par (key
+    // position 8g + e <-> key 16(e/4) + 4g + (e%4)), with the rescale request
+    auto bias_of = [&](auto JC, int kb) __attribute__((always_inline)) -> f32x4 {
+      return *reinterpret_cast<const f32x4*>(bias_s + decltype(JC)::value * kNK + 16 * kb + 4 * g);
+    };
+    auto softmax = [&](int par, const f32x4 x0, const f32x4 x1, bool first)
+        __attribute__((always_inline)) {
+      // raw logits; the scale (> 0) commutes with the max and goes into the
+      // exponent's fused multiply-add
+      const float m0 = fmaxf(fmaxf(x0[0], x0[1]), fmaxf(x0[2], x0[3]));
+      const float m1 = fmaxf(fmaxf(x1[0], x1[1]), fmaxf(x1[2], x1[3]));
+      const float tmax = xgroup_max(fmaxf(m0, m1)) * sl2;
+      float alpha = 1.f;
+      if (first) {
+        const float mnew = fmaxf(mref, tmax);
+        if (mnew != mref) alpha = __builtin_amdgcn_exp2f(mref - mnew);
+        mref = mnew;
+        rfl_s[par][w4] = 0;
+      } else {
+        const bool up = tmax > mref + kRescale;
+        if (up) {
+          alpha = __builtin_amdgcn_exp2f(mref - tmax);
+          mref = tmax;
+        }
+        // every lane writes the wave's verdict (no branch: this chain is
+        // interleaved with matrix instructions)
+        rfl_s[par][w4] = __ballot(up) != 0ull ? 1 : 0;
+        if (g == 0) alpha_s[par][hq] = alpha;
+      }
+      const float mbase = (mref == -INFINITY) ? 0.f : mref;
+      float pv[8];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        pv[r] = __builtin_amdgcn_exp2f(fmaf(x0[r], sl2, -mbase));
+        pv[4 + r] = __builtin_amdgcn_exp2f(fmaf(x1[r], sl2, -mbase));
+      }
+      const float ps = ((pv[0] + pv[1]) + (pv[2] + pv[3])) + ((pv[4] + pv[5]) + (pv[6] + pv[7]));
+      lrun = lrun * alpha + xgroup_sum(ps);
+      *reinterpret_cast<uint4*>(Ps + (par * HG + hq) * kPS + 8 * g) =
+          make_uint4(pack2(pv[0], pv[1]), pack2(pv[2], pv[3]), pack2(pv[4], pv[5]),
+                     pack2(pv[6], pv[7]));
+    };
+    // ---- S-wave step: S + softmax of the tile in buffer JN (P buffer par),
+    // the K groups read one group ahead of their products
+    auto s_step = [&](auto JN, int par, bool first) __attribute__((always_inline)) {
+      uint4 kv[2][4][2];
+      k_group(JN, 0, kv[0]);
+      const f32x4 bias0 = bias_of(JN, 0), bias1 = bias_of(JN, 1);
+      f32x4 sa[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sa[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int grp = 0; grp < NG; ++grp) {
+        __builtin_amdgcn_sched_barrier(0);
+        if (grp + 1 < NG) k_group(JN, grp + 1, kv[(grp + 1) & 1]);
+        s_group(grp, kv[grp & 1], sa);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      softmax(par, sa[0] + sa[2] + bias0, sa[1] + sa[3] + bias1, first);
+    };
+    // ---- an item's end: running max and sum of each head, for the PV waves
+    // (1/l) or the merge of the splits
+    auto finish = [&](const Item& it, const int (&mt)[4], int slot) __attribute__((always_inline)) {
+      if (g == 0) {
+        const float nanv = __int_as_float(0x7fc00000);
+        if (split_mode) {
+          float* ml = args.ws + ((size_t)it.row * args.nsplit + it.split) * H * 2;
+          ml[2 * (it.h0 + hq)] = mt[3] ? nanv : mref;
+          ml[2 * (it.h0 + hq) + 1] = mt[3] ? 0.f : lrun;
+        } else {
+          fin_s[slot][hq] = mt[3] ? nanv : lrun > 0.f ? 1.f / lrun : 0.f;
+        }
+      }
+    };
+
+    // ---- prologue: items 0 and 1 (metadata, scan of item 0, queries of
+    // item 0), the loads that item 0's last round will need (scan of item 1,
+    // positions of item 2), then the first tile
+    Item cur = item_at(0);
+    if (cur.row < 0) return;                // no item (the PV waves leave as well)
+    Item nx = item_at(1), nx2 = item_at(2);
+    int qp0, wp0, qp1, wp1, qp2, wp2;
+    load_pos(cur, qp0, wp0);
+    load_pos(nx, qp1, wp1);
+    load_pos(nx2, qp2, wp2);
+    int wsc[NSCAN], wsc1[NSCAN];
+    scan_load(cur, wsc);
+    scan_load(nx, wsc1);
+    int mt_cur[4], mt_nx[4], mt_nx2[4];
+    pos_meta(cur, qp0, wp0, mt_cur);
+    q_load(cur, mt_cur[0]);
+    scan_publish(wsc, 0);
+    scan_publish(wsc1, 1);
+    scan_load(nx2, wsc);
+    pos_meta(nx, qp1, wp1, mt_nx);
+    if (w4 == 0 && lane == 0) {
+      *reinterpret_cast<int4*>(meta_s[0]) = make_int4(mt_cur[0], mt_cur[1], mt_cur[2], mt_cur[3]);
+      *reinterpret_cast<int4*>(meta_s[1]) = make_int4(mt_nx[0], mt_nx[1], mt_nx[2], mt_nx[3]);
     }
-    for (int e = tid; e < HG * dv; e += NT)
-      store1<true>(p.out, (row * H + h0) * dv + e, __int_as_float(0x7fc00000));
+    lds_barrier();  // L0: metadata and index rows of items 0 and 1 published
+    int n = 0;
+    int ntl = tiles_of(meta_of(cur, mt_cur[0], mt_cur[1], mt_cur[2], mt_cur[3]),
+                       npool_of(mt_cur, 0));
+    int start = 0, end = padded(ntl);
+    // (the queries land while the first gathers are in flight)
+    q_rotate();
+    cs_publish(0);
+    state_reset();
+    lds_barrier();  // tile 0 landed
+    s_step(std::integral_constant<int, 0>{}, 0, true);
+    lds_barrier();  // B(0)
+
+    // ---- an item's last round, after its last S step (the query registers
+    // are free): publish the index row, list length and metadata of the item
+    // after next (loaded one item ago), load the next item's queries, then the
+    // index row and positions of the item after that (issued after the
+    // queries, so that waiting for the queries never waits for them)
+    auto prefetch = [&]() __attribute__((always_inline)) {
+      scan_publish(wsc, n & 1);
+      pos_meta(nx2, qp2, wp2, mt_nx2);
+      if (w4 == 0 && lane == 0)
+        *reinterpret_cast<int4*>(meta_s[n & 1]) =
+            make_int4(mt_nx2[0], mt_nx2[1], mt_nx2[2], mt_nx2[3]);
+      q_load(nx, mt_nx[0]);
+      const Item n3 = item_at(n + 3);
+      scan_load(n3, wsc);
+      load_pos(n3, qp2, wp2);
+    };
+    // ---- the move to the next item, at the last iteration of an item's
+    // last round (before S of the next item's first tile)
+    bool moved = false;
+    auto advance = [&]() __attribute__((always_inline)) {
+      finish(cur, mt_cur, n & 1);
+      ++n;
+      cur = nx;
+      nx = nx2;
+      nx2 = item_at(n + 2);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) { mt_cur[e] = mt_nx[e]; mt_nx[e] = mt_nx2[e]; }
+      if (cur.row >= 0) {
+        q_rotate();
+        cs_publish(n & 1);
+        state_reset();
+      }
+      // the new item starts here; its tile count is known after the round
+      // (its first tile is always computed)
+      start = end;
+      ntl = 1;
+      moved = true;
+    };
+
+    for (int r = 0;; ++r) {
+      const bool last_round = (r + 1) * NBUF == end;
+      auto iter = [&](auto JC, int j) __attribute__((always_inline)) {
+        constexpr int J = decltype(JC)::value;
+        const int q = j + 1;                // the tile this step computes
+        if constexpr (J == NBUF - 1) {
+          if (last_round) advance();
+        }
+        const int u = q - start;
+        if (cur.row >= 0 && u < ntl)
+          s_step(std::integral_constant<int, (J + 1) % NBUF>{}, q & 1, u == 0);
+        if constexpr (J == NBUF - 2) {
+          if (last_round && nx.row >= 0) prefetch();
+        }
+        lds_barrier();  // B(j+1)
+      };
+      iter(std::integral_constant<int, 0>{}, r * NBUF);
+      iter(std::integral_constant<int, 1>{}, r * NBUF + 1);
+      iter(std::integral_constant<int, 2>{}, r * NBUF + 2);
+      if constexpr (NBUF == 4) iter(std::integral_constant<int, 3>{}, r * NBUF + 3);
+      if (moved) {
+        moved = false;
+        if (cur.row < 0) break;
+        ntl = tiles_of(meta_of(cur, mt_cur[0], mt_cur[1], mt_cur[2], mt_cur[3]),
+                       npool_of(mt_cur, n & 1));
+        end = start + padded(ntl);
+      }
+    }
     return;
   }
 
-  // ---- effective key list: visible window rows, then the pool slots, each
-  // part padded to whole tiles so that a tile reads one tensor
-  int n_win = 0, r_lo = 0;
-  if (p.window > 0 && p.kv_win != nullptr) {
-    const long wp0 = p.win_pos0[b];
-    const long lo = max(t - p.window + 1, max(0L, wp0));
-    const long hi = min(t, wp0 + (long)p.L_win - 1);
-    if (hi >= lo) { n_win = (int)(hi - lo + 1); r_lo = (int)(lo - wp0); }
-  }
-  const int WT = (n_win + kNK - 1) / kNK;
-  const int tile0 = split * args.tiles_per_split;
-
-  const u16* win_base = p.kv_win ? reinterpret_cast<const u16*>(p.kv_win) + (size_t)b * p.L_win * D
-                                 : nullptr;
-  const u16* pool_base = p.pool ? reinterpret_cast<const u16*>(p.pool) + (size_t)b * p.T * D
-                                : nullptr;
-  // gather descriptors are built per tile from these (a zero size past the
-  // tile range: the loads then fill zeros)
-  const int win_bytes = win_base ? p.L_win * D * 2 : 0;
-  const int pool_bytes = pool_base ? p.T * D * 2 : 0;
+  // ======================================================================
+  // PV waves
+  // ======================================================================
   // gather source offset of lane l for tile row 8w + q: logical chunk
   // l ^ f(8w + q) (loop-invariant registers)
   int lane_off[RPW];
 #pragma unroll
   for (int q = 0; q < RPW; ++q) lane_off[q] = (lane ^ swz(RPW * w4 + q)) << 4;
+  const int win_bytes = p.kv_win ? p.L_win * D * 2 : 0;
+  const int pool_bytes = p.pool ? p.T * D * 2 : 0;
 
-  // Row ids of a tile's rows 8w .. 8w+7 (w = the wave's index in its role):
-  // kv_win / pool row of this sequence, -1 = empty (or past the tile range).
-  // The pool index entries come in with ONE vector load per tile (lane l:
-  // entry of row 8w + l % 8), through a bounded descriptor, so that a window
-  // tile or a tile past the range reads nothing; vector loads keep the scalar
-  // data counter free for LDS waits, and retire in order with the gathers.
-  const __amdgpu_buffer_rsrc_t idx_rs = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<int*>(p.idx ? p.idx + row * p.k : p.q_pos), 0, p.idx ? p.k * 4 : 0,
-      0x00020000);
-  auto rid_load = [=](int tile) __attribute__((always_inline)) -> int {
-    const int jj = (tile - WT) * kNK + w4 * RPW + (lane & 7);  // < 0 for window tiles
-    const int off = jj * 4;  // a negative offset is out of range: reads 0
-    return (int)__builtin_amdgcn_raw_buffer_load_b32(idx_rs, off, 0, 0);
+  // Row id of row 8w + lane % 8 of a tile (w = the wave's index in its role):
+  // kv_win / pool row of the item's sequence, -1 = empty (or past the item's
+  // range); pool entries come from the item's index row, which the S waves
+  // put in LDS (slot = item parity) one item ahead.
+  auto rid_of = [&](const Meta& m, int tile, int slot) __attribute__((always_inline)) -> int {
+    if (m.bad || tile >= m.tlim) return -1;
+    if (tile < m.WT) {
+      const int jj = tile * kNK + w4 * RPW + (lane & 7);
+      return jj < m.n_win ? m.r_lo + jj : -1;
+    }
+    const int jj = (tile - m.WT) * kNK + w4 * RPW + (lane & 7);
+    const int w = p.dense ? jj : idx_s[slot][min(jj, kMaxK - 1)];
+    return (jj < m.bound && w >= 0 && w < p.T) ? w : -1;
   };
+
   // This wave's share of a tile's gather into buffer J: rows 8w .. 8w+7, one
   // 1 KiB load per row (and one 8-lane load of the last 128 bytes when D =
   // 576).  An empty slot gathers a stand-in row, the first non-empty one of
   // the 8 (finite data that the -inf bias of the slot cancels: its
-  // probability is exactly 0); when all 8 are empty (or the tile is past the
-  // range) the loads go through a zero-size descriptor (zero fill).
-  // The row is wave-uniform: its offset goes in the scalar operand, so the
-  // per-lane operands are the loop-invariant lane_off[q] (the compiler's
-  // wait-count model treats a register that fed a gather as pending until the
-  // gather lands, so a per-gather temporary reused later for other data would
-  // cost a wait).
-  auto issue = [=](auto JC, int tile, int rid) __attribute__((always_inline)) {
+  // probability is exactly 0); when all 8 are empty the loads go through a
+  // zero-size descriptor (zero fill).  The row is wave-uniform: its offset
+  // goes in the scalar operand, so the per-lane operands are the
+  // loop-invariant lane_off[q] (the compiler's wait-count model treats a
+  // register that fed a gather as pending until the gather lands, so a
+  // per-gather temporary reused later for other data would cost a wait).
+  auto issue = [&](auto JC, const Meta& m, int tile, int rid) __attribute__((always_inline)) {
     constexpr int J = decltype(JC)::value;
     unsigned char* kbuf = kbuf_of(JC);
     if (lane < RPW) bias_s[J * kNK + w4 * RPW + lane] = rid >= 0 ? 0.f : -INFINITY;
     const uint64_t live = __ballot(lane < RPW && rid >= 0);
-    const bool win = tile < WT;
+    const bool win = tile < m.WT;
+    const u16* base = win ? reinterpret_cast<const u16*>(p.kv_win) + (size_t)m.b * p.L_win * D
+                          : reinterpret_cast<const u16*>(p.pool) + (size_t)m.b * p.T * D;
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<u16*>(win ? win_base : pool_base), 0,
-        live == 0ull ? 0 : win ? win_bytes : pool_bytes, 0x00020000);
+        const_cast<u16*>(base), 0, live == 0ull ? 0 : win ? win_bytes : pool_bytes,
+        0x00020000);
     const int stand_in =
         live == 0ull ? 0 : __builtin_amdgcn_readlane(rid, (int)__builtin_ctzll(live));
 #pragma unroll
@@ -381,176 +769,6 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(MfmaArgs args) {
     }
   };
 
-  // PV waves: the first NBUF-1 gathers and the index entries of the first
-  // NBUF tiles (issued whether or not the tiles exist, as in the loop, so that
-  // the wait counts are the same on every path).  When those gathers are all
-  // window tiles inside this split's range they need neither the index row
-  // nor the list length, so they go out first, before the length is known
-  // (the waits hold for either order).
-  const bool win_first = tile0 + NBUF - 2 < WT && NBUF - 2 < args.tiles_per_split;
-  auto win_rid = [=](int tile) __attribute__((always_inline)) -> int {
-    const int jj = tile * kNK + w4 * RPW + (lane & 7);
-    return jj < n_win ? r_lo + jj : -1;
-  };
-  auto win_issue = [&]() __attribute__((always_inline)) {
-    issue(std::integral_constant<int, 0>{}, tile0, win_rid(tile0));
-    issue(std::integral_constant<int, 1>{}, tile0 + 1, win_rid(tile0 + 1));
-    if constexpr (NBUF == 4) issue(std::integral_constant<int, 2>{}, tile0 + 2, win_rid(tile0 + 2));
-  };
-
-  // ---- length of the key list: every ready entry (dense), else up to the
-  // last non-empty slot of the index row, found by the S waves and passed on
-  // through LDS (both roles call this after their first loads)
-  const bool scan = !p.dense && p.k > 0 && p.pool;
-  int npool = 0, tile1 = 0;
-  auto list_length = [&]() __attribute__((always_inline)) {
-    if (p.dense) {
-      npool = p.pool ? ready_count(t, p.m, p.T) : 0;
-    } else if (scan) {
-      lds_barrier();
-#pragma unroll
-      for (int q = 0; q < NS; ++q) npool = max(npool, flags[q] + 1);
-      // (read back from LDS: made wave-uniform explicitly so that it stays in
-      // a scalar register)
-      npool = __builtin_amdgcn_readfirstlane(npool);
-    }
-    tile1 = min(WT + (npool + kNK - 1) / kNK, tile0 + args.tiles_per_split);
-  };
-
-  // row id of row 8w + lane % 8 of a tile, from its loaded index entry
-  auto rid_of = [&](int tile, int raw) __attribute__((always_inline)) -> int {
-    if (tile >= tile1) return -1;
-    if (tile < WT) return win_rid(tile);
-    const int jj = (tile - WT) * kNK + w4 * RPW + (lane & 7);
-    const int w = p.dense ? jj : raw;
-    return (jj < npool && w >= 0 && w < p.T) ? w : -1;
-  };
-
-  int rid_raw_next = 0;
-  auto prologue_issue = [&](bool win_done) __attribute__((always_inline)) {
-    int raw[NBUF];
-    if (win_first) {
-      if (!win_done) win_issue();
-#pragma unroll
-      for (int u = 0; u < NBUF; ++u) raw[u] = rid_load(tile0 + u);
-    } else {
-#pragma unroll
-      for (int u = 0; u < NBUF; ++u) raw[u] = rid_load(tile0 + u);
-      issue(std::integral_constant<int, 0>{}, tile0, rid_of(tile0, raw[0]));
-      issue(std::integral_constant<int, 1>{}, tile0 + 1, rid_of(tile0 + 1, raw[1]));
-      if constexpr (NBUF == 4) issue(std::integral_constant<int, 2>{}, tile0 + 2, rid_of(tile0 + 2, raw[2]));
-    }
-    rid_raw_next = raw[NBUF - 1];
-  };
-
-  // ---- S waves' first loads: the first index entries of the scan (bounded:
-  // nothing is read without an index row), the sink of head hq, then the Q
-  // fragments (B operand of S^T = K Q^T: head hq, dims 32ks + 8g .. +7), so
-  // that the scan waits for its own loads only.  Every S-wave path issues the
-  // same loads, and the PV waves' code joins none of them, so the compiler's
-  // wait counts never merge paths of different load histories.
-  const bool use_sink = p.sink && !split_mode;
-  const __amdgpu_buffer_rsrc_t sink_rs = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<float*>(use_sink ? p.sink : p.cs), 0, use_sink ? H * 4 : 0, 0x00020000);
-  bf16x8 qf[KS];
-  auto s_first_loads = [&]() __attribute__((always_inline)) -> float {
-    constexpr int NSCAN = 8;   // first scan loads per lane: 2048 index slots
-    int w[NSCAN];
-#pragma unroll
-    for (int u = 0; u < NSCAN; ++u)
-      w[u] = (int)__builtin_amdgcn_raw_buffer_load_b32(idx_rs, 4 * (NS * 64 * u + tid), 0, 0);
-    const float sinkv = __builtin_bit_cast(
-        float, (int)__builtin_amdgcn_raw_buffer_load_b32(sink_rs, 4 * (h0 + hq), 0, 0));
-    __builtin_amdgcn_sched_barrier(0);
-    uint4 qraw[KS];
-    const u16* qrow = reinterpret_cast<const u16*>(p.q) + (row * H + h0 + hq) * D;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      qraw[ks] = *reinterpret_cast<const uint4*>(qrow + 32 * ks + 8 * g);
-    __builtin_amdgcn_sched_barrier(0);
-    if (scan) {
-      int last = -1;
-#pragma unroll
-      for (int u = 0; u < NSCAN; ++u) {
-        const int jj = NS * 64 * u + tid;
-        if (jj < p.k && w[u] >= 0 && w[u] < p.T) last = jj;
-      }
-      for (int j = NSCAN * NS * 64 + tid; j < p.k; j += NS * 64) {
-        const int v = (int)__builtin_amdgcn_raw_buffer_load_b32(idx_rs, 4 * j, 0, 0);
-        if (v >= 0 && v < p.T) last = j;
-      }
-#pragma unroll
-      for (int sh = 32; sh > 0; sh >>= 1) last = max(last, __shfl_xor(last, sh, 64));
-      if (lane == 0) flags[w4] = last;
-    }
-    // rotate the rope slice of q at +t, round to bf16
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const int d0 = 32 * ks + 8 * g;
-      uint4 u = qraw[ks];
-      if (32 * ks >= rbase) {
-        float v[8] = {bf_lo(u.x), bf_hi(u.x), bf_lo(u.y), bf_hi(u.y),
-                      bf_lo(u.z), bf_hi(u.z), bf_lo(u.w), bf_hi(u.w)};
-#pragma unroll
-        for (int e = 0; e < 8; e += 2) {
-          const float2 r = cs[t * half + ((d0 + e - rbase) >> 1)];
-          const float a = v[e], bb = v[e + 1];
-          v[e] = a * r.x - bb * r.y;
-          v[e + 1] = a * r.y + bb * r.x;
-        }
-        u.x = pack2(v[0], v[1]); u.y = pack2(v[2], v[3]);
-        u.z = pack2(v[4], v[5]); u.w = pack2(v[6], v[7]);
-      }
-      qf[ks] = as_bf16x8(u);
-    }
-    return sinkv;
-  };
-
-  // ---- softmax state of head hq (replicated over the 4 lane groups), log2
-  // domain (set by the S waves once the sink is in)
-  const float sl2 = p.scale * kLog2e;
-  float sink_l2 = -INFINITY, mref = -INFINITY, lrun = 0.f, mseen = -INFINITY;
-
-  // ---- S phase pieces.  S^T for keys 16kb + c16 (kb = 0, 1) and the 16
-  // heads of this wave, in groups of 4 k-steps; lane supplies K row
-  // 16kb + c16, 16-byte chunk 4ks + g.  Four accumulation chains (key block x
-  // even/odd k-step).
-  constexpr int NG = (KS + 3) / 4;
-  // K row c16 (and 16 + c16, same swizzle), logical chunk 4ks + g: physical
-  // chunk ((4 (ks % 4) + g) ^ f(c16)) + 16 (ks / 4)
-  const int fk = swz(c16);
-  int koff[4];
-#pragma unroll
-  for (int u = 0; u < 4; ++u) koff[u] = c16 * KT::ROWB + 16 * ((4 * u + g) ^ fk);
-  auto k_group = [&](auto JC, int grp, uint4 (&kv)[4][2]) __attribute__((always_inline)) {
-    const unsigned char* kbase = kbuf_of(JC);
-    // tail area: rows c16 and 16 + c16 sit in wave blocks c16/8 and 2 + c16/8
-    const unsigned char* ktail = tbuf_of(JC) + (c16 >> 3) * KT::TBLK + (c16 & 7) * 16 + 128 * g;
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const int ks = 4 * grp + kk;
-      if (ks < KT::MAIN / 32) {
-        const unsigned char* kp = kbase + koff[ks & 3] + 256 * (ks >> 2);
-        kv[kk][0] = *reinterpret_cast<const uint4*>(kp);
-        kv[kk][1] = *reinterpret_cast<const uint4*>(kp + 16 * KT::ROWB);
-      } else if (ks < KS) {
-        const int u = ks - KT::MAIN / 32;   // tail chunk 4u + g
-        kv[kk][0] = *reinterpret_cast<const uint4*>(ktail + 512 * u);
-        kv[kk][1] = *reinterpret_cast<const uint4*>(ktail + 2 * KT::TBLK + 512 * u);
-      }
-    }
-  };
-  auto s_group = [&](int grp, const uint4 (&kv)[4][2], f32x4 (&sa)[4])
-      __attribute__((always_inline)) {
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const int ks = 4 * grp + kk;
-      if (ks < KS) {
-        sa[(kk & 1) * 2 + 0] = mfma16x16x32(as_bf16x8(kv[kk][0]), qf[ks], sa[(kk & 1) * 2 + 0]);
-        sa[(kk & 1) * 2 + 1] = mfma16x16x32(as_bf16x8(kv[kk][1]), qf[ks], sa[(kk & 1) * 2 + 1]);
-      }
-    }
-  };
   // V: column block nb, keys 4g + e (first read) and 16 + 4g + e (second):
   // lane (g, s) of a 16-lane block reads row 4g + s/4, columns 4(s%4) ..
   typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -568,136 +786,26 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(MfmaArgs args) {
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
   };
 
-  // ---- softmax of a tile (buffer J) from its logits: P to P buffer par (key
-  // position 8g + e <-> key 16(e/4) + 4g + (e%4)).  On the first tile of the
-  // range the reference max is set (the accumulators are still zero, only the
-  // running sum is rescaled); afterwards a tile far above it requests a
-  // restart.
-  auto bias_of = [&](auto JC, int kb) __attribute__((always_inline)) -> f32x4 {
-    return *reinterpret_cast<const f32x4*>(bias_s + decltype(JC)::value * kNK + 16 * kb + 4 * g);
-  };
-  auto softmax = [&](int par, const f32x4 x0, const f32x4 x1, bool first)
-      __attribute__((always_inline)) {
-    // raw logits; the scale (> 0) commutes with the max and goes into the
-    // exponent's fused multiply-add
-    const float m0 = fmaxf(fmaxf(x0[0], x0[1]), fmaxf(x0[2], x0[3]));
-    const float m1 = fmaxf(fmaxf(x1[0], x1[1]), fmaxf(x1[2], x1[3]));
-    const float tmax = xgroup_max(fmaxf(m0, m1)) * sl2;
-    mseen = fmaxf(mseen, tmax);
-    float alpha = 1.f;
-    if (first) {
-      const float mnew = fmaxf(mref, tmax);
-      if (mnew != mref) alpha = __builtin_amdgcn_exp2f(mref - mnew);
-      mref = mnew;
-    } else {
-      // every lane writes the wave's verdict (no branch: this chain is
-      // interleaved with matrix instructions)
-      rflag_s[par * NS + w4] = __ballot(tmax > mref + kRestart) != 0ull ? 1 : 0;
-    }
-    const float mbase = (mref == -INFINITY) ? 0.f : mref;
-    float pv[8];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      pv[r] = __builtin_amdgcn_exp2f(fmaf(x0[r], sl2, -mbase));
-      pv[4 + r] = __builtin_amdgcn_exp2f(fmaf(x1[r], sl2, -mbase));
-    }
-    const float ps = ((pv[0] + pv[1]) + (pv[2] + pv[3])) + ((pv[4] + pv[5]) + (pv[6] + pv[7]));
-    lrun = lrun * alpha + xgroup_sum(ps);
-    *reinterpret_cast<uint4*>(Ps + (par * HG + hq) * kPS + 8 * g) =
-        make_uint4(pack2(pv[0], pv[1]), pack2(pv[2], pv[3]), pack2(pv[4], pv[5]),
-                   pack2(pv[6], pv[7]));
-  };
-
-  // ---- S-wave step: S + softmax of the tile in buffer JN (P buffer par),
-  // the K groups read one group ahead of their products
-  auto s_step = [&](auto JN, int par, bool first) __attribute__((always_inline)) {
-    uint4 kv[2][4][2];
-    k_group(JN, 0, kv[0]);
-    const f32x4 bias0 = bias_of(JN, 0), bias1 = bias_of(JN, 1);
-    f32x4 sa[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) sa[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int grp = 0; grp < NG; ++grp) {
-      __builtin_amdgcn_sched_barrier(0);
-      if (grp + 1 < NG) k_group(JN, grp + 1, kv[(grp + 1) & 1]);
-      s_group(grp, kv[grp & 1], sa);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    softmax(par, sa[0] + sa[2] + bias0, sa[1] + sa[3] + bias1, first);
-  };
-  if (tid < 2 * NS) rflag_s[tid] = 0;
-  // restart requests for tile j+1 (written by the S waves in step j)
-  auto again_of = [&](int par) __attribute__((always_inline)) -> bool {
-    const int4 rf = *reinterpret_cast<const int4*>(rflag_s + (par ^ 1) * NS);
-    return __builtin_amdgcn_readfirstlane(rf.x | rf.y | rf.z | rf.w) != 0;
-  };
-  // Both roles run the same barriers: two in the prologue, one per iteration
-  // (whole rounds of NBUF iterations), one per restart and one before the
-  // output.  Between barriers B(j) and B(j+1) the S waves run S + softmax of
-  // tile j+1 while the PV waves run PV of tile j and gather tile j+NBUF-1
-  // (into the buffer of tile j-1).  The PV waves alone touch global memory in
-  // the loop, so they alone wait for it: before B(j+1) their loads of tile
-  // j+2 must have landed.  Their vector memory operations per iteration, in
-  // order: the index load of tile j+NBUF, the G gathers of tile j+NBUF-1.
-  if (s_role) {
-    const float sinkv = s_first_loads();
-    list_length();
-    if (use_sink) sink_l2 = sinkv * kLog2e;
-    mref = sink_l2;
-    lrun = use_sink ? 1.f : 0.f;
-    for (;;) {
-      // ---- prologue: S + softmax of the first tile
-      lds_barrier();  // tile0 landed
-      s_step(std::integral_constant<int, 0>{}, 0, true);
-      lds_barrier();  // B(tile0)
-      bool again = false;
-      auto iter = [&](auto JC, int j) __attribute__((always_inline)) {
-        constexpr int J = decltype(JC)::value;
-        const int par = (j - tile0) & 1;
-        if (j + 1 < tile1 && !again)
-          s_step(std::integral_constant<int, (J + 1) % NBUF>{}, par ^ 1, false);
-        lds_barrier();  // B(j+1)
-        again = again_of(par);
-      };
-      for (int tile = tile0; tile < tile1 && !again; tile += NBUF) {
-        iter(std::integral_constant<int, 0>{}, tile);
-        iter(std::integral_constant<int, 1>{}, tile + 1);
-        iter(std::integral_constant<int, 2>{}, tile + 2);
-        if constexpr (NBUF == 4) iter(std::integral_constant<int, 3>{}, tile + 3);
-      }
-      if (!again) break;
-      // ---- restart with the reference max raised to the largest one seen
-      lds_barrier();
-      mref = mseen;
-      lrun = use_sink ? __builtin_amdgcn_exp2f(sink_l2 - mref) : 0.f;
-      if (tid < 2 * NS) rflag_s[tid] = 0;
-    }
-    // ---- running max and sum of each head, for the PV waves / the merge
-    if (g == 0) {
-      if (split_mode) {
-        float* ml = args.ws + ((size_t)row * args.nsplit + split) * H * 2;
-        ml[2 * (h0 + hq)] = mref;
-        ml[2 * (h0 + hq) + 1] = lrun;
-      } else {
-        fin_s[hq] = lrun > 0.f ? 1.f / lrun : 0.f;
-      }
-    }
-    lds_barrier();
-    return;
-  }
-
-  // ---- PV waves
-  if (win_first) win_issue();
-  list_length();
-  prologue_issue(true);
   f32x4 acc[4][NB];
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // ---- PV-wave step: PV of the tile in buffer J (P buffer par)
+  // ---- PV-wave step: PV of the tile in buffer J (P buffer par), after the
+  // rescale the S waves may have asked for with this P
   auto pv_step = [&](auto JC, int par) __attribute__((always_inline)) {
+    const int4 rf = *reinterpret_cast<const int4*>(rfl_s[par]);
+    if (__builtin_amdgcn_readfirstlane(rf.x | rf.y | rf.z | rf.w) != 0) {
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) {
+        const float4 a = *reinterpret_cast<const float4*>(&alpha_s[par][16 * mb + 4 * g]);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          acc[mb][nb][0] *= a.x; acc[mb][nb][1] *= a.y;
+          acc[mb][nb][2] *= a.z; acc[mb][nb][3] *= a.w;
+        }
+      }
+    }
     bf16x8 pa[4];
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb)
@@ -712,102 +820,145 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(MfmaArgs args) {
       for (int mb = 0; mb < 4; ++mb) acc[mb][nb] = mfma16x16x32(pa[mb], vb[nb], acc[mb][nb]);
   };
 
-  for (;;) {
-    wait_vmcnt<(NBUF - 2) * G>();
-    lds_barrier();  // tile0 landed
-    wait_vmcnt<(NBUF - 3) * G>();
-    lds_barrier();  // B(tile0)
-    bool again = false;
-    auto iter = [&](auto JC, int j) __attribute__((always_inline)) {
-      constexpr int J = decltype(JC)::value;
-      const int par = (j - tile0) & 1;
-      const int raw = rid_load(j + NBUF);
-      issue(std::integral_constant<int, (J + NBUF - 1) % NBUF>{}, j + NBUF - 1,
-            rid_of(j + NBUF - 1, rid_raw_next));
-      rid_raw_next = raw;
-      if (j < tile1 && !again) pv_step(JC, par);
-      // this wave's loads of tile j+2 have landed (NBUF = 4: the index load
-      // of tile j+4 and the gathers of tile j+3 may be in flight)
-      wait_vmcnt<(NBUF - 3) * (G + 1)>();
-      lds_barrier();  // B(j+1)
-      again = again_of(par);
-    };
-    for (int tile = tile0; tile < tile1 && !again; tile += NBUF) {
-      iter(std::integral_constant<int, 0>{}, tile);
-      iter(std::integral_constant<int, 1>{}, tile + 1);
-      iter(std::integral_constant<int, 2>{}, tile + 2);
-      if constexpr (NBUF == 4) iter(std::integral_constant<int, 3>{}, tile + 3);
-    }
-    // no gather may still be writing this workgroup's LDS when it exits or
-    // starts over
-    wait_vmcnt<0>();
-    if (!again) break;
-    lds_barrier();  // restart
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    prologue_issue(false);
-  }
-  lds_barrier();  // the S waves' max and sum are in place
-
-  // ---- output.  Lane (g, c16) holds, for head block mb and column block nb,
-  // O[head 16mb + 4g + j][column cbase + 16nb + c16], j = 0..3.  Stores go out
-  // as column pairs: adjacent lanes trade one value (even lane: row j, columns
-  // c, c+1; odd lane: row j+1, columns c-1, c).
+  // ---- output of an item.  Lane (g, c16) holds, for head block mb and column
+  // block nb, O[head 16mb + 4g + j][column cbase + 16nb + c16], j = 0..3.
+  // Stores go out as column pairs: adjacent lanes trade one value (even lane:
+  // row j, columns c, c+1; odd lane: row j+1, columns c-1, c).
   const bool odd = (c16 & 1) != 0;
   auto partner = [&](float v) __attribute__((always_inline)) -> float {
     return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true));
   };
-  if (split_mode) {
-    float* po = args.ws + (size_t)((long)p.B * p.S) * args.nsplit * H * 2 +
-                ((size_t)row * args.nsplit + split) * H * dv + (size_t)h0 * dv;
+  auto output = [&](const Meta& m, int slot) __attribute__((always_inline)) {
+    if (split_mode) {
+      float* po = args.ws + (size_t)args.rows * args.nsplit * H * 2 +
+                  ((size_t)m.row * args.nsplit + m.split) * H * dv + (size_t)m.h0 * dv;
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
+      for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          const int col = cbase + 16 * nb + c16;
+#pragma unroll
+          for (int j = 0; j < 4; j += 2) {
+            const float v0 = acc[mb][nb][j], v1 = acc[mb][nb][j + 1];
+            const float r = partner(odd ? v0 : v1);
+            const int hr = 16 * mb + 4 * g + j + (odd ? 1 : 0);
+            *reinterpret_cast<float2*>(po + (size_t)hr * dv + col - (odd ? 1 : 0)) =
+                odd ? make_float2(r, v1) : make_float2(v0, r);
+          }
+        }
+      return;
+    }
+    u16* out = reinterpret_cast<u16*>(p.out) + ((long)m.row * H + m.h0) * dv;
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+      const float4 li = *reinterpret_cast<const float4*>(&fin_s[slot][16 * mb + 4 * g]);
+      const float lv[4] = {li.x, li.y, li.z, li.w};
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
         const int col = cbase + 16 * nb + c16;
+        float v[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v[j] = acc[mb][nb][j] * lv[j];
+        if (dv == D && cbase + 16 * nb + 16 > rbase) {
+          // de-rotate the rope slice at -t: pairs (even column, odd column)
+          // sit in adjacent lanes
+          const float2 rr = cs_s[slot][((col & ~1) - rbase) >> 1];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float o = partner(v[j]);
+            v[j] = odd ? (-o * rr.y + v[j] * rr.x) : (v[j] * rr.x + o * rr.y);
+          }
+        }
 #pragma unroll
         for (int j = 0; j < 4; j += 2) {
-          const float v0 = acc[mb][nb][j], v1 = acc[mb][nb][j + 1];
-          const float r = partner(odd ? v0 : v1);
+          const float r = partner(odd ? v[j] : v[j + 1]);
           const int hr = 16 * mb + 4 * g + j + (odd ? 1 : 0);
-          *reinterpret_cast<float2*>(po + (size_t)hr * dv + col - (odd ? 1 : 0)) =
-              odd ? make_float2(r, v1) : make_float2(v0, r);
+          *reinterpret_cast<uint32_t*>(out + hr * dv + col - (odd ? 1 : 0)) =
+              odd ? pack2(r, v[j + 1]) : pack2(v[j], r);
         }
-      }
-    return;
-  }
-  u16* out = reinterpret_cast<u16*>(p.out) + (row * H + h0) * dv;
-#pragma unroll
-  for (int mb = 0; mb < 4; ++mb) {
-    const float4 li = *reinterpret_cast<const float4*>(fin_s + 16 * mb + 4 * g);
-    const float lv[4] = {li.x, li.y, li.z, li.w};
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      const int col = cbase + 16 * nb + c16;
-      float v[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) v[j] = acc[mb][nb][j] * lv[j];
-      if (dv == D && cbase + 16 * nb + 16 > rbase) {
-        // de-rotate the rope slice at -t: pairs (even column, odd column)
-        // sit in adjacent lanes
-        const float2 rr = cs[t * half + (((col & ~1) - rbase) >> 1)];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float o = partner(v[j]);
-          v[j] = odd ? (-o * rr.y + v[j] * rr.x) : (v[j] * rr.x + o * rr.y);
-        }
-      }
-#pragma unroll
-      for (int j = 0; j < 4; j += 2) {
-        const float r = partner(odd ? v[j] : v[j + 1]);
-        const int hr = 16 * mb + 4 * g + j + (odd ? 1 : 0);
-        *reinterpret_cast<uint32_t*>(out + hr * dv + col - (odd ? 1 : 0)) =
-            odd ? pack2(r, v[j + 1]) : pack2(v[j], r);
       }
     }
+  };
+
+  auto meta_read = [&](const Item& it, int slot) __attribute__((always_inline)) -> Meta {
+    const int4 mt = *reinterpret_cast<const int4*>(meta_s[slot]);
+    return meta_of(it, __builtin_amdgcn_readfirstlane(mt.x), __builtin_amdgcn_readfirstlane(mt.y),
+                   __builtin_amdgcn_readfirstlane(mt.z), __builtin_amdgcn_readfirstlane(mt.w));
+  };
+  auto npool_read = [&](const Meta& m, int slot) __attribute__((always_inline)) -> int {
+    if (p.dense) return m.bound;
+    if (!scan) return 0;
+    const int4 s4 = *reinterpret_cast<const int4*>(scan_s[slot]);
+    return __builtin_amdgcn_readfirstlane(max(max(s4.x, s4.y), max(s4.z, s4.w)) + 1);
+  };
+
+  // ---- prologue: the first NBUF-1 gathers (an item has at least NBUF
+  // tiles)
+  Item it_cur = item_at(0);
+  if (it_cur.row < 0) return;
+  lds_barrier();  // L0
+  Meta mc = meta_read(it_cur, 0);
+  Meta mn = meta_read(item_at(1), 1);
+  int n = 0;
+  int ntl = tiles_of(mc, npool_read(mc, 0));
+  int start = 0, end = padded(ntl);
+  issue(std::integral_constant<int, 0>{}, mc, mc.tile0, rid_of(mc, mc.tile0, 0));
+  issue(std::integral_constant<int, 1>{}, mc, mc.tile0 + 1, rid_of(mc, mc.tile0 + 1, 0));
+  if constexpr (NBUF == 4)
+    issue(std::integral_constant<int, 2>{}, mc, mc.tile0 + 2, rid_of(mc, mc.tile0 + 2, 0));
+  wait_vmcnt<(NBUF - 2) * G>();
+  lds_barrier();  // tile 0 landed
+  wait_vmcnt<(NBUF - 3) * G>();
+  lds_barrier();  // B(0)
+
+  for (int r = 0;; ++r) {
+    if (r * NBUF == end) {
+      // item n ended with the previous round: its output (the S waves wrote
+      // its 1/l before the last barrier), then the next item's list length
+      // and the metadata of the one after (published with that barrier)
+      output(mc, n & 1);
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      ++n;
+      mc = mn;
+      if (mc.row < 0) break;
+      mn = meta_read(item_at(n + 1), (n + 1) & 1);
+      start = end;
+      ntl = tiles_of(mc, npool_read(mc, n & 1));
+      end = start + padded(ntl);
+    }
+    // the item of the next round (the gathers run up to a round ahead)
+    const bool ahead_next = (r + 1) * NBUF >= end;
+    const Meta& ma = ahead_next ? mn : mc;
+    const int sa = ahead_next ? end : start;
+    const int slot_a = ahead_next ? (n + 1) & 1 : n & 1;
+    auto iter = [&](auto JC, int j) __attribute__((always_inline)) {
+      constexpr int J = decltype(JC)::value;
+      // gather of position j+NBUF-1 (in this round for J = 0, in the next one
+      // after)
+      if constexpr (J == 0) {
+        const int tile = mc.tile0 + (j + NBUF - 1 - start);
+        issue(std::integral_constant<int, NBUF - 1>{}, mc, tile, rid_of(mc, tile, n & 1));
+      } else {
+        const int tile = ma.tile0 + (j + NBUF - 1 - sa);
+        issue(std::integral_constant<int, (J + NBUF - 1) % NBUF>{}, ma, tile,
+              rid_of(ma, tile, slot_a));
+      }
+      if (j - start < ntl) pv_step(JC, j & 1);
+      // this wave's gathers of position j+2 have landed (NBUF = 4: those of
+      // j+3 may be in flight)
+      wait_vmcnt<(NBUF - 3) * G>();
+      lds_barrier();  // B(j+1)
+    };
+    iter(std::integral_constant<int, 0>{}, r * NBUF);
+    iter(std::integral_constant<int, 1>{}, r * NBUF + 1);
+    iter(std::integral_constant<int, 2>{}, r * NBUF + 2);
+    if constexpr (NBUF == 4) iter(std::integral_constant<int, 3>{}, r * NBUF + 3);
   }
+  // no gather may still be writing this workgroup's LDS when it exits
+  wait_vmcnt<0>();
 }
 
 // Merge split partials: M = max(z, m_s), L = e^(z-M) + sum e^(m_s-M) l_s,
@@ -871,8 +1022,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnParams p, const f
 // D = 512 (CSA / HCA) or 576 (DSA: 512 latent + 64 rope), dv = 512, rope 64.
 
 bool mfma_shape(int H, int D, int dv, int rope_dim, int k) {
-  (void)k;
-  return H % 64 == 0 && dv == 512 && rope_dim == 64 && (D == 512 || D == 576);
+  return H % 64 == 0 && dv == 512 && rope_dim == 64 && (D == 512 || D == 576) && k <= kMaxK;
 }
 
 
@@ -895,15 +1045,18 @@ int device_cus() {
 
 }  // namespace
 
-AttnPlan plan_attention(int B, int S, int H, int D, int dv, int rope_dim, int max_slots,
-                        bool bf16, long max_rows, int k) {
+AttnPlan plan_attention(int B, int S, int H, int D, int dv, int rope_dim, int window,
+                        int npool_max, bool bf16, long max_rows, int k) {
   AttnPlan pl{0, 1, 1 << 30, 0};
   if (!bf16 || !mfma_shape(H, D, dv, rope_dim, k)) return pl;
   // the gather addresses one sequence's rows with 32-bit buffer offsets
   if (max_rows * D * 2 >= 0x7ffffff0L) return pl;
+  const long rows = (long)B * S;
+  const int tiles = (window + kNK - 1) / kNK + (npool_max + kNK - 1) / kNK;
+  // work items are counted in 32-bit arithmetic
+  if ((rows + 7) / 8 * 8 * (H / 64) * (long)std::max(tiles, 1) >= 0x7fffffffL) return pl;
   pl.kernel = 1;
-  const long wgs = (long)B * S * (H / 64);
-  const int tiles = (max_slots + kNK - 1) / kNK;
+  const long wgs = rows * (H / 64);
   const int cus = device_cus();
   if (wgs < cus && tiles > 1) {
     int ns = (int)std::min<long>(tiles, (cus + wgs - 1) / wgs);
@@ -942,12 +1095,16 @@ hipError_t launch_attention(const AttnParams& p, const AttnPlan& plan, void* ws,
   a.ws = split ? reinterpret_cast<float*>(ws) : nullptr;
   a.nsplit = split ? plan.nsplit : 1;
   a.tiles_per_split = split ? plan.tiles_per_split : (1 << 30);
-  a.rows_per_xcd = (int)((rows + 7) / 8);
-  dim3 grid((unsigned)(8 * (long)a.rows_per_xcd), a.nsplit, p.H / 64);
+  a.nhg = p.H / 64;
+  a.rows = (int)rows;
+  a.n_items = (rows + 7) / 8 * 8 * a.nsplit * a.nhg;
+  // persistent: one workgroup per compute unit (the LDS use allows no more),
+  // a multiple of 8 so that a workgroup's items keep one residue mod 8
+  const long grid = (std::min<long>(device_cus(), a.n_items) + 7) / 8 * 8;
   if (p.D == 512)
-    hipLaunchKernelGGL((attn_mfma_kernel<512, 4>), grid, dim3(512), 0, s, a);
+    hipLaunchKernelGGL((attn_mfma_kernel<512, 4>), dim3((unsigned)grid), dim3(512), 0, s, a);
   else
-    hipLaunchKernelGGL((attn_mfma_kernel<576, 3>), grid, dim3(512), 0, s, a);
+    hipLaunchKernelGGL((attn_mfma_kernel<576, 3>), dim3((unsigned)grid), dim3(512), 0, s, a);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || !split) return err;
   const int per_wg = 256 / (p.dv / 8);

@@ -105,10 +105,10 @@ csa::AttnParams make_params(const void* q, const void* kv_win, const int32_t* wi
   return p;
 }
 
-csa_status_t run_attn(const char* fn, const csa::AttnParams& p, int max_slots,
+csa_status_t run_attn(const char* fn, const csa::AttnParams& p, int npool_max,
                       void* workspace, size_t ws_bytes, hipStream_t s) {
-  csa::AttnPlan plan = csa::plan_attention(p.B, p.S, p.H, p.D, p.dv, p.rope_dim, max_slots,
-                                           p.bf16, std::max<long>(p.L_win, p.T),
+  csa::AttnPlan plan = csa::plan_attention(p.B, p.S, p.H, p.D, p.dv, p.rope_dim, p.window,
+                                           npool_max, p.bf16, std::max<long>(p.L_win, p.T),
                                            p.dense ? 0 : p.k);
   void* ws = nullptr;
   if (plan.nsplit > 1) {
@@ -210,14 +210,14 @@ size_t csa_sparse_attn_workspace_size(int32_t B, int32_t S, int32_t H, int32_t D
                                       int32_t rope_dim, int32_t k, int32_t window,
                                       int32_t dtype) {
   if (B < 0 || S < 0 || H < 1 || D < 1 || dv < 1 || k < 0 || window < 0) return 0;
-  return csa::plan_attention(B, S, H, D, dv, rope_dim, window + k, dtype == CSA_BF16, 0, k)
+  return csa::plan_attention(B, S, H, D, dv, rope_dim, window, k, dtype == CSA_BF16, 0, k)
       .ws_bytes;
 }
 
 size_t hca_attn_workspace_size(int32_t B, int32_t S, int32_t H, int32_t D, int32_t dv,
                                int32_t rope_dim, int32_t T, int32_t window, int32_t dtype) {
   if (B < 0 || S < 0 || H < 1 || D < 1 || dv < 1 || T < 0 || window < 0) return 0;
-  return csa::plan_attention(B, S, H, D, dv, rope_dim, window + T, dtype == CSA_BF16, T, 0)
+  return csa::plan_attention(B, S, H, D, dv, rope_dim, window, T, dtype == CSA_BF16, T, 0)
       .ws_bytes;
 }
 
@@ -243,7 +243,7 @@ csa_status_t csa_sparse_attn(const void* q, const void* kv_win, const int32_t* w
     p.k = 0;
     p.dense = 0;
   }
-  return run_attn(fn, p, p.window + p.k, workspace, ws_bytes, as_stream(stream));
+  return run_attn(fn, p, p.k, workspace, ws_bytes, as_stream(stream));
 }
 
 csa_status_t hca_attn(const void* q, const void* kv_win, const int32_t* win_pos0,
@@ -261,7 +261,7 @@ csa_status_t hca_attn(const void* q, const void* kv_win, const int32_t* win_pos0
   csa::AttnParams p = make_params(q, kv_win, win_pos0, L_win, pool, T, nullptr, 0, m, sink,
                                   out, q_pos, B, S, H, D, dv, rope_dim, cs, n_pos, window,
                                   scale, dtype);
-  return run_attn(fn, p, p.window + T, workspace, ws_bytes, as_stream(stream));
+  return run_attn(fn, p, T, workspace, ws_bytes, as_stream(stream));
 }
 
 }  // extern "C"

@@ -183,10 +183,11 @@ struct AttnPlan {
   size_t ws_bytes;        // workspace the split needs
 };
 
-// max_rows: the larger of L_win and T (rows of one sequence a gather
-// addresses); k: index slots per query (0 in dense mode)
-AttnPlan plan_attention(int B, int S, int H, int D, int dv, int rope_dim, int max_slots,
-                        bool bf16, long max_rows, int k);
+// window: window slots per query; npool_max: pool slots per query (k, or T in
+// dense mode); max_rows: the larger of L_win and T (rows of one sequence a
+// gather addresses); k: index slots per query (0 in dense mode)
+AttnPlan plan_attention(int B, int S, int H, int D, int dv, int rope_dim, int window,
+                        int npool_max, bool bf16, long max_rows, int k);
 hipError_t launch_attention(const AttnParams& p, const AttnPlan& plan, void* ws,
                             hipStream_t s);
 
