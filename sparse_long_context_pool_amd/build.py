@@ -52,8 +52,23 @@ def build(resource_usage: bool = False) -> str:
     tmp = LIB + ".tmp"
     subprocess.run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs],
                    check=True)
+    _check_stubs(tmp)
     os.replace(tmp, LIB)
     return LIB
+
+
+def _check_stubs(lib: str) -> None:
+    """Fail the build when a kernel's host launch stub is referenced but not
+    defined: hipcc's host pass can drop the stub of a kernel template without
+    a diagnostic, and the library would then fail to load."""
+    r = subprocess.run(["nm", "-u", lib], capture_output=True, text=True)
+    if r.returncode != 0:
+        return  # no nm: nothing to check with
+    missing = [ln.split()[-1] for ln in r.stdout.splitlines() if "__device_stub__" in ln]
+    if missing:
+        os.remove(lib)
+        raise RuntimeError("kernel launch stubs missing from the host objects: "
+                           + ", ".join(missing))
 
 
 if __name__ == "__main__":
