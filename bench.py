@@ -330,7 +330,7 @@ DOMINANT = {                # stage -> kernels that make it (name prefixes)
                   "csa::(anonymous namespace)::attn_combine_kernel",
                   "csa::(anonymous namespace)::attn_generic_kernel"),
     "index_scores": ("csa::(anonymous namespace)::index_scores",),
-    "topk": ("csa::(anonymous namespace)::topk_kernel",),
+    "topk": ("csa::(anonymous namespace)::topk_",),
 }
 
 
