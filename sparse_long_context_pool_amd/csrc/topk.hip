@@ -191,9 +191,11 @@ __global__ __launch_bounds__(kTopkThreads) void topk_reg(
     const uint32_t dmask = pass == 2 ? 1023u : 2047u;
     uint32_t* h = hist[buf];
     __syncthreads();  // h cleared, meta of the last pass read
+    // (entries past R, key 0, are skipped: they would all hit one bin of the
+    // first pass and serialise its atomics)
 #pragma unroll
     for (int j = 0; j < KPT; ++j)
-      if ((key[j] & pmask) == prefix) atomicAdd(&h[(key[j] >> shift) & dmask], 1u);
+      if (key[j] != 0u && (key[j] & pmask) == prefix) atomicAdd(&h[(key[j] >> shift) & dmask], 1u);
     // clear the other copy for the next pass meanwhile
     for (int j = tid; j < 2048; j += kTopkThreads) hist[buf ^ 1][j] = 0u;
     __syncthreads();
@@ -232,15 +234,25 @@ __global__ __launch_bounds__(kTopkThreads) void topk_reg(
   // copies of K, in index order
   const uint32_t K = prefix;
   const uint64_t lt = lanemask_lt(lane);
+  // slices in groups of GS: the ballots of a group are in flight together
+  // (all 2 KPT of them would not fit the scalar registers)
+  constexpr int GS = KPT < 8 ? KPT : 8;
 #pragma unroll
-  for (int j = 0; j < KPT; ++j) {
-    const uint64_t mg = __ballot(key[j] > K);
-    const uint64_t me = __ballot(key[j] == K);
-    if (lane == 0) {
-      gtot[j * NW + wave] = __popcll(mg);
-      etot[j * NW + wave] = __popcll(me);
+  for (int j0 = 0; j0 < KPT; j0 += GS) {
+    uint64_t mg[GS], me[GS];
+#pragma unroll
+    for (int u = 0; u < GS; ++u) {
+      mg[u] = __ballot(key[j0 + u] > K);
+      me[u] = __ballot(key[j0 + u] == K);
     }
-    __builtin_amdgcn_sched_barrier(0);  // one slice at a time (scalar registers)
+    if (lane == 0) {
+#pragma unroll
+      for (int u = 0; u < GS; ++u) {
+        gtot[(j0 + u) * NW + wave] = __popcll(mg[u]);
+        etot[(j0 + u) * NW + wave] = __popcll(me[u]);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
   }
   __syncthreads();
   // exclusive prefix over (slice, wave) in index order, by wave 0
@@ -261,18 +273,27 @@ __global__ __launch_bounds__(kTopkThreads) void topk_reg(
     }
   }
   __syncthreads();
-  // the ballots are recomputed rather than kept (64 of them would not fit the
-  // scalar registers): opaque keys stop the compiler from reusing the first
-  // ones
+  // the ballots are recomputed rather than kept: opaque keys stop the
+  // compiler from reusing the first ones
 #pragma unroll
   for (int j = 0; j < KPT; ++j) asm volatile("" : "+v"(key[j]));
 #pragma unroll
-  for (int j = 0; j < KPT; ++j) {
-    const bool gt = key[j] > K, eq = key[j] == K;
-    const uint64_t mg = __ballot(gt), me = __ballot(eq);
-    const int gb = gtot[j * NW + wave] + __popcll(mg & lt);
-    const int eb = etot[j * NW + wave] + __popcll(me & lt);
-    if (gt || (eq && eb < kk)) out[gb + min(eb, kk)] = j * kTopkThreads + tid;
+  for (int j0 = 0; j0 < KPT; j0 += GS) {
+    int gb0[GS], eb0[GS];
+#pragma unroll
+    for (int u = 0; u < GS; ++u) {
+      gb0[u] = gtot[(j0 + u) * NW + wave];
+      eb0[u] = etot[(j0 + u) * NW + wave];
+    }
+#pragma unroll
+    for (int u = 0; u < GS; ++u) {
+      const int j = j0 + u;
+      const bool gt = key[j] > K, eq = key[j] == K;
+      const uint64_t mg = __ballot(gt), me = __ballot(eq);
+      const int gb = gb0[u] + __popcll(mg & lt);
+      const int eb = eb0[u] + __popcll(me & lt);
+      if (gt || (eq && eb < kk)) out[gb + min(eb, kk)] = j * kTopkThreads + tid;
+    }
     __builtin_amdgcn_sched_barrier(0);
   }
 }
