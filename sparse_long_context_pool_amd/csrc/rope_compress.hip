@@ -142,6 +142,38 @@ __global__ __launch_bounds__(256) void compress_kernel(
   }
 }
 
+// m = 1 without overlap, gate or slot bias: the window of an entry is its own
+// token, whose softmax weight is exactly 1, so the entry is the token with
+// its rope slice rotated at pos0 + w.  One thread per 8-channel chunk: a
+// plain streaming pass instead of one workgroup per entry.
+template <bool BF16>
+__global__ __launch_bounds__(256) void rope_copy_kernel(
+    const void* __restrict__ x, void* __restrict__ pool, long rows, int S, int D,
+    int rope_dim, const float2* __restrict__ cs, int pos0) {
+  const int nchunk = D >> 3;
+  const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= rows * nchunk) return;
+  const long r = i / nchunk;
+  const int ch = (int)(i - r * nchunk);
+  const int w = (int)(r % S);
+  float v[8];
+  load8<BF16>(x, r * D + ch * 8, v);
+  const int rope_base = D - rope_dim;
+  if (ch * 8 + 8 > rope_base) {
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+      const int c = ch * 8 + e;
+      if (c >= rope_base) {
+        const float2 rr = cs[((long)pos0 + w) * (rope_dim >> 1) + ((c - rope_base) >> 1)];
+        const float a0 = v[e], a1 = v[e + 1];
+        v[e] = a0 * rr.x - a1 * rr.y;
+        v[e + 1] = a0 * rr.y + a1 * rr.x;
+      }
+    }
+  }
+  store8<BF16>(pool, r * D + ch * 8, v);
+}
+
 }  // namespace
 
 hipError_t launch_rope_table(float* cs, int n_pos, int rope_dim, double theta,
@@ -160,6 +192,17 @@ hipError_t launch_compress(const void* x, const void* gate, const float* slot_bi
                            hipStream_t s) {
   const int T = S / m;
   if (T == 0 || B == 0) return hipSuccess;
+  if (m == 1 && overlap == 0 && gate == nullptr && slot_bias == nullptr && D % 8 == 0) {
+    const long rows = (long)B * S;
+    const long blocks = (rows * (D / 8) + 255) / 256;
+    if (bf16)
+      hipLaunchKernelGGL(rope_copy_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, s, x,
+                         pool, rows, S, D, rope_dim, reinterpret_cast<const float2*>(cs), pos0);
+    else
+      hipLaunchKernelGGL(rope_copy_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, s, x,
+                         pool, rows, S, D, rope_dim, reinterpret_cast<const float2*>(cs), pos0);
+    return hipGetLastError();
+  }
   const size_t lds = (size_t)kCompressWaves * 3 * D * sizeof(float);
   dim3 grid(T, B);
   if (bf16)

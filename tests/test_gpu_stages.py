@@ -44,7 +44,8 @@ def test_rope_table(ops, theta, rope_dim):
 @pytest.mark.parametrize("bf16", [False, True])
 @pytest.mark.parametrize("m,ov,D,rope,gate,bias", [
     (4, 1, 512, 64, True, False), (4, 1, 64, 16, True, True), (128, 0, 512, 64, True, False),
-    (1, 0, 576, 64, False, False), (1, 0, 128, 0, False, False), (8, 0, 96, 32, False, True),
+    (1, 0, 576, 64, False, False), (1, 0, 128, 0, False, False), (1, 0, 64, 16, True, False),
+    (8, 0, 96, 32, False, True),
     (4, 1, 128, 0, True, False)])
 def test_compress(ops, bf16, m, ov, D, rope, gate, bias):
     B = 2
