@@ -142,6 +142,78 @@ __global__ __launch_bounds__(256) void compress_kernel(
   }
 }
 
+// Short windows (at most 32 rows): one wave per entry, 4 entries per
+// workgroup; lane l owns channel chunks l and l + 64 and runs the per-channel
+// online softmax over the whole window, so no merge is needed.
+template <bool BF16>
+__global__ __launch_bounds__(256) void compress_wave_kernel(
+    const void* __restrict__ x, const void* __restrict__ gate,
+    const float* __restrict__ slot_bias, void* __restrict__ pool, int B, int S, int D, int m,
+    int overlap, int rope_dim, const float2* __restrict__ cs, int pos0) {
+  const int T = S / m;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const long e = (long)blockIdx.x * 4 + wave;   // entry over all sequences
+  if (e >= (long)B * T) return;
+  const int b = (int)(e / T), w = (int)(e - (long)b * T);
+  const int nchunk = D >> 3;
+  const long first = (long)(w - overlap) * m;  // token held by slot 0
+  const long j0 = first < 0 ? 0 : first;
+  const long j1 = (long)(w + 1) * m;
+  const long row0 = (long)b * S;
+  const int rope_base = D - rope_dim;
+#pragma unroll
+  for (int cc = 0; cc < kMaxChunksPerLane; ++cc) {
+    const int ch = lane + 64 * cc;
+    if (ch >= nchunk) break;
+    float mx[8], sm[8], ac[8];
+#pragma unroll
+    for (int v = 0; v < 8; ++v) { mx[v] = -INFINITY; sm[v] = 0.f; ac[v] = 0.f; }
+    for (long j = j0; j < j1; ++j) {
+      float xv[8], a[8];
+      load8<BF16>(x, (row0 + j) * D + ch * 8, xv);
+      if (gate) {
+        load8<BF16>(gate, (row0 + j) * D + ch * 8, a);
+      } else {
+#pragma unroll
+        for (int v = 0; v < 8; ++v) a[v] = 0.f;
+      }
+      if (slot_bias) {
+        const float4* sb = reinterpret_cast<const float4*>(slot_bias + (j - first) * D + ch * 8);
+        float4 s0 = sb[0], s1 = sb[1];
+        a[0] += s0.x; a[1] += s0.y; a[2] += s0.z; a[3] += s0.w;
+        a[4] += s1.x; a[5] += s1.y; a[6] += s1.z; a[7] += s1.w;
+      }
+#pragma unroll
+      for (int v = 0; v < 8; ++v) {
+        if (a[v] > mx[v]) {
+          const float r = __expf(mx[v] - a[v]);
+          sm[v] = sm[v] * r + 1.f;
+          ac[v] = ac[v] * r + xv[v];
+          mx[v] = a[v];
+        } else {
+          const float ev = __expf(a[v] - mx[v]);
+          sm[v] += ev;
+          ac[v] += ev * xv[v];
+        }
+      }
+    }
+    float val[8];
+#pragma unroll
+    for (int v = 0; v < 8; ++v) val[v] = ac[v] / sm[v];
+#pragma unroll
+    for (int v = 0; v < 8; v += 2) {
+      const int c = ch * 8 + v;
+      if (c >= rope_base) {
+        const float2 r = cs[((long)pos0 + (long)w * m) * (rope_dim >> 1) + ((c - rope_base) >> 1)];
+        const float a0 = val[v], a1 = val[v + 1];
+        val[v] = a0 * r.x - a1 * r.y;
+        val[v + 1] = a0 * r.y + a1 * r.x;
+      }
+    }
+    store8<BF16>(pool, ((long)b * T + w) * D + ch * 8, val);
+  }
+}
+
 // m = 1 without overlap, gate or slot bias: the window of an entry is its own
 // token, whose softmax weight is exactly 1, so the entry is the token with
 // its rope slice rotated at pos0 + w.  One thread per 8-channel chunk: a
@@ -201,6 +273,18 @@ hipError_t launch_compress(const void* x, const void* gate, const float* slot_bi
     else
       hipLaunchKernelGGL(rope_copy_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, s, x,
                          pool, rows, S, D, rope_dim, reinterpret_cast<const float2*>(cs), pos0);
+    return hipGetLastError();
+  }
+  if (m * (1 + overlap) <= 32 && D % 8 == 0) {
+    const long blocks = ((long)B * T + 3) / 4;
+    if (bf16)
+      hipLaunchKernelGGL(compress_wave_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, s, x,
+                         gate, slot_bias, pool, B, S, D, m, overlap, rope_dim,
+                         reinterpret_cast<const float2*>(cs), pos0);
+    else
+      hipLaunchKernelGGL(compress_wave_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, s, x,
+                         gate, slot_bias, pool, B, S, D, m, overlap, rope_dim,
+                         reinterpret_cast<const float2*>(cs), pos0);
     return hipGetLastError();
   }
   const size_t lds = (size_t)kCompressWaves * 3 * D * sizeof(float);
