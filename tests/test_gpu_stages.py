@@ -164,6 +164,8 @@ ATTN_CASES = {
     "generic_f32": (2, 45, 4, 64, 64, 16, 64, 16, 32, 4, [0, 200], True, False, False),
     "generic_bf16": (1, 30, 6, 40, 40, 8, 20, 8, 8, 4, [60], True, True, False),
     "generic_hca_f32": (1, 40, 3, 32, 24, 8, 10, 0, 5, 4, [0], False, False, True),
+    # more index slots than the matrix-core kernel keeps in LDS: generic kernel
+    "generic_bigk_bf16": (1, 2, 64, 512, 512, 64, 3200, 3000, 32, 4, [20000], True, True, False),
 }
 
 
@@ -197,6 +199,47 @@ def test_attention(ops, name):
                                m=m, sink=z, rope_dim=rope, theta=theta, scale=scale, dv=dv)
         err = np.abs(out[b] - ref).max()
         assert err <= tol, (name, b, float(err))
+
+
+@pytest.mark.parametrize("name", ["csa_mfma", "csa_mfma_split", "hca_mfma_split", "dsa_mfma",
+                                  "dsa_mfma_split"])
+def test_attention_large_logits(ops, name):
+    """Logits that grow by far more than the kernel's lazy-rescale margin from
+    one key tile to the next: window keys are tiny, pool keys large, and the
+    score scale is 12, so the running maximum jumps by ~2^7 (log2 units) when
+    the first pool tile arrives and again, now and then, between pool tiles.
+    The query's RoPE channels are zero so that its rotation is exact and the
+    large scale does not amplify the rounding of the rotated query."""
+    B, S, H, D, dv, rope, T, k, window, m, qp, sink, bf16, dense = ATTN_CASES[name]
+    q, kv, pool, z, idx = _attn_case(zlib.crc32(name.encode()) % 1000 + 17, B, S, H, D, dv, rope,
+                                     T, k, window, m, qp, sink, bf16, dense)
+    q[..., D - rope:] = 0.0
+    pool *= 0.25                       # powers of two: still bf16 values
+    if kv is not None:
+        kv *= 1.0 / 64.0
+    theta, scale = 160000.0, 12.0
+    cs = ops.csa_rope_table(max(qp) + S + 1, rope, theta)
+    dt = torch.bfloat16
+    q_pos = torch.tensor(qp, dtype=torch.int32, device="cuda")
+    win_pos0 = torch.zeros(B, dtype=torch.int32, device="cuda")
+    kvd = dev(kv, dt) if kv is not None else None
+    zd = dev(z, torch.float32) if z is not None else None
+    if dense:
+        out = ops.hca_attn(dev(q, dt), kvd, win_pos0, dev(pool, dt), zd, q_pos, m=m,
+                           rope_dim=rope, cs=cs, window=window, scale=scale, dv=dv)
+    else:
+        out = ops.csa_sparse_attn(dev(q, dt), kvd, win_pos0, dev(pool, dt), dev(idx, torch.int32),
+                                  zd, q_pos, rope_dim=rope, cs=cs, window=window, scale=scale,
+                                  dv=dv)
+    out = host(out)
+    for b in range(B):
+        t = qp[b] + np.arange(S)
+        ref = oracle.attention(q[b], t, kv_win=None if kv is None else kv[b], win_pos0=0,
+                               window=window, pool=pool[b], idx=None if dense else idx[b],
+                               m=m, sink=z, rope_dim=rope, theta=theta, scale=scale, dv=dv)
+        assert np.all(np.isfinite(out[b]))
+        err = np.abs(out[b] - ref).max()
+        assert err <= BF16_ATOL, (name, b, float(err))
 
 
 def test_attention_edge_rows(ops):
