@@ -149,6 +149,25 @@ __global__ __launch_bounds__(256) void attn_generic_kernel(AttnParams p) {
 
 // ------------------------------------------------------------------ matrix-core
 
+// Division of n < 2^31 by an invariant d < 2^31 with one multiply-high: m =
+// floor(2^32 / d) + 1 makes floor(n m / 2^32) either n / d or one more (the
+// excess n (m - 2^32 / d) / 2^32 is below 1/2), which one compare settles.
+// m = 0 stands for d = 1.
+struct FastDiv {
+  unsigned d, m;
+};
+inline FastDiv make_fastdiv(unsigned d) {
+  FastDiv f;
+  f.d = d;
+  f.m = d <= 1 ? 0u : (unsigned)((1ull << 32) / d + 1);
+  return f;
+}
+__device__ __forceinline__ unsigned fdiv(unsigned n, FastDiv f) {
+  if (f.m == 0) return n;
+  const unsigned q = __umulhi(n, f.m);
+  return q * f.d > n ? q - 1 : q;
+}
+
 struct MfmaArgs {
   AttnParams p;
   float* ws;              // split partials, or nullptr
@@ -157,6 +176,7 @@ struct MfmaArgs {
   int nhg;                // groups of 64 heads
   int rows;               // query rows B * S
   long n_items;           // work items: rows rounded up to 8, x splits x head groups
+  FastDiv by_nhg, by_nsplit, by_S, by_m;
 };
 
 // K=V tile of 32 rows in LDS, 1 KiB per row, the 16-byte chunks of row r
@@ -315,16 +335,21 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(MfmaArgs args) {
     const long n = (long)blockIdx.x + (long)i * gridDim.x;
     if (n >= args.n_items) return it;
     const int x = (int)(n & 7);
-    const int rest = (int)(n >> 3);
-    const int hg = rest % args.nhg;
-    const int rest2 = rest / args.nhg;
-    it.split = rest2 % args.nsplit;
-    const int row = (rest2 / args.nsplit) * 8 + x;
+    const unsigned rest = (unsigned)(n >> 3);
+    const unsigned rest2 = fdiv(rest, args.by_nhg);
+    const int hg = (int)(rest - rest2 * args.nhg);
+    const unsigned rest3 = fdiv(rest2, args.by_nsplit);
+    it.split = (int)(rest2 - rest3 * args.nsplit);
+    const int row = (int)rest3 * 8 + x;
     if (row >= args.rows) return it;
     it.row = row;
     it.h0 = hg * HG;
-    it.b = row / p.S;
+    it.b = (int)fdiv((unsigned)row, args.by_S);
     return it;
+  };
+  // ready pool entries of a valid position t (0 <= t < n_pos)
+  auto ready_of = [&](int t) __attribute__((always_inline)) -> int {
+    return min((int)fdiv((unsigned)t + 1u, args.by_m), p.T);
   };
   // what the gathers of an item need (t, the window range and the validity
   // come from the S waves through LDS)
@@ -340,7 +365,7 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(MfmaArgs args) {
     m.tile0 = it.split * args.tiles_per_split;
     m.tlim = m.tile0 + args.tiles_per_split;
     // pool slots a gather may read: every ready entry (dense) or the k slots
-    m.bound = m.bad ? 0 : p.dense ? (p.pool ? ready_count(t, p.m, p.T) : 0) : p.k;
+    m.bound = m.bad ? 0 : p.dense ? (p.pool ? ready_of(t) : 0) : p.k;
     return m;
   };
   // tiles of an item's slice of the key list (at least one, so that every
@@ -401,19 +426,20 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(MfmaArgs args) {
     // an item's index row into LDS (slot = item parity) for the gathers, and
     // this wave's last live slot of it (-1: none) for the list length
     auto scan_publish = [&](const int (&w)[NSCAN], int slot) __attribute__((always_inline)) {
+      // (the wave's last live slot from ballots: scalar work, no lane
+      // exchange)
       int last = -1;
 #pragma unroll
       for (int u = 0; u < NSCAN; ++u) {
         const int jj = NS * 64 * u + tid;
         idx_s[slot][jj] = w[u];
-        if (jj < p.k && w[u] >= 0 && w[u] < p.T) last = jj;
+        const uint64_t live = __ballot(jj < p.k && w[u] >= 0 && w[u] < p.T);
+        if (live != 0ull) last = NS * 64 * u + 64 * w4 + 63 - (int)__builtin_clzll(live);
       }
-#pragma unroll
-      for (int sh = 32; sh > 0; sh >>= 1) last = max(last, __shfl_xor(last, sh, 64));
       if (lane == 0) scan_s[slot][w4] = last;
     };
     auto npool_of = [&](const int (&mt)[4], int slot) __attribute__((always_inline)) -> int {
-      if (p.dense) return p.pool ? ready_count(mt[0], p.m, p.T) : 0;
+      if (p.dense) return p.pool ? ready_of(mt[0]) : 0;
       if (!scan) return 0;
       const int4 s4 = *reinterpret_cast<const int4*>(scan_s[slot]);
       return __builtin_amdgcn_readfirstlane(max(max(s4.x, s4.y), max(s4.z, s4.w)) + 1);
@@ -678,6 +704,7 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(MfmaArgs args) {
         if constexpr (J == NBUF - 1) {
           if (last_round) advance();
         }
+
         const int u = q - start;
         if (cur.row >= 0 && u < ntl)
           s_step(std::integral_constant<int, (J + 1) % NBUF>{}, q & 1, u == 0);
@@ -786,23 +813,23 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(MfmaArgs args) {
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
   };
 
+  // O^T = V^T P^T: V is the A operand and P the B operand, so lane (g, c16)
+  // holds, for head block mb and column block nb, the four adjacent columns
+  // cbase + 16nb + 4g .. +3 of head 16mb + c16.
   f32x4 acc[4][NB];
-#pragma unroll
-  for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
   // ---- PV-wave step: PV of the tile in buffer J (P buffer par), after the
-  // rescale the S waves may have asked for with this P
-  auto pv_step = [&](auto JC, int par) __attribute__((always_inline)) {
-    const int4 rf = *reinterpret_cast<const int4*>(rfl_s[par]);
-    if (__builtin_amdgcn_readfirstlane(rf.x | rf.y | rf.z | rf.w) != 0) {
+  // rescale the S waves may have asked for with this P.  An item's first tile
+  // starts the sums from zero (no reset of the accumulators between items).
+  auto pv_step = [&](auto JC, int par, auto FIRST) __attribute__((always_inline)) {
+    constexpr bool first = decltype(FIRST)::value;
+    if constexpr (!first) {
+      const int4 rf = *reinterpret_cast<const int4*>(rfl_s[par]);
+      if (__builtin_amdgcn_readfirstlane(rf.x | rf.y | rf.z | rf.w) != 0) {
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb) {
-        const float4 a = *reinterpret_cast<const float4*>(&alpha_s[par][16 * mb + 4 * g]);
+        for (int mb = 0; mb < 4; ++mb) {
+          const float a = alpha_s[par][16 * mb + c16];
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-          acc[mb][nb][0] *= a.x; acc[mb][nb][1] *= a.y;
-          acc[mb][nb][2] *= a.z; acc[mb][nb][3] *= a.w;
+          for (int nb = 0; nb < NB; ++nb) acc[mb][nb] *= a;
         }
       }
     }
@@ -817,17 +844,13 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(MfmaArgs args) {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb) acc[mb][nb] = mfma16x16x32(pa[mb], vb[nb], acc[mb][nb]);
+      for (int mb = 0; mb < 4; ++mb)
+        acc[mb][nb] = mfma16x16x32(vb[nb], pa[mb],
+                                   first ? f32x4{0.f, 0.f, 0.f, 0.f} : acc[mb][nb]);
   };
 
-  // ---- output of an item.  Lane (g, c16) holds, for head block mb and column
-  // block nb, O[head 16mb + 4g + j][column cbase + 16nb + c16], j = 0..3.
-  // Stores go out as column pairs: adjacent lanes trade one value (even lane:
-  // row j, columns c, c+1; odd lane: row j+1, columns c-1, c).
-  const bool odd = (c16 & 1) != 0;
-  auto partner = [&](float v) __attribute__((always_inline)) -> float {
-    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true));
-  };
+  // ---- output of an item (lane: head 16mb + c16, columns cbase + 16nb + 4g
+  // .. +3 of each block)
   auto output = [&](const Meta& m, int slot) __attribute__((always_inline)) {
     if (split_mode) {
       float* po = args.ws + (size_t)args.rows * args.nsplit * H * 2 +
@@ -835,47 +858,67 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(MfmaArgs args) {
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-          const int col = cbase + 16 * nb + c16;
-#pragma unroll
-          for (int j = 0; j < 4; j += 2) {
-            const float v0 = acc[mb][nb][j], v1 = acc[mb][nb][j + 1];
-            const float r = partner(odd ? v0 : v1);
-            const int hr = 16 * mb + 4 * g + j + (odd ? 1 : 0);
-            *reinterpret_cast<float2*>(po + (size_t)hr * dv + col - (odd ? 1 : 0)) =
-                odd ? make_float2(r, v1) : make_float2(v0, r);
-          }
-        }
+        for (int nb = 0; nb < NB; ++nb)
+          *reinterpret_cast<f32x4*>(po + (size_t)(16 * mb + c16) * dv + cbase + 16 * nb + 4 * g) =
+              acc[mb][nb];
       return;
     }
-    u16* out = reinterpret_cast<u16*>(p.out) + ((long)m.row * H + m.h0) * dv;
+    // The bf16 results go out through LDS as 16-byte stores: the buffer the
+    // next gather (issued after this) fills is free here, and this wave
+    // stages in the rows it gathers itself, so no other wave touches them.
+    // Two passes of 32 heads x 128 columns (8 KiB).  Staged head row h holds
+    // 16 chunks of 8 columns, chunk c at position c ^ 2 (h % 8): an 8-byte
+    // write instruction (16 heads x 2 chunks) spreads evenly over the banks.
+    // (stores through a descriptor: one lane offset register, the head and
+    // pass in the scalar offset)
+    const __amdgpu_buffer_rsrc_t ors = __builtin_amdgcn_make_buffer_rsrc(
+        reinterpret_cast<u16*>(p.out) + ((long)m.row * H + m.h0) * dv + cbase, 0, HG * dv * 2,
+        0x00020000);
+    const int olane = (g * dv + 8 * c16) * 2;
+    unsigned char* stg = kbuf_of(std::integral_constant<int, NBUF - 1>{}) + w4 * RPW * KT::ROWB;
+    auto stg_pos = [](int h, int c) __attribute__((always_inline)) -> int {
+      return h * 256 + ((c ^ ((h & 7) << 1)) << 4);
+    };
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
-      const float4 li = *reinterpret_cast<const float4*>(&fin_s[slot][16 * mb + 4 * g]);
-      const float lv[4] = {li.x, li.y, li.z, li.w};
+    for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        const int col = cbase + 16 * nb + c16;
-        float v[4];
+      for (int mh = 0; mh < 2; ++mh) {
+        const int mb = 2 * pass + mh;
+        const float li = fin_s[slot][16 * mb + c16];
+        const int hl = 16 * mh + c16;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) v[j] = acc[mb][nb][j] * lv[j];
-        if (dv == D && cbase + 16 * nb + 16 > rbase) {
-          // de-rotate the rope slice at -t: pairs (even column, odd column)
-          // sit in adjacent lanes
-          const float2 rr = cs_s[slot][((col & ~1) - rbase) >> 1];
+        for (int nb = 0; nb < NB; ++nb) {
+          f32x4 v = acc[mb][nb] * li;
+          if (dv == D && cbase + 16 * nb + 16 > rbase) {
+            // de-rotate the rope slice at -t: the pairs (4g, 4g+1) and
+            // (4g+2, 4g+3) of the block
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const float o = partner(v[j]);
-            v[j] = odd ? (-o * rr.y + v[j] * rr.x) : (v[j] * rr.x + o * rr.y);
+            for (int e = 0; e < 4; e += 2) {
+              const float2 rr = cs_s[slot][(cbase + 16 * nb + 4 * g + e - rbase) >> 1];
+              const float a = v[e], bq = v[e + 1];
+              v[e] = a * rr.x + bq * rr.y;
+              v[e + 1] = bq * rr.x - a * rr.y;
+            }
           }
+          const int cl = 16 * nb + 4 * g;
+          *reinterpret_cast<uint2*>(stg + stg_pos(hl, cl >> 3) + 2 * (cl & 7)) =
+              make_uint2(pack2(v[0], v[1]), pack2(v[2], v[3]));
         }
+      }
+      // (LDS accesses of one wave complete in order: no barrier)
+      // (four reads in flight, then their four stores)
+      typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 #pragma unroll
-        for (int j = 0; j < 4; j += 2) {
-          const float r = partner(odd ? v[j] : v[j + 1]);
-          const int hr = 16 * mb + 4 * g + j + (odd ? 1 : 0);
-          *reinterpret_cast<uint32_t*>(out + hr * dv + col - (odd ? 1 : 0)) =
-              odd ? pack2(r, v[j + 1]) : pack2(v[j], r);
-        }
+      for (int i0 = 0; i0 < 8; i0 += 4) {
+        u32x4 d[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          d[i] = *reinterpret_cast<const u32x4*>(stg + stg_pos(4 * (i0 + i) + g, c16));
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          __builtin_amdgcn_raw_buffer_store_b128(d[i], ors, olane,
+                                                 (32 * pass + 4 * (i0 + i)) * dv * 2, 0);
       }
     }
   };
@@ -917,10 +960,6 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(MfmaArgs args) {
       // its 1/l before the last barrier), then the next item's list length
       // and the metadata of the one after (published with that barrier)
       output(mc, n & 1);
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
       ++n;
       mc = mn;
       if (mc.row < 0) break;
@@ -946,7 +985,13 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(MfmaArgs args) {
         issue(std::integral_constant<int, (J + NBUF - 1) % NBUF>{}, ma, tile,
               rid_of(ma, tile, slot_a));
       }
-      if (j - start < ntl) pv_step(JC, j & 1);
+      if constexpr (J == 0) {
+        // (a round start can be an item's first tile)
+        if (j == start) pv_step(JC, j & 1, std::true_type{});
+        else if (j - start < ntl) pv_step(JC, j & 1, std::false_type{});
+      } else {
+        if (j - start < ntl) pv_step(JC, j & 1, std::false_type{});
+      }
       // this wave's gathers of position j+2 have landed (NBUF = 4: those of
       // j+3 may be in flight)
       wait_vmcnt<(NBUF - 3) * G>();
@@ -1098,6 +1143,10 @@ hipError_t launch_attention(const AttnParams& p, const AttnPlan& plan, void* ws,
   a.nhg = p.H / 64;
   a.rows = (int)rows;
   a.n_items = (rows + 7) / 8 * 8 * a.nsplit * a.nhg;
+  a.by_nhg = make_fastdiv((unsigned)a.nhg);
+  a.by_nsplit = make_fastdiv((unsigned)a.nsplit);
+  a.by_S = make_fastdiv((unsigned)p.S);
+  a.by_m = make_fastdiv((unsigned)std::max(p.m, 1));
   // persistent: one workgroup per compute unit (the LDS use allows no more),
   // a multiple of 8 so that a workgroup's items keep one residue mod 8
   const long grid = (std::min<long>(device_cus(), a.n_items) + 7) / 8 * 8;
