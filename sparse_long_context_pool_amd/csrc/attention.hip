@@ -704,7 +704,6 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(MfmaArgs args) {
         if constexpr (J == NBUF - 1) {
           if (last_round) advance();
         }
-
         const int u = q - start;
         if (cur.row >= 0 && u < ntl)
           s_step(std::integral_constant<int, (J + 1) % NBUF>{}, q & 1, u == 0);
@@ -949,6 +948,9 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(MfmaArgs args) {
   issue(std::integral_constant<int, 1>{}, mc, mc.tile0 + 1, rid_of(mc, mc.tile0 + 1, 0));
   if constexpr (NBUF == 4)
     issue(std::integral_constant<int, 2>{}, mc, mc.tile0 + 2, rid_of(mc, mc.tile0 + 2, 0));
+  // row ids of the next gather, looked up one iteration ahead of its issue so
+  // that the index-row read is off the issue's path
+  int rid_pend = rid_of(mc, mc.tile0 + NBUF - 1, 0);
   wait_vmcnt<(NBUF - 2) * G>();
   lds_barrier();  // tile 0 landed
   wait_vmcnt<(NBUF - 3) * G>();
@@ -976,15 +978,15 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(MfmaArgs args) {
     auto iter = [&](auto JC, int j) __attribute__((always_inline)) {
       constexpr int J = decltype(JC)::value;
       // gather of position j+NBUF-1 (in this round for J = 0, in the next one
-      // after)
+      // after), then the row ids of position j+NBUF (always the next round's)
       if constexpr (J == 0) {
-        const int tile = mc.tile0 + (j + NBUF - 1 - start);
-        issue(std::integral_constant<int, NBUF - 1>{}, mc, tile, rid_of(mc, tile, n & 1));
+        issue(std::integral_constant<int, NBUF - 1>{}, mc, mc.tile0 + (j + NBUF - 1 - start),
+              rid_pend);
       } else {
-        const int tile = ma.tile0 + (j + NBUF - 1 - sa);
-        issue(std::integral_constant<int, (J + NBUF - 1) % NBUF>{}, ma, tile,
-              rid_of(ma, tile, slot_a));
+        issue(std::integral_constant<int, (J + NBUF - 1) % NBUF>{}, ma,
+              ma.tile0 + (j + NBUF - 1 - sa), rid_pend);
       }
+      rid_pend = rid_of(ma, ma.tile0 + (j + NBUF - sa), slot_a);
       if constexpr (J == 0) {
         // (a round start can be an item's first tile)
         if (j == start) pv_step(JC, j & 1, std::true_type{});
