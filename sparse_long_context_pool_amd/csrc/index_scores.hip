@@ -39,24 +39,25 @@ __device__ __forceinline__ float relu_bits(float x) {
   return __int_as_float(max(__float_as_int(x), 0));
 }
 
-// Many query rows (prefill, token-level indexer): workgroup = 8 consecutive
+// Many query rows (prefill, token-level indexer): workgroup = QR consecutive
 // query rows (one per wave) x one chunk of the pool.  The pool is walked in
-// 128-entry tiles (32 KiB), triple-buffered in LDS and shared by the 8 rows:
-// each wave fills four 1 KiB slices of every tile, two tiles ahead of the
-// products, with one barrier per tile.  Each wave keeps its row's
+// NT-entry tiles (NT = 16 QR, so QR x 4 KiB), triple-buffered in LDS and
+// shared by the QR rows: each wave fills four 1 KiB slices of every tile, two
+// tiles ahead of the products, with one barrier per tile.  Each wave keeps its row's
 // query fragments (the A operand, 64 heads x 128) in registers and, per
 // 32-entry block, runs 16 matrix instructions, the ReLU-and-weight epilogue
 // and one 128-byte store.  Row blocks are launched heaviest first.
-template <int NI, int CI>
-__global__ __launch_bounds__(512) void index_scores_mfma(
+template <int NI, int CI, int QR, int NT>
+__global__ __launch_bounds__(64 * QR) void index_scores_mfma(
     const u16* __restrict__ q_idx, const float* __restrict__ w_idx,
     const u16* __restrict__ k_pool, float* __restrict__ scores,
     const int* __restrict__ q_pos, int S, int T, int m, int chunk) {
-  constexpr int QR = 8;            // query rows = waves per workgroup
+  // QR query rows = waves per workgroup, NT entries per tile
   constexpr int MB = NI / 32;      // 32-head blocks
   constexpr int KS = CI / 16;      // k-steps of 16
-  constexpr int NT = 128;          // entries per tile
   constexpr int TB = NT * CI * 2;  // bytes per tile
+  constexpr int SPT = NT / 32;     // 32-entry blocks (and stores) per tile
+  static_assert(TB == QR * 4096, "each wave fills four 1 KiB slices of a tile");
   static_assert(CI == 128, "a key row is 16 chunks of 16 bytes");
   static_assert(NI <= 64, "one head weight per lane");
   // one static array per buffer (a load in flight into one buffer then does
@@ -191,20 +192,20 @@ __global__ __launch_bounds__(512) void index_scores_mfma(
   lds_barrier();
   issue(std::integral_constant<int, 2>{}, 2);
   compute(std::integral_constant<int, 0>{}, 0);
-  wait_vmcnt<8>();
+  wait_vmcnt<4 + SPT>();
   lds_barrier();
   issue(std::integral_constant<int, 0>{}, 3);
   compute(std::integral_constant<int, 1>{}, 1);
   for (int j = 2; j < ntiles; j += 3) {  // whole rounds: every wave, every path
-    wait_vmcnt<12>();
+    wait_vmcnt<4 + 2 * SPT>();
     lds_barrier();
     issue(std::integral_constant<int, 1>{}, j + 2);
     compute(std::integral_constant<int, 2>{}, j);
-    wait_vmcnt<12>();
+    wait_vmcnt<4 + 2 * SPT>();
     lds_barrier();
     issue(std::integral_constant<int, 2>{}, j + 3);
     compute(std::integral_constant<int, 0>{}, j + 1);
-    wait_vmcnt<12>();
+    wait_vmcnt<4 + 2 * SPT>();
     lds_barrier();
     issue(std::integral_constant<int, 0>{}, j + 4);
     compute(std::integral_constant<int, 1>{}, j + 2);
@@ -413,17 +414,20 @@ hipError_t launch_index_scores(const void* q_idx, const float* w_idx, const void
                          reinterpret_cast<const u16*>(k_pool), scores, q_pos, S, T, m, chunk);
       return hipGetLastError();
     }
-    constexpr int QR = 8;
+    // 4 rows per workgroup and 64-entry tiles (48 KiB of LDS): two workgroups
+    // share a compute unit, so one's query loads overlap the other's products
+    constexpr int QR = 4, NT = 16 * QR;
+    const int ntile = (T + NT - 1) / NT;
     const int nrb = (S + QR - 1) / QR;
     // split the pool over workgroups until the chip has enough of them
     const long wgs = (long)nrb * B;
     int nchunk = 1;
-    if (wgs < 1024) nchunk = (int)std::min<long>(tiles, (1024 + wgs - 1) / wgs);
-    int chunk_tiles = (tiles + nchunk - 1) / nchunk;
-    nchunk = (tiles + chunk_tiles - 1) / chunk_tiles;
-    const int chunk = chunk_tiles * kIdxTile;
+    if (wgs < 1024) nchunk = (int)std::min<long>(ntile, (1024 + wgs - 1) / wgs);
+    int chunk_tiles = (ntile + nchunk - 1) / nchunk;
+    nchunk = (ntile + chunk_tiles - 1) / chunk_tiles;
+    const int chunk = chunk_tiles * NT;
     dim3 grid(nrb, nchunk, B);
-    hipLaunchKernelGGL((index_scores_mfma<64, 128>), grid, dim3(512), 0, s,
+    hipLaunchKernelGGL((index_scores_mfma<64, 128, QR, NT>), grid, dim3(64 * QR), 0, s,
                        reinterpret_cast<const u16*>(q_idx), w_idx,
                        reinterpret_cast<const u16*>(k_pool), scores, q_pos, S, T, m, chunk);
     return hipGetLastError();
