@@ -95,30 +95,78 @@ class Runner:
     def add(self, name, fn):
         self.stages.append((name, fn))
 
+    def _capture(self, fns):
+        """A HIP graph of the launches of `fns` (launched once on the capture
+        stream first; the C entry points enqueue on torch's current stream)."""
+        torch = self.torch
+        cap = torch.cuda.Stream()
+        cap.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(cap):
+            for fn in fns:
+                fn()
+        torch.cuda.current_stream().wait_stream(cap)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for fn in fns:
+                fn()
+        torch.cuda.synchronize()
+        return graph
+
     def run(self, steps, warmup, flush=None):
+        """The step time (the reported value) comes from a HIP graph holding
+        one whole step (every stage's launches, no host work between them):
+        `warmup` untimed replays, then `steps` timed ones.  The per-stage
+        times (each kernel's roofline) come from one graph per stage,
+        replayed `steps` times with an event pair around each replay on the
+        stream the kernels run on; the host never waits inside a step, so it
+        runs ahead and no stage time holds host launch work.  `flush` (reads
+        that evict the caches) runs before every timed step, outside the
+        events."""
         torch = self.torch
         for _ in range(warmup):
             for _, fn in self.stages:
                 fn()
         torch.cuda.synchronize()
-        ev = {n: [] for n, _ in self.stages}
-        total_ms = 0.0
-        for _ in range(steps):
-            if flush is not None:
-                flush()
+        whole = self._capture([fn for _, fn in self.stages])
+        per = [(name, self._capture([fn])) for name, fn in self.stages]
+        for _ in range(warmup):
+            whole.replay()
+        torch.cuda.synchronize()
+        if flush is None:
             s0 = torch.cuda.Event(enable_timing=True)
             s1 = torch.cuda.Event(enable_timing=True)
             s0.record()
-            for name, fn in self.stages:
+            for _ in range(steps):
+                whole.replay()
+            s1.record()
+            torch.cuda.synchronize()
+            total_ms = s0.elapsed_time(s1)
+        else:
+            pairs = []
+            for _ in range(steps):
+                flush()
+                s0 = torch.cuda.Event(enable_timing=True)
+                s1 = torch.cuda.Event(enable_timing=True)
+                s0.record()
+                whole.replay()
+                s1.record()
+                pairs.append((s0, s1))
+            torch.cuda.synchronize()
+            total_ms = sum(a.elapsed_time(b) for a, b in pairs)
+        ev = {n: [] for n, _ in self.stages}
+        for _ in range(steps):
+            if flush is not None:
+                flush()
+            for name, g in per:
                 a = torch.cuda.Event(enable_timing=True)
                 b = torch.cuda.Event(enable_timing=True)
                 a.record()
-                fn()
+                g.replay()
                 b.record()
                 ev[name].append((a, b))
-            s1.record()
-            torch.cuda.synchronize()
-            total_ms += s0.elapsed_time(s1)
+        torch.cuda.synchronize()
+        del whole, per
         avg = {n: float(np.mean([a.elapsed_time(b) for a, b in v])) for n, v in ev.items()}
         return total_ms / steps, avg
 
@@ -258,8 +306,7 @@ def run_workload(name, steps, warmup, csa, torch, synth, WORKLOADS):
         junk = torch.ones(1 << 28, dtype=torch.int32, device="cuda")
 
         def flush():
-            junk.sum()
-            torch.cuda.synchronize()
+            junk.sum()          # stream-ordered before the step that follows
     ms_step, avg = r.run(steps, warmup, flush)
     work, keys = work_counts(wl)
     stages = stage_report(wl, avg, work)

@@ -214,36 +214,120 @@ __global__ __launch_bounds__(256) void compress_wave_kernel(
   }
 }
 
+// Rotation of a channel slice [8ch, 8ch + 8) at position pos: the pairs at or
+// above rope_base turn by the table's angle.
+__device__ __forceinline__ void rope8(float v[8], int ch, int rope_base, int rope_dim,
+                                      const float2* __restrict__ cs, long pos) {
+  if (ch * 8 + 8 <= rope_base) return;
+#pragma unroll
+  for (int e = 0; e < 8; e += 2) {
+    const int c = ch * 8 + e;
+    if (c >= rope_base) {
+      const float2 rr = cs[pos * (rope_dim >> 1) + ((c - rope_base) >> 1)];
+      const float a0 = v[e], a1 = v[e + 1];
+      v[e] = a0 * rr.x - a1 * rr.y;
+      v[e + 1] = a0 * rr.y + a1 * rr.x;
+    }
+  }
+}
+
 // m = 1 without overlap, gate or slot bias: the window of an entry is its own
 // token, whose softmax weight is exactly 1, so the entry is the token with
-// its rope slice rotated at pos0 + w.  One thread per 8-channel chunk: a
-// plain streaming pass instead of one workgroup per entry.
+// its rope slice rotated at pos0 + w.  A streaming pass: thread i takes the
+// 8-channel chunks i, i + n/4, i + 2n/4, i + 3n/4 of the n = rows x D/8
+// chunks, their four loads in flight together (a wave still reads 1 KiB
+// contiguous per load).
+constexpr int kCopyUnroll = 4;
 template <bool BF16>
 __global__ __launch_bounds__(256) void rope_copy_kernel(
     const void* __restrict__ x, void* __restrict__ pool, long rows, int S, int D,
     int rope_dim, const float2* __restrict__ cs, int pos0) {
-  const int nchunk = D >> 3;
-  const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= rows * nchunk) return;
-  const long r = i / nchunk;
-  const int ch = (int)(i - r * nchunk);
-  const int w = (int)(r % S);
-  float v[8];
-  load8<BF16>(x, r * D + ch * 8, v);
-  const int rope_base = D - rope_dim;
-  if (ch * 8 + 8 > rope_base) {
+  // (index arithmetic in 32 bits: the launcher keeps rows x D/8 < 2^31)
+  const unsigned nchunk = (unsigned)D >> 3;
+  const unsigned n = (unsigned)rows * nchunk;
+  const unsigned q = (n + kCopyUnroll - 1) / kCopyUnroll;
+  const unsigned i0 = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i0 >= q) return;
+  float v[kCopyUnroll][8];
 #pragma unroll
-    for (int e = 0; e < 8; e += 2) {
-      const int c = ch * 8 + e;
-      if (c >= rope_base) {
-        const float2 rr = cs[((long)pos0 + w) * (rope_dim >> 1) + ((c - rope_base) >> 1)];
-        const float a0 = v[e], a1 = v[e + 1];
-        v[e] = a0 * rr.x - a1 * rr.y;
-        v[e + 1] = a0 * rr.y + a1 * rr.x;
+  for (int u = 0; u < kCopyUnroll; ++u) {
+    const unsigned i = i0 + u * q;
+    if (i < n) load8<BF16>(x, (long)i * 8, v[u]);   // row r, chunk c: element 8 (r D/8 + c)
+  }
+  const int rope_base = D - rope_dim;
+#pragma unroll
+  for (int u = 0; u < kCopyUnroll; ++u) {
+    const unsigned i = i0 + u * q;
+    if (i < n) {
+      const unsigned r = i / nchunk;
+      const int ch = (int)(i - r * nchunk);
+      rope8(v[u], ch, rope_base, rope_dim, cs, (long)pos0 + (long)(r % (unsigned)S));
+      store8<BF16>(pool, (long)i * 8, v[u]);
+    }
+  }
+}
+
+// Windows of exactly NR = m (1 + overlap) rows (the token-window sizes in
+// use): one thread per (entry, 8-channel chunk), so small widths (an index key
+// of 128 channels is 16 chunks) still fill whole waves.  The window's rows are
+// loaded together (all loads in flight at once), then per channel the max of
+// the gate logits, the softmax weights and the weighted sum.  Rows before
+// token 0 (the first entry's overlap half) take no part.
+template <bool BF16, int NR>
+__global__ __launch_bounds__(256) void compress_rows_kernel(
+    const void* __restrict__ x, const void* __restrict__ gate,
+    const float* __restrict__ slot_bias, void* __restrict__ pool, int B, int S, int D, int m,
+    int overlap, int rope_dim, const float2* __restrict__ cs, int pos0) {
+  // (index arithmetic in 32 bits: the launcher keeps B x T x D/8 < 2^31)
+  const unsigned nchunk = (unsigned)D >> 3;
+  const unsigned T = (unsigned)(S / m);
+  const unsigned i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (unsigned)B * T * nchunk) return;
+  const unsigned e = i / nchunk;
+  const int ch = (int)(i - e * nchunk);
+  const int b = (int)(e / T);
+  const long w = (long)(e - (unsigned)b * T);
+  const long first = (w - overlap) * m;            // token held by slot 0
+  const long row0 = (long)b * S;
+  float xv[NR][8], a[NR][8];
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    const long j = first + r;
+    if (j >= 0) {
+      load8<BF16>(x, (row0 + j) * D + ch * 8, xv[r]);
+      if (gate) {
+        load8<BF16>(gate, (row0 + j) * D + ch * 8, a[r]);
+      } else {
+#pragma unroll
+        for (int v = 0; v < 8; ++v) a[r][v] = 0.f;
+      }
+      if (slot_bias) {
+        const float4* sb = reinterpret_cast<const float4*>(slot_bias + r * D + ch * 8);
+        const float4 s0 = sb[0], s1 = sb[1];
+        a[r][0] += s0.x; a[r][1] += s0.y; a[r][2] += s0.z; a[r][3] += s0.w;
+        a[r][4] += s1.x; a[r][5] += s1.y; a[r][6] += s1.z; a[r][7] += s1.w;
       }
     }
   }
-  store8<BF16>(pool, r * D + ch * 8, v);
+  float val[8];
+#pragma unroll
+  for (int v = 0; v < 8; ++v) {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < NR; ++r)
+      if (first + r >= 0) mx = fmaxf(mx, a[r][v]);
+    float sm = 0.f, ac = 0.f;
+#pragma unroll
+    for (int r = 0; r < NR; ++r)
+      if (first + r >= 0) {
+        const float ev = __expf(a[r][v] - mx);
+        sm += ev;
+        ac += ev * xv[r][v];
+      }
+    val[v] = ac / sm;
+  }
+  rope8(val, ch, D - rope_dim, rope_dim, cs, (long)pos0 + w * m);
+  store8<BF16>(pool, ((long)b * T + w) * D + ch * 8, val);
 }
 
 }  // namespace
@@ -264,15 +348,32 @@ hipError_t launch_compress(const void* x, const void* gate, const float* slot_bi
                            hipStream_t s) {
   const int T = S / m;
   if (T == 0 || B == 0) return hipSuccess;
-  if (m == 1 && overlap == 0 && gate == nullptr && slot_bias == nullptr && D % 8 == 0) {
+  if (m == 1 && overlap == 0 && gate == nullptr && slot_bias == nullptr && D % 8 == 0 &&
+      (long)B * S * (D / 8) < (1L << 31)) {
     const long rows = (long)B * S;
-    const long blocks = (rows * (D / 8) + 255) / 256;
+    const long blocks = ((rows * (D / 8) + kCopyUnroll - 1) / kCopyUnroll + 255) / 256;
     if (bf16)
       hipLaunchKernelGGL(rope_copy_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, s, x,
                          pool, rows, S, D, rope_dim, reinterpret_cast<const float2*>(cs), pos0);
     else
       hipLaunchKernelGGL(rope_copy_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, s, x,
                          pool, rows, S, D, rope_dim, reinterpret_cast<const float2*>(cs), pos0);
+    return hipGetLastError();
+  }
+  if ((m * (1 + overlap) == 8 || m * (1 + overlap) == 4) && D % 8 == 0 &&
+      (long)B * T * (D / 8) < (1L << 31)) {
+    const long blocks = ((long)B * T * (D / 8) + 255) / 256;
+#define CSA_ROWS(NR)                                                                         \
+  if (bf16)                                                                                  \
+    hipLaunchKernelGGL((compress_rows_kernel<true, NR>), dim3((unsigned)blocks), dim3(256), 0, \
+                       s, x, gate, slot_bias, pool, B, S, D, m, overlap, rope_dim,            \
+                       reinterpret_cast<const float2*>(cs), pos0);                           \
+  else                                                                                       \
+    hipLaunchKernelGGL((compress_rows_kernel<false, NR>), dim3((unsigned)blocks), dim3(256), 0, \
+                       s, x, gate, slot_bias, pool, B, S, D, m, overlap, rope_dim,            \
+                       reinterpret_cast<const float2*>(cs), pos0);
+    if (m * (1 + overlap) == 8) { CSA_ROWS(8) } else { CSA_ROWS(4) }
+#undef CSA_ROWS
     return hipGetLastError();
   }
   if (m * (1 + overlap) <= 32 && D % 8 == 0) {
