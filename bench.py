@@ -303,7 +303,9 @@ def run_workload(name, steps, warmup, csa, torch, synth, WORKLOADS):
         # flush it between steps so every step reads HBM, not the cache.  The
         # flush READS 1 GiB (a write would leave dirty lines whose write-back
         # then competes with the timed kernels) and completes before the step.
-        junk = torch.ones(1 << 28, dtype=torch.int32, device="cuda")
+        # (fp32: its sum reduces in place; an int32 sum would first widen the
+        # whole buffer to int64, a 2 GiB write)
+        junk = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
 
         def flush():
             junk.sum()          # stream-ordered before the step that follows
