@@ -468,6 +468,56 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(MfmaArgs args) {
       sink_raw = __builtin_bit_cast(
           float, (int)__builtin_amdgcn_raw_buffer_load_b32(sink_rs, 4 * (it.h0 + hq), 0, 0));
     };
+    // D = 512: the next item's queries go into a second register set, their
+    // loads spread over the first three iterations of the current item's last
+    // round (a few per iteration, where the S waves have slack) instead of one
+    // burst at its end; the RoPE factors and the rope k-steps go first (the
+    // rotation needs them first).  The RoPE factors and the sink value of the
+    // current item are dead once its first tile has started, so those go
+    // straight into their registers.
+    constexpr bool kSpread = D == 512;
+    bf16x8 qn[KS];
+    auto q_load_part = [&](const Item& it, int t, auto PART) __attribute__((always_inline)) {
+      constexpr int part = decltype(PART)::value;
+      const long row = it.row < 0 ? 0 : it.row;
+      // (through a descriptor over the item's 64 query rows: one lane offset,
+      // the k-step in the scalar offset)
+      const __amdgpu_buffer_rsrc_t qrs = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<u16*>(reinterpret_cast<const u16*>(p.q) + (row * H + it.h0) * D), 0,
+          HG * D * 2, 0x00020000);
+      const int qoff = (hq * D + 8 * g) * 2;
+      auto qld = [&](int ks) __attribute__((always_inline)) -> bf16x8 {
+        return __builtin_bit_cast(bf16x8,
+                                  __builtin_amdgcn_raw_buffer_load_b128(qrs, qoff, 64 * ks, 0));
+      };
+      if constexpr (part == 0) {
+#pragma unroll
+        for (int kr = 0; kr < KR; ++kr) {
+          const float4* c4 =
+              reinterpret_cast<const float4*>(cs + (long)t * half + 16 * kr + 4 * g);
+          const float4 a = c4[0], bq = c4[1];
+          csr[kr][0] = make_float2(a.x, a.y); csr[kr][1] = make_float2(a.z, a.w);
+          csr[kr][2] = make_float2(bq.x, bq.y); csr[kr][3] = make_float2(bq.z, bq.w);
+        }
+      }
+      // part 0: the rope k-steps and the first 8 - KR; part 1: the next 6;
+      // part 2: the rest and the sink
+      constexpr int lo = part == 0 ? 0 : part == 1 ? 8 - KR : 14 - KR;
+      constexpr int hi = part == 0 ? 8 - KR : part == 1 ? 14 - KR : KS - KR;
+      if constexpr (part == 0) {
+#pragma unroll
+        for (int kr = 0; kr < KR; ++kr) qn[KS - KR + kr] = qld(KS - KR + kr);
+      }
+#pragma unroll
+      for (int ks = lo; ks < hi; ++ks) qn[ks] = qld(ks);
+      if constexpr (part == 2)
+        sink_raw = __builtin_bit_cast(
+            float, (int)__builtin_amdgcn_raw_buffer_load_b32(sink_rs, 4 * (it.h0 + hq), 0, 0));
+    };
+    auto q_take = [&]() __attribute__((always_inline)) {
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) qf[ks] = qn[ks];
+    };
     // the RoPE factors of the item's position, for the PV waves' output
     auto cs_publish = [&](int slot) __attribute__((always_inline)) {
       if (w4 == 0 && c16 == 0) {
@@ -509,20 +559,21 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(MfmaArgs args) {
     // heads of this wave, in groups of 4 k-steps; lane supplies K row
     // 16kb + c16, 16-byte chunk 4ks + g.  Four accumulation chains (key block x
     // even/odd k-step).
-    constexpr int NG = (KS + 3) / 4;
+    constexpr int GK = 4;                             // k-steps per group
+    constexpr int NG = (KS + GK - 1) / GK;
     // K row c16 (and 16 + c16, same swizzle), logical chunk 4ks + g: physical
     // chunk ((4 (ks % 4) + g) ^ f(c16)) + 16 (ks / 4)
     const int fk = swz(c16);
     int koff[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) koff[u] = c16 * KT::ROWB + 16 * ((4 * u + g) ^ fk);
-    auto k_group = [&](auto JC, int grp, uint4 (&kv)[4][2]) __attribute__((always_inline)) {
+    auto k_group = [&](auto JC, int grp, uint4 (&kv)[GK][2]) __attribute__((always_inline)) {
       const unsigned char* kbase = kbuf_of(JC);
       // tail area: rows c16 and 16 + c16 sit in wave blocks c16/8 and 2 + c16/8
       const unsigned char* ktail = tbuf_of(JC) + (c16 >> 3) * KT::TBLK + (c16 & 7) * 16 + 128 * g;
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const int ks = 4 * grp + kk;
+      for (int kk = 0; kk < GK; ++kk) {
+        const int ks = GK * grp + kk;
         if (ks < KT::MAIN / 32) {
           const unsigned char* kp = kbase + koff[ks & 3] + 256 * (ks >> 2);
           kv[kk][0] = *reinterpret_cast<const uint4*>(kp);
@@ -534,11 +585,11 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(MfmaArgs args) {
         }
       }
     };
-    auto s_group = [&](int grp, const uint4 (&kv)[4][2], f32x4 (&sa)[4])
+    auto s_group = [&](int grp, const uint4 (&kv)[GK][2], f32x4 (&sa)[4])
         __attribute__((always_inline)) {
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const int ks = 4 * grp + kk;
+      for (int kk = 0; kk < GK; ++kk) {
+        const int ks = GK * grp + kk;
         if (ks < KS) {
           sa[(kk & 1) * 2 + 0] = mfma16x16x32(as_bf16x8(kv[kk][0]), qf[ks], sa[(kk & 1) * 2 + 0]);
           sa[(kk & 1) * 2 + 1] = mfma16x16x32(as_bf16x8(kv[kk][1]), qf[ks], sa[(kk & 1) * 2 + 1]);
@@ -590,7 +641,7 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(MfmaArgs args) {
     // ---- S-wave step: S + softmax of the tile in buffer JN (P buffer par),
     // the K groups read one group ahead of their products
     auto s_step = [&](auto JN, int par, bool first) __attribute__((always_inline)) {
-      uint4 kv[2][4][2];
+      uint4 kv[2][GK][2];
       k_group(JN, 0, kv[0]);
       const f32x4 bias0 = bias_of(JN, 0), bias1 = bias_of(JN, 1);
       f32x4 sa[4];
@@ -662,13 +713,20 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(MfmaArgs args) {
     // after next (loaded one item ago), load the next item's queries, then the
     // index row and positions of the item after that (issued after the
     // queries, so that waiting for the queries never waits for them)
-    auto prefetch = [&]() __attribute__((always_inline)) {
+    auto publish = [&]() __attribute__((always_inline)) {
       scan_publish(wsc, n & 1);
       pos_meta(nx2, qp2, wp2, mt_nx2);
       if (w4 == 0 && lane == 0)
         *reinterpret_cast<int4*>(meta_s[n & 1]) =
             make_int4(mt_nx2[0], mt_nx2[1], mt_nx2[2], mt_nx2[3]);
-      q_load(nx, mt_nx[0]);
+    };
+    auto prefetch = [&]() __attribute__((always_inline)) {
+      if constexpr (!kSpread) {
+        publish();
+        q_load(nx, mt_nx[0]);
+      } else {
+        q_load_part(nx, mt_nx[0], std::integral_constant<int, 2>{});
+      }
       const Item n3 = item_at(n + 3);
       scan_load(n3, wsc);
       load_pos(n3, qp2, wp2);
@@ -685,6 +743,7 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(MfmaArgs args) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) { mt_cur[e] = mt_nx[e]; mt_nx[e] = mt_nx2[e]; }
       if (cur.row >= 0) {
+        if constexpr (kSpread) q_take();
         q_rotate();
         cs_publish(n & 1);
         state_reset();
@@ -707,6 +766,17 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(MfmaArgs args) {
         const int u = q - start;
         if (cur.row >= 0 && u < ntl)
           s_step(std::integral_constant<int, (J + 1) % NBUF>{}, q & 1, u == 0);
+        if constexpr (kSpread && J == 0) {
+          if (last_round && nx.row >= 0) q_load_part(nx, mt_nx[0], std::integral_constant<int, 0>{});
+        }
+        if constexpr (kSpread && J == 1) {
+          // (not at J = 0: the PV waves read this item's list length and the
+          // next item's metadata at the round start, before the first barrier)
+          if (last_round && nx.row >= 0) {
+            publish();
+            q_load_part(nx, mt_nx[0], std::integral_constant<int, 1>{});
+          }
+        }
         if constexpr (J == NBUF - 2) {
           if (last_round && nx.row >= 0) prefetch();
         }
