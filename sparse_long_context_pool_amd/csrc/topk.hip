@@ -7,8 +7,8 @@
 // ascending index order and padded with -1.  That result is unique, so the
 // kernel is deterministic and matches any correct implementation bit for bit.
 //
-// One workgroup (8 wavefronts) per query row.  Scores become order-preserving
-// 32-bit keys (-0 folded onto +0).  A most-significant-digit-first radix
+// One workgroup per query row (4, 8 or 16 wavefronts by row length).  Scores
+// become order-preserving 32-bit keys (-0 folded onto +0).  A most-significant-digit-first radix
 // select finds the k-th largest key K and how many copies of K to keep; a
 // final pass in index order keeps every key > K and the first copies of K,
 // with output positions from wave ballots and popcounts, so the result is
@@ -147,11 +147,15 @@ __global__ __launch_bounds__(kTopkThreads) void topk_global(
 // wave ballots of (key > K) and (key == K) give every entry its rank among the
 // earlier ones; the per-(slice, wave) totals are prefix-summed once, so the
 // ordered compaction needs a single barrier.
-template <int KPT>
-__global__ __launch_bounds__(kTopkThreads) void topk_reg(
+// NT threads per row (NT / 64 waves), KPT keys per thread; the 2048 histogram
+// bins are scanned BPT = 2048 / NT per thread.
+template <int KPT, int NT>
+__global__ __launch_bounds__(NT) void topk_reg(
     const float* __restrict__ scores, int* __restrict__ idx, const int* __restrict__ q_pos,
     int S, int T, int k, int m) {
-  constexpr int NW = kTopkWaves;
+  constexpr int NW = NT / 64;
+  constexpr int BPT = 2048 / NT;
+  static_assert(BPT == 2 || BPT == 4 || BPT == 8, "bins per thread");
   __shared__ uint32_t hist[2][2048];
   __shared__ int wtot[NW];
   __shared__ int meta[2];
@@ -165,7 +169,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_reg(
   const float* src = scores + row * T;
 
   if (R <= k) {  // every ready entry is kept
-    for (int j = tid; j < k; j += kTopkThreads) out[j] = j < R ? j : -1;
+    for (int j = tid; j < k; j += NT) out[j] = j < R ? j : -1;
     return;
   }
   // keys of entries 512 j + tid.  Entries past R get key 0, below the key of
@@ -176,15 +180,15 @@ __global__ __launch_bounds__(kTopkThreads) void topk_reg(
   // are in flight together)
   float sv[KPT];
 #pragma unroll
-  for (int j = 0; j < KPT; ++j) sv[j] = src[min(j * kTopkThreads + tid, R - 1)];
+  for (int j = 0; j < KPT; ++j) sv[j] = src[min(j * NT + tid, R - 1)];
   uint32_t key[KPT];
 #pragma unroll
-  for (int j = 0; j < KPT; ++j) key[j] = j * kTopkThreads + tid < R ? score_key(sv[j]) : 0u;
+  for (int j = 0; j < KPT; ++j) key[j] = j * NT + tid < R ? score_key(sv[j]) : 0u;
 
   uint32_t prefix = 0u, pmask = 0u;
   int kk = k;
   int buf = 0;
-  for (int j = tid; j < 2048; j += kTopkThreads) hist[0][j] = 0u;
+  for (int j = tid; j < 2048; j += NT) hist[0][j] = 0u;
 #pragma unroll
   for (int pass = 0; pass < 3; ++pass) {
     const int shift = pass == 0 ? 21 : pass == 1 ? 10 : 0;
@@ -197,11 +201,24 @@ __global__ __launch_bounds__(kTopkThreads) void topk_reg(
     for (int j = 0; j < KPT; ++j)
       if (key[j] != 0u && (key[j] & pmask) == prefix) atomicAdd(&h[(key[j] >> shift) & dmask], 1u);
     // clear the other copy for the next pass meanwhile
-    for (int j = tid; j < 2048; j += kTopkThreads) hist[buf ^ 1][j] = 0u;
+    for (int j = tid; j < 2048; j += NT) hist[buf ^ 1][j] = 0u;
     __syncthreads();
-    // thread t owns bins 4t .. 4t+3; suffix sums over the bins above
-    const uint4 hb = *reinterpret_cast<const uint4*>(&h[4 * tid]);
-    const int loc = (int)(hb.x + hb.y + hb.z + hb.w);
+    // thread t owns bins BPT t .. BPT t + BPT-1; suffix sums over the bins above
+    int cnt[BPT];
+    if constexpr (BPT == 2) {
+      const uint2 hb = *reinterpret_cast<const uint2*>(&h[2 * tid]);
+      cnt[0] = (int)hb.x; cnt[1] = (int)hb.y;
+    } else {
+#pragma unroll
+      for (int q = 0; q < BPT / 4; ++q) {
+        const uint4 hb = *reinterpret_cast<const uint4*>(&h[BPT * tid + 4 * q]);
+        cnt[4 * q] = (int)hb.x; cnt[4 * q + 1] = (int)hb.y;
+        cnt[4 * q + 2] = (int)hb.z; cnt[4 * q + 3] = (int)hb.w;
+      }
+    }
+    int loc = 0;
+#pragma unroll
+    for (int u = 0; u < BPT; ++u) loc += cnt[u];
     int suf = loc;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
@@ -213,11 +230,10 @@ __global__ __launch_bounds__(kTopkThreads) void topk_reg(
     int above = suf - loc;
 #pragma unroll
     for (int w = 0; w < NW; ++w) above += w > wave ? wtot[w] : 0;
-    const int cnt[4] = {(int)hb.x, (int)hb.y, (int)hb.z, (int)hb.w};
 #pragma unroll
-    for (int u = 3; u >= 0; --u) {
+    for (int u = BPT - 1; u >= 0; --u) {
       if (above < kk && above + cnt[u] >= kk) {
-        meta[0] = 4 * tid + u;
+        meta[0] = BPT * tid + u;
         meta[1] = above;
       }
       above += cnt[u];
@@ -292,7 +308,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_reg(
       const uint64_t mg = __ballot(gt), me = __ballot(eq);
       const int gb = gb0[u] + __popcll(mg & lt);
       const int eb = eb0[u] + __popcll(me & lt);
-      if (gt || (eq && eb < kk)) out[gb + min(eb, kk)] = j * kTopkThreads + tid;
+      if (gt || (eq && eb < kk)) out[gb + min(eb, kk)] = j * NT + tid;
     }
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -304,15 +320,21 @@ hipError_t launch_topk(const float* scores, int* idx, const int* q_pos, int B, i
                        int T, int k, int m, hipStream_t s) {
   const long rows = (long)B * S;
   if (rows == 0) return hipSuccess;
-  const dim3 grid((unsigned)rows), block(kTopkThreads);
-  if (T <= 4 * kTopkThreads)
-    hipLaunchKernelGGL(topk_reg<4>, grid, block, 0, s, scores, idx, q_pos, S, T, k, m);
-  else if (T <= 16 * kTopkThreads)
-    hipLaunchKernelGGL(topk_reg<16>, grid, block, 0, s, scores, idx, q_pos, S, T, k, m);
-  else if (T <= 64 * kTopkThreads)
-    hipLaunchKernelGGL(topk_reg<64>, grid, block, 0, s, scores, idx, q_pos, S, T, k, m);
+  const dim3 grid((unsigned)rows);
+  // short rows: 256 threads, so that eight rows share a compute unit; long
+  // rows with few of them (decode): 1024 threads, half the keys per thread
+  if (T <= 2048)
+    hipLaunchKernelGGL((topk_reg<8, 256>), grid, dim3(256), 0, s, scores, idx, q_pos, S, T, k, m);
+  else if (T <= 16 * 512)
+    hipLaunchKernelGGL((topk_reg<16, 512>), grid, dim3(512), 0, s, scores, idx, q_pos, S, T, k, m);
+  else if (T <= 32 * 1024 && rows < 256)
+    hipLaunchKernelGGL((topk_reg<32, 1024>), grid, dim3(1024), 0, s, scores, idx, q_pos, S, T, k,
+                       m);
+  else if (T <= 64 * 512)
+    hipLaunchKernelGGL((topk_reg<64, 512>), grid, dim3(512), 0, s, scores, idx, q_pos, S, T, k, m);
   else
-    hipLaunchKernelGGL(topk_global, grid, block, 0, s, scores, idx, q_pos, S, T, k, m);
+    hipLaunchKernelGGL(topk_global, grid, dim3(kTopkThreads), 0, s, scores, idx, q_pos, S, T, k,
+                       m);
   return hipGetLastError();
 }
 

@@ -111,7 +111,7 @@ def test_index_scores(ops, case):
 @pytest.mark.parametrize("T,k,m,qp,S", [
     (64, 16, 4, [0, 120], 37), (2048, 512, 4, [0, 6000], 70), (2048, 512, 1, [1000, 1500], 20),
     (32768, 2048, 4, [131071, 90000], 3), (40000, 2048, 1, [39990, 20000], 4),
-    (300, 300, 1, [0, 100], 9)])
+    (300, 300, 1, [0, 100], 9), (12000, 1024, 1, [11000, 6000], 130)])
 def test_topk_bit_exact(ops, T, k, m, qp, S):
     B = 2
     r = rng(T + k)
