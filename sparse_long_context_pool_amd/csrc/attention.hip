@@ -243,8 +243,8 @@ struct KTile {
 // S phase: S^T[keys][heads] = K Q^T with 16x16x32 matrix instructions, the
 // query fragments held in registers; a lane ends with the logits of keys
 // 4g + r and 16 + 4g + r (g = lane / 16, r = 0..3) of its head, which are
-// exactly an A operand of the PV product in the key order position
-// 8g + e <-> key 16(e/4) + 4g + (e%4).  P goes through LDS in that order, and
+// exactly a P operand of the PV product (O^T = V^T P^T, P the B operand) in
+// the key order position 8g + e <-> key 16(e/4) + 4g + (e%4).  P goes through LDS in that order, and
 // V is read with the gfx950 transposing LDS load (ds_read_b64_tr_b16: 4 keys
 // x 1 column per lane) in the same key order.
 //

@@ -16,8 +16,9 @@
 // registers; pool rows come in through direct-to-LDS loads of whole cache
 // lines, their 16-byte chunks swizzled by row so that B-fragment reads fall in
 // distinct banks.  Two kernels:
-//   many query rows (prefill, token-level indexer): 8 rows per workgroup share
-//     each 128-entry tile of the pool (MFMA-bound);
+//   many query rows (prefill, token-level indexer): 4 rows per workgroup share
+//     each 64-entry tile of the pool, two workgroups per compute unit
+//     (MFMA-bound);
 //   few query rows (decode): a pool entry meets one query row only, so each
 //     wave streams its own blocks and the pool is split over workgroups so
 //     that the whole chip streams it (HBM-bound).

@@ -8,11 +8,17 @@
 // the indexer keys.
 //
 // The compressor is HBM-bound (it reads each token row of x and gate once and
-// writes one row per m tokens).  One workgroup owns one entry; its four
-// wavefronts split the window rows, each lane owns 8 consecutive channels
-// (one 16-byte bf16 load per row), and every lane keeps an online softmax per
-// channel.  The four partial states merge through LDS, and the RoPE pair
-// rotation is applied to the merged entry before the store.
+// writes one row per m tokens).  A thread (or lane) owns 8 consecutive
+// channels (one 16-byte bf16 load per row); the RoPE pair rotation is applied
+// to the finished entry before the store.  By window shape:
+//   m = 1, no gate: the entry is its token, rotated (a streaming copy);
+//   windows of exactly 4 or 8 rows (CSA at m = 4 or 2 with overlap): one
+//     thread per (entry, chunk), the window's rows loaded together, then
+//     max, weights and weighted sum per channel;
+//   other windows of up to 32 rows: one wave per entry, an online softmax
+//     per channel over the rows;
+//   longer windows (HCA, m' = 128): one workgroup per entry, its four waves
+//     split the rows and merge their online-softmax states through LDS.
 #include "csa_device.hpp"
 
 namespace csa {
