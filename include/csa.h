@@ -106,6 +106,41 @@ csa_status_t csa_compress(const void *x, const void *gate, const float *slot_bia
                           int32_t n_pos, int32_t pos0, int32_t dtype, void *stream);
 
 /*
+ * csa_cache_append -- the decode-time cache update: appends n tokens per
+ * sequence to the compressor state, the pool and the sliding window.  Page
+ * "DeepSeek-V4", "Cache layers" (a sliding window of K=V rows plus the
+ * compressor's buffer / pool / count, with overlap state for CSA; the indexer
+ * keys run the same compressor at index_head_dim).
+ *   x, gate   [B][n][D] dtype   the new token rows (gate NULL: all zero)
+ *   slot_bias [(1+overlap)*m][D] fp32, or NULL
+ *   ring_x    [B][L][D] dtype   in/out, L = (1+overlap)*m: raw x of the last L
+ *                               tokens, position p at row p mod L
+ *   ring_g    [B][L][D] dtype   in/out, the same for gate; NULL iff gate NULL
+ *   pool      [B][T_cap][D] dtype  in/out: entry w is written when token
+ *                               (w+1)m-1 arrives, pooled exactly as
+ *                               csa_compress pools it (pos0 = 0: positions
+ *                               count from the first token); entries at or
+ *                               past T_cap are not written
+ *   win       [B][W][D] dtype   in/out, or NULL (W = 0): the last W tokens,
+ *                               rotated at their positions, position p at row
+ *                               p mod W -- the ring csa_sparse_attn reads when
+ *                               its win_pos0 is NULL
+ *   count     [B] int32         tokens appended before this call, per
+ *                               sequence (read only: the caller adds n after
+ *                               the call, e.g. with a device add)
+ *   Rows at positions past the RoPE table (n_pos) are written as NaN when
+ *   rope_dim > 0.  Two kernels in stream order (the entries read the ring
+ *   before the new tokens overwrite it); calls on one cache must not overlap.
+ *   Requires D % 8 == 0, D <= 1024, m >= 1, (1+overlap)*m <= 256, n >= 0.
+ */
+csa_status_t csa_cache_append(const void *x, const void *gate, const float *slot_bias,
+                              void *ring_x, void *ring_g, void *pool, void *win,
+                              const int32_t *count, int32_t B, int32_t n, int32_t D,
+                              int32_t m, int32_t overlap, int32_t T_cap, int32_t W,
+                              int32_t rope_dim, const float *cs, int32_t n_pos,
+                              int32_t dtype, void *stream);
+
+/*
  * csa_index_scores -- Lightning-Indexer index scores.  Page "DeepSeek-V4",
  * "Hybrid attention" (indexer scoring queries against the pool, eqs. 13-17)
  * and DeepseekV4Config (index_n_heads = n_h^I of eq. 14, index_head_dim);

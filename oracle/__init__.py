@@ -159,6 +159,47 @@ def compress(x, gate=None, slot_bias=None, *, m: int, overlap: int,
     return pool
 
 
+def cache_state(x, gate=None, slot_bias=None, *, count: int, m: int, overlap: int,
+                rope_dim: int = 0, theta: float = 1.0, W: int = 0,
+                bf16: bool = False):
+    """The decode cache of one sequence after its first `count` tokens x[:count]
+    (page "DeepSeek-V4", section "Cache layers": a sliding window of K=V rows and
+    the compressor's buffer / pool / count with overlap state), written out from
+    its definition rather than updated step by step:
+
+    * pool: the compressor over those tokens -- the count // m entries whose
+      window has closed, positions counted from token 0;
+    * ring_x / ring_g: raw rows of the last L = (1+overlap) m tokens, token p at
+      row p mod L (the compressor's buffer and overlap state);
+    * win: the last W tokens rotated at their own positions, token p at row
+      p mod W.
+
+    Returns (pool, ring_x, ring_g, win, ring_rows, win_rows): the row lists give
+    the ring / window rows that hold a token (the others hold nothing yet)."""
+    x = _f32(x)
+    D = x.shape[1]
+    g = _f32(gate)
+    L = (1 + overlap) * m
+    pool = compress(x[:count], None if g is None else g[:count], slot_bias, m=m,
+                    overlap=overlap, rope_dim=rope_dim, theta=theta, pos0=0,
+                    round_bf16=bf16)
+    ring_x = np.zeros((L, D), np.float32)
+    ring_g = np.zeros((L, D), np.float32) if g is not None else None
+    ring_rows = []
+    for p in range(max(0, count - L), count):
+        ring_x[p % L] = x[p]
+        if g is not None:
+            ring_g[p % L] = g[p]
+        ring_rows.append(p % L)
+    win = np.zeros((max(W, 1), D), np.float32)
+    win_rows = []
+    for p in range(max(0, count - W), count):
+        r = rope_apply(x[p:p + 1], rope_dim, theta, np.array([p]), +1)[0] if rope_dim else x[p]
+        win[p % W] = round_bf16(r) if bf16 else r
+        win_rows.append(p % W)
+    return pool, ring_x, ring_g, win[:W], sorted(ring_rows), sorted(win_rows)
+
+
 def index_scores(qI, wI, tpos, kI, *, m: int) -> np.ndarray:
     """qI[n, nI, cI], wI[n, nI], tpos[n], kI[T, cI] -> scores[n, T] (-inf if not ready)."""
     qI, wI, kI = _f32(qI), _f32(wI), _f32(kI)

@@ -33,6 +33,8 @@ def lib():
             "csa_rope_table": ([vp, i32, i32, f64, vp], ctypes.c_int),
             "csa_compress": ([vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp, i32, i32,
                               i32, vp], ctypes.c_int),
+            "csa_cache_append": ([vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
+                                  i32, i32, i32, vp, i32, i32, vp], ctypes.c_int),
             "csa_index_scores": ([vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
                                   vp], ctypes.c_int),
             "csa_topk": ([vp, vp, vp, i32, i32, i32, i32, i32, vp], ctypes.c_int),
@@ -53,6 +55,7 @@ def lib():
 
 
 EXPORTS = ("csa_last_error", "csa_version", "csa_rope_table", "csa_compress",
+           "csa_cache_append",
            "csa_index_scores", "csa_topk", "csa_sparse_attn",
            "csa_sparse_attn_workspace_size", "hca_attn", "hca_attn_workspace_size")
 
@@ -113,6 +116,26 @@ def csa_compress(x, gate=None, slot_bias=None, *, m: int, overlap: int, rope_dim
                               overlap, rope_dim, _ptr(cs), n_pos, pos0, _dtype(x), _stream()),
            "csa_compress")
     return out
+
+
+def csa_cache_append(x, gate, slot_bias, count, ring_x, ring_g, pool, win=None, *, m: int,
+                     overlap: int, rope_dim: int = 0, cs=None) -> None:
+    """Append x [B, n, D] (+ gate) to a decode cache: ring_x/ring_g [B, (1+overlap)m, D]
+    (compressor buffer and overlap state), pool [B, T_cap, D], win [B, W, D] or None
+    (the sliding window as a ring); count [B] int32 = tokens appended before (the
+    caller adds n afterwards)."""
+    B, n, D = x.shape
+    if gate is not None:
+        assert gate.shape == x.shape and gate.dtype == x.dtype
+    assert count.dtype == torch.int32 and count.numel() == B
+    T_cap = pool.shape[1]
+    W = 0 if win is None else win.shape[1]
+    n_pos = 0 if cs is None else cs.shape[0]
+    _check(lib().csa_cache_append(_ptr(x), _ptr(gate), _ptr(slot_bias), _ptr(ring_x),
+                                  _ptr(ring_g), _ptr(pool), _ptr(win), _ptr(count), B, n, D, m,
+                                  overlap, T_cap, W, rope_dim, _ptr(cs), n_pos, _dtype(x),
+                                  _stream()),
+           "csa_cache_append")
 
 
 def csa_index_scores(q_idx, w_idx, k_pool, q_pos, *, m: int, out=None) -> torch.Tensor:

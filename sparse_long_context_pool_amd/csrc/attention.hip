@@ -60,7 +60,7 @@ __device__ __forceinline__ long slot_row(const AttnParams& p, const RowInfo& ri,
     *from_win = true;
     const long pos = ri.t - ri.window + 1 + s;
     if (pos < 0 || p.kv_win == nullptr) return -1;
-    const long r = pos - (long)p.win_pos0[ri.b];
+    const long r = p.win_ring ? pos % p.L_win : pos - (long)p.win_pos0[ri.b];
     if (r < 0 || r >= p.L_win) return -1;
     return ((long)ri.b * p.L_win + r) * p.D;
   }
@@ -389,8 +389,9 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(MfmaArgs args) {
     const __amdgpu_buffer_rsrc_t qpos_rs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<int*>(p.q_pos), 0, p.B * 4, 0x00020000);
     const bool has_win = p.window > 0 && p.kv_win != nullptr;
+    const bool lin_win = has_win && !p.win_ring;
     const __amdgpu_buffer_rsrc_t wpos_rs = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<int*>(has_win ? p.win_pos0 : p.q_pos), 0, has_win ? p.B * 4 : 0,
+        const_cast<int*>(lin_win ? p.win_pos0 : p.q_pos), 0, lin_win ? p.B * 4 : 0,
         0x00020000);
     const __amdgpu_buffer_rsrc_t sink_rs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<float*>(use_sink ? p.sink : p.cs), 0, use_sink ? H * 4 : 0, 0x00020000);
@@ -407,9 +408,16 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(MfmaArgs args) {
       const int bad = (it.row < 0 || t < 0 || t >= p.n_pos) ? 1 : 0;
       int n_win = 0, r_lo = 0;
       if (!bad && has_win) {
-        const long lo = max(t - p.window + 1, max(0L, (long)wp));
-        const long hi = min(t, (long)wp + (long)p.L_win - 1);
-        if (hi >= lo) { n_win = (int)(hi - lo + 1); r_lo = (int)(lo - wp); }
+        if (p.win_ring) {
+          // the ring holds positions (t - L_win, t]: row of position lo
+          const long lo = max(t - p.window + 1, 0L);
+          n_win = (int)(t - lo + 1);
+          r_lo = (int)(lo % p.L_win);
+        } else {
+          const long lo = max(t - p.window + 1, max(0L, (long)wp));
+          const long hi = min(t, (long)wp + (long)p.L_win - 1);
+          if (hi >= lo) { n_win = (int)(hi - lo + 1); r_lo = (int)(lo - wp); }
+        }
       }
       mt[0] = bad ? 0 : (int)t; mt[1] = n_win; mt[2] = r_lo; mt[3] = bad;
     };
@@ -816,7 +824,9 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(MfmaArgs args) {
     if (m.bad || tile >= m.tlim) return -1;
     if (tile < m.WT) {
       const int jj = tile * kNK + w4 * RPW + (lane & 7);
-      return jj < m.n_win ? m.r_lo + jj : -1;
+      if (jj >= m.n_win) return -1;
+      const int r = m.r_lo + jj;       // (a ring wraps once at most: n_win <= L_win)
+      return r >= p.L_win ? r - p.L_win : r;
     }
     const int jj = (tile - m.WT) * kNK + w4 * RPW + (lane & 7);
     const int w = p.dense ? jj : idx_s[slot][min(jj, kMaxK - 1)];

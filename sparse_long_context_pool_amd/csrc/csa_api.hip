@@ -62,9 +62,14 @@ csa_status_t check_attn(const char* fn, const void* q, const void* kv_win,
   if (!aligned16(q) || !aligned16(out))
     return fail(CSA_ERR_INVALID, "%s: q and out must be 16-byte aligned", fn);
   if (window > 0 && L_win > 0) {
-    if (!kv_win || !win_pos0)
-      return fail(CSA_ERR_INVALID, "%s: kv_win and win_pos0 are required when window > 0", fn);
+    if (!kv_win)
+      return fail(CSA_ERR_INVALID, "%s: kv_win is required when window > 0", fn);
     if (!aligned16(kv_win)) return fail(CSA_ERR_INVALID, "%s: kv_win not 16-byte aligned", fn);
+    // win_pos0 NULL: kv_win is a ring (position p at row p mod L_win) that
+    // must still hold every window position of every query row
+    if (!win_pos0 && L_win < window + S - 1)
+      return fail(CSA_ERR_INVALID, "%s: a ring window needs L_win >= window + S - 1 (%d < %d)",
+                  fn, L_win, window + S - 1);
   }
   if (T > 0) {
     if (!pool) return fail(CSA_ERR_INVALID, "%s: pool is required when T > 0", fn);
@@ -86,6 +91,7 @@ csa::AttnParams make_params(const void* q, const void* kv_win, const int32_t* wi
   p.q = q;
   p.kv_win = has_win ? kv_win : nullptr;
   p.win_pos0 = has_win ? win_pos0 : nullptr;
+  p.win_ring = has_win && win_pos0 == nullptr;
   p.L_win = has_win ? L_win : 0;
   p.pool = T > 0 ? pool : nullptr;
   p.T = T;
@@ -167,6 +173,44 @@ csa_status_t csa_compress(const void* x, const void* gate, const float* slot_bia
   return launched(csa::launch_compress(x, gate, slot_bias, pool, B, S, D, m, overlap,
                                        rope_dim, cs, pos0, dtype == CSA_BF16,
                                        as_stream(stream)),
+                  fn);
+}
+
+csa_status_t csa_cache_append(const void* x, const void* gate, const float* slot_bias,
+                              void* ring_x, void* ring_g, void* pool, void* win,
+                              const int32_t* count, int32_t B, int32_t n, int32_t D, int32_t m,
+                              int32_t overlap, int32_t T_cap, int32_t W, int32_t rope_dim,
+                              const float* cs, int32_t n_pos, int32_t dtype, void* stream) {
+  const char* fn = "csa_cache_append";
+  if (!dtype_ok(dtype)) return fail(CSA_ERR_INVALID, "%s: unknown dtype %d", fn, dtype);
+  if (B < 0 || n < 0 || D < 8 || m < 1 || (overlap != 0 && overlap != 1) || T_cap < 0 ||
+      W < 0)
+    return fail(CSA_ERR_INVALID, "%s: bad sizes (B=%d n=%d D=%d m=%d overlap=%d T_cap=%d W=%d)",
+                fn, B, n, D, m, overlap, T_cap, W);
+  if (D % 8 != 0) return fail(CSA_ERR_INVALID, "%s: D=%d must be a multiple of 8", fn, D);
+  if (D > 1024) return fail(CSA_ERR_UNSUPPORTED, "%s: D=%d > 1024", fn, D);
+  if ((1 + overlap) * m > 256)
+    return fail(CSA_ERR_UNSUPPORTED, "%s: window of %d rows > 256", fn, (1 + overlap) * m);
+  if (rope_dim < 0 || (rope_dim & 1) || rope_dim > D)
+    return fail(CSA_ERR_INVALID, "%s: rope_dim=%d must be even and in [0, D]", fn, rope_dim);
+  if ((long)B * n == 0) return CSA_OK;
+  if ((long)n * (D / 8) >= (1L << 30))
+    return fail(CSA_ERR_UNSUPPORTED, "%s: n=%d too large", fn, n);
+  if (!x || !ring_x || !pool || !count)
+    return fail(CSA_ERR_INVALID, "%s: x, ring_x, pool and count are required", fn);
+  if ((gate == nullptr) != (ring_g == nullptr))
+    return fail(CSA_ERR_INVALID, "%s: gate and ring_g go together", fn);
+  if ((W > 0) != (win != nullptr))
+    return fail(CSA_ERR_INVALID, "%s: win is required exactly when W > 0", fn);
+  if (!aligned16(x) || !aligned16(ring_x) || !aligned16(pool) || (gate && !aligned16(gate)) ||
+      (ring_g && !aligned16(ring_g)) || (win && !aligned16(win)) ||
+      (slot_bias && !aligned16(slot_bias)))
+    return fail(CSA_ERR_INVALID, "%s: tensors must be 16-byte aligned", fn);
+  if (rope_dim > 0 && (!cs || n_pos < 1))
+    return fail(CSA_ERR_INVALID, "%s: the RoPE table is required", fn);
+  return launched(csa::launch_cache_append(x, gate, slot_bias, ring_x, ring_g, pool, win,
+                                           count, B, n, D, m, overlap, T_cap, W, rope_dim, cs,
+                                           n_pos, dtype == CSA_BF16, as_stream(stream)),
                   fn);
 }
 

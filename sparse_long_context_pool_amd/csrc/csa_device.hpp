@@ -145,6 +145,12 @@ hipError_t launch_compress(const void* x, const void* gate, const float* slot_bi
                            int rope_dim, const float* cs, int pos0, bool bf16,
                            hipStream_t s);
 
+hipError_t launch_cache_append(const void* x, const void* gate, const float* slot_bias,
+                               void* ring_x, void* ring_g, void* pool, void* win,
+                               const int* count, int B, int n, int D, int m, int overlap,
+                               int T_cap, int W, int rope_dim, const float* cs, int n_pos,
+                               bool bf16, hipStream_t s);
+
 hipError_t launch_index_scores(const void* q_idx, const float* w_idx, const void* k_pool,
                                float* scores, const int* q_pos, int B, int S, int T,
                                int n_heads, int head_dim, int m, bool bf16,
@@ -156,7 +162,8 @@ hipError_t launch_topk(const float* scores, int* idx, const int* q_pos, int B, i
 struct AttnParams {
   const void* q;          // [B][S][H][D]
   const void* kv_win;     // [B][L_win][D]
-  const int* win_pos0;    // [B]
+  const int* win_pos0;    // [B]; nullptr with kv_win: a ring, position p at row p % L_win
+  int win_ring;
   int L_win;
   const void* pool;       // [B][T][D]
   int T;

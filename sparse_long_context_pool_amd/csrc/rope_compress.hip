@@ -336,6 +336,130 @@ __global__ __launch_bounds__(256) void compress_rows_kernel(
   store8<BF16>(pool, ((long)b * T + w) * D + ch * 8, val);
 }
 
+// Cache update (page "DeepSeek-V4", section "Cache layers": the compressor's
+// buffer / pool / count with the CSA overlap state, and the sliding window of
+// K=V rows).  Per sequence b: ring_x / ring_g hold the raw rows of the last
+// L = (1+overlap) m tokens at row p mod L (the compressor's buffer and overlap
+// state), win the last W rotated rows at row p mod W, pool the entries; count[b]
+// tokens came before this call, which appends tokens count[b] .. count[b]+n-1
+// (x and gate [B][n][D]).  Positions past the RoPE table give NaN rows.
+//
+// Pass 1: the entries whose window closes within the call, w from
+// count/m to (count+n)/m - 1; window row j comes from x when the call brings
+// it (j >= count), else from the ring.  Pooled as the compressor pools them:
+// per channel the max of the logits, the weights, the weighted sum.
+template <bool BF16>
+__global__ __launch_bounds__(256) void cache_entries_kernel(
+    const void* __restrict__ x, const void* __restrict__ gate,
+    const float* __restrict__ slot_bias, const void* __restrict__ ring_x,
+    const void* __restrict__ ring_g, void* __restrict__ pool, const int* __restrict__ count,
+    int n, int D, int m, int overlap, int T_cap, int E, int rope_dim,
+    const float2* __restrict__ cs, int n_pos) {
+  const int nchunk = D >> 3;
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  const int b = blockIdx.y;
+  if (i >= E * nchunk) return;
+  const int e = i / nchunk, ch = i - e * nchunk;
+  const long c0 = count[b];
+  const long w = c0 / m + e;
+  if (c0 < 0 || w >= (c0 + n) / m || w >= T_cap) return;
+  const int L = (1 + overlap) * m;
+  const long first = (w - overlap) * m;             // token held by slot 0
+  const long j0 = first < 0 ? 0 : first, j1 = (w + 1) * m;
+  auto row_x = [&](long j, float v[8]) {
+    if (j >= c0) load8<BF16>(x, ((long)b * n + (j - c0)) * D + ch * 8, v);
+    else load8<BF16>(ring_x, ((long)b * L + j % L) * D + ch * 8, v);
+  };
+  auto row_a = [&](long j, float a[8]) {
+    if (gate) {
+      if (j >= c0) load8<BF16>(gate, ((long)b * n + (j - c0)) * D + ch * 8, a);
+      else load8<BF16>(ring_g, ((long)b * L + j % L) * D + ch * 8, a);
+    } else {
+#pragma unroll
+      for (int v = 0; v < 8; ++v) a[v] = 0.f;
+    }
+    if (slot_bias) {
+      const float4* sb = reinterpret_cast<const float4*>(slot_bias + (j - first) * D + ch * 8);
+      const float4 s0 = sb[0], s1 = sb[1];
+      a[0] += s0.x; a[1] += s0.y; a[2] += s0.z; a[3] += s0.w;
+      a[4] += s1.x; a[5] += s1.y; a[6] += s1.z; a[7] += s1.w;
+    }
+  };
+  float mx[8], sm[8], ac[8];
+#pragma unroll
+  for (int v = 0; v < 8; ++v) { mx[v] = -INFINITY; sm[v] = 0.f; ac[v] = 0.f; }
+  for (long j = j0; j < j1; ++j) {
+    float a[8];
+    row_a(j, a);
+#pragma unroll
+    for (int v = 0; v < 8; ++v) mx[v] = fmaxf(mx[v], a[v]);
+  }
+  for (long j = j0; j < j1; ++j) {
+    float a[8], xv[8];
+    row_a(j, a);
+    row_x(j, xv);
+#pragma unroll
+    for (int v = 0; v < 8; ++v) {
+      const float ev = __expf(a[v] - mx[v]);
+      sm[v] += ev;
+      ac[v] += ev * xv[v];
+    }
+  }
+  float val[8];
+#pragma unroll
+  for (int v = 0; v < 8; ++v) val[v] = ac[v] / sm[v];
+  const long pos = w * m;
+  if (rope_dim > 0) {
+    if (pos < n_pos) {
+      rope8(val, ch, D - rope_dim, rope_dim, cs, pos);
+    } else {
+#pragma unroll
+      for (int v = 0; v < 8; ++v) val[v] = __int_as_float(0x7fc00000);
+    }
+  }
+  store8<BF16>(pool, ((long)b * T_cap + w) * D + ch * 8, val);
+}
+
+// Pass 2 (after pass 1, which reads the ring): the call's last L tokens into
+// the ring, its last W tokens, rotated at their positions, into the window.
+template <bool BF16>
+__global__ __launch_bounds__(256) void cache_tokens_kernel(
+    const void* __restrict__ x, const void* __restrict__ gate, void* __restrict__ ring_x,
+    void* __restrict__ ring_g, void* __restrict__ win, const int* __restrict__ count, int n,
+    int D, int L, int W, int rope_dim, const float2* __restrict__ cs, int n_pos) {
+  const int nchunk = D >> 3;
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  const int b = blockIdx.y;
+  if (i >= n * nchunk) return;
+  const int k = i / nchunk, ch = i - k * nchunk;
+  const long c0 = count[b];
+  if (c0 < 0) return;
+  const long p = c0 + k;
+  const long src = ((long)b * n + k) * D + ch * 8;
+  float v[8];
+  load8<BF16>(x, src, v);
+  if (k >= n - L) {
+    // (bf16 -> fp32 -> bf16 is exact: the ring keeps the rows bit for bit)
+    store8<BF16>(ring_x, ((long)b * L + p % L) * D + ch * 8, v);
+    if (gate) {
+      float g[8];
+      load8<BF16>(gate, src, g);
+      store8<BF16>(ring_g, ((long)b * L + p % L) * D + ch * 8, g);
+    }
+  }
+  if (win != nullptr && k >= n - W) {
+    if (rope_dim > 0) {
+      if (p < n_pos) {
+        rope8(v, ch, D - rope_dim, rope_dim, cs, p);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = __int_as_float(0x7fc00000);
+      }
+    }
+    store8<BF16>(win, ((long)b * W + p % W) * D + ch * 8, v);
+  }
+}
+
 }  // namespace
 
 hipError_t launch_rope_table(float* cs, int n_pos, int rope_dim, double theta,
@@ -404,6 +528,37 @@ hipError_t launch_compress(const void* x, const void* gate, const float* slot_bi
     hipLaunchKernelGGL(compress_kernel<false>, grid, dim3(256), lds, s, x, gate, slot_bias,
                        pool, S, D, m, overlap, rope_dim,
                        reinterpret_cast<const float2*>(cs), pos0);
+  return hipGetLastError();
+}
+
+hipError_t launch_cache_append(const void* x, const void* gate, const float* slot_bias,
+                               void* ring_x, void* ring_g, void* pool, void* win,
+                               const int* count, int B, int n, int D, int m, int overlap,
+                               int T_cap, int W, int rope_dim, const float* cs, int n_pos,
+                               bool bf16, hipStream_t s) {
+  if (B == 0 || n == 0) return hipSuccess;
+  const int nchunk = D / 8;
+  const int E = n / m + 2;  // entries that can close within n tokens, and spare
+  const float2* cs2 = reinterpret_cast<const float2*>(cs);
+  const dim3 g1((unsigned)((E * nchunk + 255) / 256), (unsigned)B);
+  if (bf16)
+    hipLaunchKernelGGL(cache_entries_kernel<true>, g1, dim3(256), 0, s, x, gate, slot_bias,
+                       ring_x, ring_g, pool, count, n, D, m, overlap, T_cap, E, rope_dim, cs2,
+                       n_pos);
+  else
+    hipLaunchKernelGGL(cache_entries_kernel<false>, g1, dim3(256), 0, s, x, gate, slot_bias,
+                       ring_x, ring_g, pool, count, n, D, m, overlap, T_cap, E, rope_dim, cs2,
+                       n_pos);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int L = (1 + overlap) * m;
+  const dim3 g2((unsigned)((n * nchunk + 255) / 256), (unsigned)B);
+  if (bf16)
+    hipLaunchKernelGGL(cache_tokens_kernel<true>, g2, dim3(256), 0, s, x, gate, ring_x, ring_g,
+                       win, count, n, D, L, W, rope_dim, cs2, n_pos);
+  else
+    hipLaunchKernelGGL(cache_tokens_kernel<false>, g2, dim3(256), 0, s, x, gate, ring_x, ring_g,
+                       win, count, n, D, L, W, rope_dim, cs2, n_pos);
   return hipGetLastError();
 }
 

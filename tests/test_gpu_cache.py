@@ -1,0 +1,177 @@
+"""The decode cache update (csa_cache_append) against the oracle's cache state,
+and attention over a ring window (win_pos0 NULL) against the oracle over the
+same rows laid out linearly.  Every GPU input comes from the oracle or the
+seeded generators: the starting cache state is the oracle's, and each call's
+result is compared with the oracle's state after the same tokens."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from parity import BF16_ATOL, F32_ATOL, dev, host
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def ops():
+    from sparse_long_context_pool_amd import csa
+    assert torch.cuda.is_available()
+    csa.lib()
+    return csa
+
+
+def rnd(shape, seed, bf16):
+    a = np.random.default_rng(seed).standard_normal(shape).astype(np.float32)
+    return oracle.round_bf16(a) if bf16 else a
+
+
+CACHE_CASES = {
+    # name: (D, rope, m, overlap, gate, slot_bias, W, bf16, start counts, calls)
+    "csa_kv_bf16": (512, 64, 4, 1, True, False, 128, True, [0, 5, 130], [1, 3, 1, 8, 9, 1]),
+    "csa_keys_bf16": (128, 0, 4, 1, True, False, 0, True, [3, 0, 64], [1, 1, 4, 7]),
+    "csa_f32_bias": (64, 16, 4, 1, True, True, 16, False, [0, 9, 2], [2, 5, 1, 12]),
+    "hca_bf16": (512, 64, 128, 0, True, False, 128, True, [0, 127, 300], [1, 130, 1, 128]),
+    "nogate_m2_f32": (64, 16, 2, 1, False, False, 8, False, [1, 0, 6], [1, 2, 3]),
+}
+
+
+@pytest.mark.parametrize("name", sorted(CACHE_CASES))
+def test_cache_append(ops, name):
+    D, R, m, ov, has_gate, has_bias, W, bf16, c0, calls = CACHE_CASES[name]
+    B, theta, L = len(c0), 160000.0, (1 + ov) * m
+    dt = torch.bfloat16 if bf16 else torch.float32
+    N = max(c0) + sum(calls)
+    T_cap = N // m + 1
+    x = rnd((B, N, D), 1, bf16)
+    g = rnd((B, N, D), 2, bf16) if has_gate else None
+    sb = rnd((L, D), 3, False) if has_bias else None
+    cs = ops.csa_rope_table(N + 1, max(R, 2), theta) if R else None
+
+    def state(b, count):
+        return oracle.cache_state(x[b], None if g is None else g[b], sb, count=count, m=m,
+                                  overlap=ov, rope_dim=R, theta=theta, W=W, bf16=bf16)
+
+    # the starting caches: the oracle's state after c0[b] tokens
+    ring_x = np.zeros((B, L, D), np.float32)
+    ring_g = np.zeros((B, L, D), np.float32)
+    pool = np.zeros((B, T_cap, D), np.float32)
+    win = np.zeros((B, max(W, 1), D), np.float32)
+    for b in range(B):
+        p0, rx, rg, w0, _, _ = state(b, c0[b])
+        ring_x[b], pool[b, :len(p0)] = rx, p0
+        if has_gate:
+            ring_g[b] = rg
+        if W:
+            win[b] = w0
+    ring_x_d, pool_d = dev(ring_x, dt), dev(pool, dt)
+    ring_g_d = dev(ring_g, dt) if has_gate else None
+    win_d = dev(win, dt) if W else None
+    count = list(c0)
+    count_d = torch.tensor(c0, dtype=torch.int32, device="cuda")
+    sb_d = None if sb is None else dev(sb, torch.float32)
+    tol = 2.0 ** -7 if bf16 else 1e-5
+    for n in calls:
+        xn = np.stack([x[b, count[b]:count[b] + n] for b in range(B)])
+        gn = None if g is None else np.stack([g[b, count[b]:count[b] + n] for b in range(B)])
+        ops.csa_cache_append(dev(xn, dt), None if gn is None else dev(gn, dt), sb_d, count_d,
+                             ring_x_d, ring_g_d, pool_d, win_d, m=m, overlap=ov, rope_dim=R,
+                             cs=cs)
+        count = [c + n for c in count]
+        count_d.add_(n)
+        gx, gp = host(ring_x_d), host(pool_d)
+        gg = host(ring_g_d) if has_gate else None
+        gw = host(win_d) if W else None
+        for b in range(B):
+            p_ref, rx, rg, w_ref, rows, wrows = state(b, count[b])
+            np.testing.assert_allclose(gp[b, :len(p_ref)], p_ref, rtol=tol, atol=1e-5,
+                                       err_msg=f"{name} pool b={b} count={count[b]}")
+            assert np.array_equal(gx[b, rows], rx[rows]), (name, b, "ring_x")
+            if has_gate:
+                assert np.array_equal(gg[b, rows], rg[rows]), (name, b, "ring_g")
+            if W:
+                np.testing.assert_allclose(gw[b, wrows], w_ref[wrows], rtol=tol, atol=1e-5,
+                                           err_msg=f"{name} window b={b}")
+
+
+def test_cache_append_matches_compress(ops):
+    """Token by token, the cache's pool is the compressor's pool over the whole
+    sequence, bit for bit (the two kernels pool a window the same way)."""
+    B, S, D, R, m = 2, 37, 512, 64, 4
+    x = dev(rnd((B, S, D), 5, True), torch.bfloat16)
+    g = dev(rnd((B, S, D), 6, True), torch.bfloat16)
+    cs = ops.csa_rope_table(S + 1, R, 160000.0)
+    full = ops.csa_compress(x, g, m=m, overlap=1, rope_dim=R, cs=cs, pos0=0)
+    T = S // m
+    ring_x = torch.zeros((B, 2 * m, D), dtype=torch.bfloat16, device="cuda")
+    ring_g = torch.zeros_like(ring_x)
+    pool = torch.zeros((B, T + 1, D), dtype=torch.bfloat16, device="cuda")
+    count = torch.zeros(B, dtype=torch.int32, device="cuda")
+    for t in range(S):
+        ops.csa_cache_append(x[:, t:t + 1].contiguous(), g[:, t:t + 1].contiguous(), None,
+                             count, ring_x, ring_g, pool, None, m=m, overlap=1, rope_dim=R,
+                             cs=cs)
+        count.add_(1)
+    assert torch.equal(pool[:, :T].view(torch.int16), full.view(torch.int16))
+
+
+@pytest.mark.parametrize("H,D,dv,R,W,S,k,bf16", [
+    (64, 512, 512, 64, 128, 1, 48, True),     # matrix-core kernel, decode shape
+    (64, 512, 512, 64, 128, 3, 48, True),     # several rows: ring of W + S - 1 rows
+    (4, 64, 64, 16, 16, 2, 8, False),         # generic kernel, fp32
+])
+def test_attention_ring_window(ops, H, D, dv, R, W, S, k, bf16):
+    B, T, theta, m = 2, 64, 160000.0, 4
+    t0 = [300, 97]                       # position of each sequence's first query row
+    Lr = W + S - 1
+    dt = torch.bfloat16 if bf16 else torch.float32
+    q = rnd((B, S, H, D), 21, bf16)
+    pool = rnd((B, T, D), 22, bf16)
+    z = rnd((H,), 23, False)
+    r = np.random.default_rng(24)
+    idx = np.full((B, S, k), -1, np.int32)
+    for b in range(B):
+        for i in range(S):
+            rc = oracle.ready_count(t0[b] + i, m, T)
+            sel = np.sort(r.choice(rc, size=min(k, rc), replace=False))
+            idx[b, i, :len(sel)] = sel
+    # window rows for positions t0 + S - 1 - Lr + 1 .. t0 + S - 1, laid out
+    # linearly for the oracle and as a ring (position p at row p mod Lr)
+    ring = np.zeros((B, Lr, D), np.float32)
+    lin, lin0 = [], []
+    for b in range(B):
+        top = t0[b] + S - 1
+        p0 = max(0, top - Lr + 1)
+        rows = rnd((top - p0 + 1, D), 30 + b, bf16)
+        lin.append(rows)
+        lin0.append(p0)
+        for j, p in enumerate(range(p0, top + 1)):
+            ring[b, p % Lr] = rows[j]
+    cs = ops.csa_rope_table(max(t0) + S + 1, R, theta)
+    q_pos = torch.tensor(t0, dtype=torch.int32, device="cuda")
+    scale = 1.0 / math.sqrt(D)
+    out = host(ops.csa_sparse_attn(dev(q, dt), dev(ring, dt), None, dev(pool, dt),
+                                   dev(idx, torch.int32), dev(z, torch.float32), q_pos,
+                                   rope_dim=R, cs=cs, window=W, scale=scale, dv=dv))
+    tol = BF16_ATOL if bf16 else F32_ATOL
+    for b in range(B):
+        ref = oracle.attention(q[b], t0[b] + np.arange(S), kv_win=lin[b], win_pos0=lin0[b],
+                               window=W, pool=pool[b], idx=idx[b], m=m, sink=z, rope_dim=R,
+                               theta=theta, scale=scale, dv=dv)
+        err = np.abs(out[b] - ref).max()
+        assert err <= tol, (b, float(err))
+
+
+def test_ring_window_too_short_is_rejected(ops):
+    B, S, H, D, W = 1, 3, 64, 512, 128
+    q = torch.zeros((B, S, H, D), dtype=torch.bfloat16, device="cuda")
+    ring = torch.zeros((B, W, D), dtype=torch.bfloat16, device="cuda")   # needs W + S - 1
+    pool = torch.zeros((B, 8, D), dtype=torch.bfloat16, device="cuda")
+    idx = torch.full((B, S, 4), -1, dtype=torch.int32, device="cuda")
+    cs = ops.csa_rope_table(16, 64, 1e4)
+    q_pos = torch.zeros(B, dtype=torch.int32, device="cuda")
+    with pytest.raises(RuntimeError, match="ring window"):
+        ops.csa_sparse_attn(q, ring, None, pool, idx, None, q_pos, rope_dim=64, cs=cs,
+                            window=W, scale=0.05)

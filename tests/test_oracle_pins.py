@@ -409,3 +409,38 @@ def test_attention_empty_row_is_zero(orc):
     out = orc.attention(q, np.array([0, 5]), pool=np.zeros((3, 16), np.float32),
                         idx=np.full((2, 2), -1, np.int32), scale=0.25, m=4)
     assert np.all(out == 0)
+
+
+def test_cache_state_is_causal_and_holds_the_last_tokens(orc):
+    """The decode cache after `count` tokens ("DeepSeek-V4", section "Cache
+    layers"): an entry, once its window has closed, never changes as tokens
+    arrive (the compressor reads no token past its window); the buffer holds
+    the raw rows of the last (1+overlap) m tokens; the window holds the last W
+    tokens rotated at their positions (a rotation keeps each pair's length)."""
+    r = np.random.default_rng(11)
+    S, D, m, ov, R, W = 41, 16, 4, 1, 8, 6
+    x = r.standard_normal((S, D)).astype(np.float32)
+    g = r.standard_normal((S, D)).astype(np.float32)
+    prev = None
+    for count in range(S + 1):
+        pool, rx, rg, win, rows, wrows = orc.cache_state(x, g, count=count, m=m, overlap=ov,
+                                                         rope_dim=R, theta=1e4, W=W)
+        assert pool.shape == (count // m, D)
+        if prev is not None:
+            assert np.array_equal(pool[:len(prev)], prev)
+        prev = pool
+        L = (1 + ov) * m
+        assert rows == sorted(p % L for p in range(max(0, count - L), count))
+        for p in range(max(0, count - L), count):
+            assert np.array_equal(rx[p % L], x[p]) and np.array_equal(rg[p % L], g[p])
+        for p in range(max(0, count - W), count):
+            row = win[p % W]
+            assert np.array_equal(row[:D - R], x[p, :D - R])
+            pr = row[D - R:].reshape(-1, 2)
+            px = x[p, D - R:].reshape(-1, 2)
+            np.testing.assert_allclose(np.hypot(pr[:, 0], pr[:, 1]),
+                                       np.hypot(px[:, 0], px[:, 1]), rtol=1e-6)
+    # with no gate the entry is the window mean (as the compressor's own pin)
+    pool = orc.cache_state(x, None, count=S, m=m, overlap=0, rope_dim=0, W=0)[0]
+    np.testing.assert_allclose(pool, x[:S // m * m].reshape(-1, m, D).mean(1), rtol=1e-6,
+                               atol=1e-6)
