@@ -67,6 +67,10 @@ def work_counts(wl):
         if wl.n_idx_heads:
             gates = 2 if wl.kind != "dsa" else 1
             w["compress_idx"] = ("hbm", B * (gates * wl.ctx + wl.T) * wl.idx_dim * e)
+    if wl.decode:
+        # the new token into both caches: x and gate read, written to the
+        # compressor buffers, and (K=V) rotated into the window
+        w["cache_append"] = ("hbm", B * wl.S * (wl.D * e * 5 + wl.idx_dim * e * 4))
     if wl.n_idx_heads:
         pairs = int(R.sum()) * B
         if wl.decode:   # streams the index-key pool once: HBM-bound
@@ -196,10 +200,30 @@ def setup(wl, csa, torch, synth):
     q = gen("q", B * S, (wl.H, wl.D)).view(B, S, wl.H, wl.D)
     out = torch.empty((B, S, wl.H, wl.dv), dtype=bf, device=dev)
     if wl.decode:
+        # caches after q_pos0 tokens: pool and index keys (T entries), the
+        # sliding window as a ring (position p at row p mod W), the compressor
+        # buffers (raw rows of the last 2m tokens); the step appends the new
+        # token to both caches first (no entry closes at this position, so
+        # every step repeats the same update)
         pool = gen("pool", B * wl.T, (wl.D,)).view(B, wl.T, wl.D)
         k_idx = gen("k_idx", B * wl.T, (wl.idx_dim,)).view(B, wl.T, wl.idx_dim)
         kv_win = gen("kv_win", B * wl.window, (wl.D,)).view(B, wl.window, wl.D)
-        win_pos0 = torch.full((B,), wl.q_pos0 - wl.window + 1, dtype=torch.int32, device=dev)
+        win_pos0 = None
+        L = (1 + wl.overlap) * wl.m
+        ring_x = gen("ring_x", B * L, (wl.D,)).view(B, L, wl.D)
+        ring_g = gen("ring_g", B * L, (wl.D,)).view(B, L, wl.D)
+        ring_xi = gen("ring_xi", B * L, (wl.idx_dim,)).view(B, L, wl.idx_dim)
+        ring_gi = gen("ring_gi", B * L, (wl.idx_dim,)).view(B, L, wl.idx_dim)
+        x_new = gen("x_new", B, (1, wl.D)).view(B, 1, wl.D)
+        g_new = gen("g_new", B, (1, wl.D)).view(B, 1, wl.D)
+        xi_new = gen("xi_new", B, (1, wl.idx_dim)).view(B, 1, wl.idx_dim)
+        gi_new = gen("gi_new", B, (1, wl.idx_dim)).view(B, 1, wl.idx_dim)
+        count = torch.full((B,), wl.q_pos0, dtype=torch.int32, device=dev)
+        r.add("cache_append", lambda: (
+            csa.csa_cache_append(x_new, g_new, None, count, ring_x, ring_g, pool, kv_win,
+                                 m=wl.m, overlap=wl.overlap, rope_dim=wl.rope_dim, cs=cs),
+            csa.csa_cache_append(xi_new, gi_new, None, count, ring_xi, ring_gi, k_idx, None,
+                                 m=wl.m, overlap=wl.overlap)))
     else:
         x = gen("x", B * wl.ctx, (wl.D,)).view(B, wl.ctx, wl.D)
         kv_win = torch.empty_like(x)

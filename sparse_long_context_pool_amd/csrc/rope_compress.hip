@@ -348,21 +348,14 @@ __global__ __launch_bounds__(256) void compress_rows_kernel(
 // count/m to (count+n)/m - 1; window row j comes from x when the call brings
 // it (j >= count), else from the ring.  Pooled as the compressor pools them:
 // per channel the max of the logits, the weights, the weighted sum.
+// entry w of sequence b, channels [8ch, 8ch + 8)
 template <bool BF16>
-__global__ __launch_bounds__(256) void cache_entries_kernel(
+__device__ __forceinline__ void cache_entry(
     const void* __restrict__ x, const void* __restrict__ gate,
     const float* __restrict__ slot_bias, const void* __restrict__ ring_x,
-    const void* __restrict__ ring_g, void* __restrict__ pool, const int* __restrict__ count,
-    int n, int D, int m, int overlap, int T_cap, int E, int rope_dim,
-    const float2* __restrict__ cs, int n_pos) {
-  const int nchunk = D >> 3;
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  const int b = blockIdx.y;
-  if (i >= E * nchunk) return;
-  const int e = i / nchunk, ch = i - e * nchunk;
-  const long c0 = count[b];
-  const long w = c0 / m + e;
-  if (c0 < 0 || w >= (c0 + n) / m || w >= T_cap) return;
+    const void* __restrict__ ring_g, void* __restrict__ pool, int b, long c0, long w, int ch,
+    int n, int D, int m, int overlap, int T_cap, int rope_dim, const float2* __restrict__ cs,
+    int n_pos) {
   const int L = (1 + overlap) * m;
   const long first = (w - overlap) * m;             // token held by slot 0
   const long j0 = first < 0 ? 0 : first, j1 = (w + 1) * m;
@@ -420,21 +413,13 @@ __global__ __launch_bounds__(256) void cache_entries_kernel(
   store8<BF16>(pool, ((long)b * T_cap + w) * D + ch * 8, val);
 }
 
-// Pass 2 (after pass 1, which reads the ring): the call's last L tokens into
-// the ring, its last W tokens, rotated at their positions, into the window.
+// token k of this call (position p) of sequence b into the ring (if it is
+// among the call's last L) and the window (if among the last W)
 template <bool BF16>
-__global__ __launch_bounds__(256) void cache_tokens_kernel(
+__device__ __forceinline__ void cache_token(
     const void* __restrict__ x, const void* __restrict__ gate, void* __restrict__ ring_x,
-    void* __restrict__ ring_g, void* __restrict__ win, const int* __restrict__ count, int n,
+    void* __restrict__ ring_g, void* __restrict__ win, int b, long p, int k, int ch, int n,
     int D, int L, int W, int rope_dim, const float2* __restrict__ cs, int n_pos) {
-  const int nchunk = D >> 3;
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  const int b = blockIdx.y;
-  if (i >= n * nchunk) return;
-  const int k = i / nchunk, ch = i - k * nchunk;
-  const long c0 = count[b];
-  if (c0 < 0) return;
-  const long p = c0 + k;
   const long src = ((long)b * n + k) * D + ch * 8;
   float v[8];
   load8<BF16>(x, src, v);
@@ -458,6 +443,69 @@ __global__ __launch_bounds__(256) void cache_tokens_kernel(
     }
     store8<BF16>(win, ((long)b * W + p % W) * D + ch * 8, v);
   }
+}
+
+// Pass 1: the entries whose window closes within the call, w from count/m
+// to (count+n)/m - 1; window row j comes from x when the call brings it
+// (j >= count), else from the ring.  Pooled as the compressor pools them: per
+// channel the max of the logits, the weights, the weighted sum.
+template <bool BF16>
+__global__ __launch_bounds__(256) void cache_entries_kernel(
+    const void* __restrict__ x, const void* __restrict__ gate,
+    const float* __restrict__ slot_bias, const void* __restrict__ ring_x,
+    const void* __restrict__ ring_g, void* __restrict__ pool, const int* __restrict__ count,
+    int n, int D, int m, int overlap, int T_cap, int E, int rope_dim,
+    const float2* __restrict__ cs, int n_pos) {
+  const int nchunk = D >> 3;
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  const int b = blockIdx.y;
+  if (i >= E * nchunk) return;
+  const int e = i / nchunk, ch = i - e * nchunk;
+  const long c0 = count[b];
+  const long w = c0 / m + e;
+  if (c0 < 0 || w >= (c0 + n) / m || w >= T_cap) return;
+  cache_entry<BF16>(x, gate, slot_bias, ring_x, ring_g, pool, b, c0, w, ch, n, D, m, overlap,
+                    T_cap, rope_dim, cs, n_pos);
+}
+
+// Pass 2 (after pass 1, which reads the ring): the call's last L tokens into
+// the ring, its last W tokens, rotated at their positions, into the window.
+template <bool BF16>
+__global__ __launch_bounds__(256) void cache_tokens_kernel(
+    const void* __restrict__ x, const void* __restrict__ gate, void* __restrict__ ring_x,
+    void* __restrict__ ring_g, void* __restrict__ win, const int* __restrict__ count, int n,
+    int D, int L, int W, int rope_dim, const float2* __restrict__ cs, int n_pos) {
+  const int nchunk = D >> 3;
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  const int b = blockIdx.y;
+  if (i >= n * nchunk) return;
+  const int k = i / nchunk, ch = i - k * nchunk;
+  const long c0 = count[b];
+  if (c0 < 0) return;
+  cache_token<BF16>(x, gate, ring_x, ring_g, win, b, c0 + k, k, ch, n, D, L, W, rope_dim, cs,
+                    n_pos);
+}
+
+// One token per sequence (decode): both passes in one kernel.  The thread of
+// a chunk pools its entry (if the token closes one) before it overwrites the
+// ring row of the token L positions back, which that entry does not read.
+template <bool BF16>
+__global__ __launch_bounds__(256) void cache_one_kernel(
+    const void* __restrict__ x, const void* __restrict__ gate,
+    const float* __restrict__ slot_bias, void* __restrict__ ring_x, void* __restrict__ ring_g,
+    void* __restrict__ pool, void* __restrict__ win, const int* __restrict__ count, int D,
+    int m, int overlap, int T_cap, int W, int rope_dim, const float2* __restrict__ cs,
+    int n_pos) {
+  const int ch = blockIdx.x * blockDim.x + threadIdx.x;
+  const int b = blockIdx.y;
+  if (ch >= (D >> 3)) return;
+  const long c0 = count[b];
+  if (c0 < 0) return;
+  if ((c0 + 1) % m == 0 && (c0 + 1) / m - 1 < T_cap)
+    cache_entry<BF16>(x, gate, slot_bias, ring_x, ring_g, pool, b, c0, (c0 + 1) / m - 1, ch, 1,
+                      D, m, overlap, T_cap, rope_dim, cs, n_pos);
+  cache_token<BF16>(x, gate, ring_x, ring_g, win, b, c0, 0, ch, 1, D, (1 + overlap) * m, W,
+                    rope_dim, cs, n_pos);
 }
 
 }  // namespace
@@ -538,6 +586,18 @@ hipError_t launch_cache_append(const void* x, const void* gate, const float* slo
                                bool bf16, hipStream_t s) {
   if (B == 0 || n == 0) return hipSuccess;
   const int nchunk = D / 8;
+  if (n == 1) {
+    const dim3 g((unsigned)((nchunk + 255) / 256), (unsigned)B);
+    if (bf16)
+      hipLaunchKernelGGL(cache_one_kernel<true>, g, dim3(256), 0, s, x, gate, slot_bias, ring_x,
+                         ring_g, pool, win, count, D, m, overlap, T_cap, W, rope_dim,
+                         reinterpret_cast<const float2*>(cs), n_pos);
+    else
+      hipLaunchKernelGGL(cache_one_kernel<false>, g, dim3(256), 0, s, x, gate, slot_bias,
+                         ring_x, ring_g, pool, win, count, D, m, overlap, T_cap, W, rope_dim,
+                         reinterpret_cast<const float2*>(cs), n_pos);
+    return hipGetLastError();
+  }
   const int E = n / m + 2;  // entries that can close within n tokens, and spare
   const float2* cs2 = reinterpret_cast<const float2*>(cs);
   const dim3 g1((unsigned)((E * nchunk + 255) / 256), (unsigned)B);

@@ -22,6 +22,9 @@ TID = {
     "q": 1, "x": 2, "gate": 3, "x_idx": 4, "gate_idx": 5, "q_idx": 6, "w_idx": 7,
     "sink": 8, "pool": 9, "k_idx": 10, "kv_win": 11, "slot_bias": 12,
     "slot_bias_idx": 13, "scores": 14,
+    # decode caches: compressor buffers and the step's new token
+    "ring_x": 15, "ring_g": 16, "ring_xi": 17, "ring_gi": 18, "x_new": 19, "g_new": 20,
+    "xi_new": 21, "gi_new": 22,
 }
 
 

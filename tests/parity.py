@@ -156,9 +156,14 @@ def gpu_pipeline(wl: Workload, inp: Inputs, ops, keep_intermediates=True):
     if wl.decode:
         pool = inp.get_torch("pool").view(B, wl.T, wl.D)
         k_idx = inp.get_torch("k_idx").view(B, wl.T, wl.idx_dim)
-        kv_win = inp.get_torch("kv_win").view(B, wl.window, wl.D)
-        win_pos0 = torch.full((B,), wl.q_pos0 - wl.window + 1, dtype=torch.int32,
-                              device="cuda")
+        # the window as the decode cache keeps it (and the benchmark reads it):
+        # a ring, position p at row p mod W; the rows are the synthetic window
+        # rows of positions q_pos0 - W + 1 .. q_pos0, moved to their ring rows
+        lin = inp.get_torch("kv_win").view(B, wl.window, wl.D)
+        kv_win = torch.roll(lin, shifts=(wl.q_pos0 - wl.window + 1) % wl.window,
+                            dims=1).contiguous()
+        del lin
+        win_pos0 = None
     else:
         x = inp.get_torch("x").view(B, wl.ctx, wl.D)
         kv_win = ops.csa_compress(x, m=1, overlap=0, rope_dim=wl.rope_dim, cs=cs, pos0=0)
