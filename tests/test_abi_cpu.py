@@ -87,6 +87,35 @@ def test_invalid_arguments_are_rejected_on_the_host(L):
     assert L.csa_compress(nul, nul, nul, nul, 1, 3, 16, 4, 1, 0, nul, 0, 0, 1, nul) == 0
 
 
+def test_cache_append_rejects_bad_arguments_on_the_host(L):
+    nul = None
+    fake = ctypes.c_void_p(0x10000)
+
+    def call(x=fake, gate=nul, ring_x=fake, ring_g=nul, pool=fake, win=nul, count=fake, B=2,
+             n=1, D=64, m=4, ov=1, T_cap=8, W=0, R=0, cs=nul, n_pos=0, dt=1):
+        return L.csa_cache_append(x, gate, nul, ring_x, ring_g, pool, win, count, B, n, D, m,
+                                  ov, T_cap, W, R, cs, n_pos, dt, nul)
+    assert call(dt=5) == 1 and b"dtype" in L.csa_last_error()
+    assert call(D=60) == 1                                   # D % 8
+    assert call(m=0) == 1 and b"bad sizes" in L.csa_last_error()
+    assert call(m=200, ov=1) == 2                            # window of 400 rows
+    assert call(gate=fake) == 1 and b"gate and ring_g" in L.csa_last_error()
+    assert call(W=8) == 1 and b"win" in L.csa_last_error()
+    assert call(count=nul) == 1 and b"required" in L.csa_last_error()
+    assert call(R=16) == 1 and b"RoPE table" in L.csa_last_error()
+    assert call(pool=ctypes.c_void_p(0x10004)) == 1 and b"aligned" in L.csa_last_error()
+    assert call(n=0) == 0                                    # nothing to append
+
+
+def test_ring_window_must_cover_every_row(L):
+    fake = ctypes.c_void_p(0x10000)
+    # window 8, S = 4 query rows: a ring (win_pos0 NULL) needs L_win >= 11
+    args = [fake, fake, None, 10, fake, 4, fake, 2, None, fake, fake, 1, 4, 4, 64, 64, 16,
+            fake, 100, 8, ctypes.c_float(0.125), None, ctypes.c_size_t(0), 1, None]
+    assert L.csa_sparse_attn(*args) == 1
+    assert b"ring window" in L.csa_last_error()
+
+
 def test_workspace_plans(L):
     # decode shape: few rows, many keys -> split over workgroups, workspace > 0
     ws = L.csa_sparse_attn_workspace_size(64, 1, 64, 512, 512, 64, 2048, 128, 1)
