@@ -121,19 +121,18 @@ class Runner:
         """The step time (the reported value) comes from a HIP graph holding
         one whole step (every stage's launches, no host work between them):
         `warmup` untimed replays, then `steps` timed ones.  The per-stage
-        times (each kernel's roofline) come from one graph per stage,
-        replayed `steps` times with an event pair around each replay on the
-        stream the kernels run on; the host never waits inside a step, so it
-        runs ahead and no stage time holds host launch work.  `flush` (reads
-        that evict the caches) runs before every timed step, outside the
-        events."""
+        times (each kernel's roofline) come from `steps` eager steps with an
+        event pair around every stage on the stream the kernels run on; the
+        GPU first runs a spin kernel (or the cache flush) long enough for the
+        host to enqueue ahead, so no stage time holds host launch work.
+        `flush` (reads that evict the caches) runs before every timed step,
+        outside the events."""
         torch = self.torch
         for _ in range(warmup):
             for _, fn in self.stages:
                 fn()
         torch.cuda.synchronize()
         whole = self._capture([fn for _, fn in self.stages])
-        per = [(name, self._capture([fn])) for name, fn in self.stages]
         for _ in range(warmup):
             whole.replay()
         torch.cuda.synchronize()
@@ -158,19 +157,21 @@ class Runner:
                 pairs.append((s0, s1))
             torch.cuda.synchronize()
             total_ms = sum(a.elapsed_time(b) for a, b in pairs)
+        del whole
         ev = {n: [] for n, _ in self.stages}
+        if flush is None:
+            torch.cuda._sleep(1 << 22)   # a few ms of spinning: the host runs ahead
         for _ in range(steps):
             if flush is not None:
                 flush()
-            for name, g in per:
+            for name, fn in self.stages:
                 a = torch.cuda.Event(enable_timing=True)
                 b = torch.cuda.Event(enable_timing=True)
                 a.record()
-                g.replay()
+                fn()
                 b.record()
                 ev[name].append((a, b))
         torch.cuda.synchronize()
-        del whole, per
         avg = {n: float(np.mean([a.elapsed_time(b) for a, b in v])) for n, v in ev.items()}
         return total_ms / steps, avg
 
