@@ -237,6 +237,29 @@ __device__ __forceinline__ void rope8(float v[8], int ch, int rope_base, int rop
   }
 }
 
+// The same rotation in two halves: the factors of the slice's rope pairs
+// first (so their loads can go out with the data's), then the rotation.
+__device__ __forceinline__ void rope8_load(float2 rr[4], int ch, int rope_base, int rope_dim,
+                                          const float2* __restrict__ cs, long pos) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int c = ch * 8 + 2 * e;
+    rr[e] = c >= rope_base ? cs[pos * (rope_dim >> 1) + ((c - rope_base) >> 1)]
+                           : make_float2(1.f, 0.f);
+  }
+}
+__device__ __forceinline__ void rope8_apply(float v[8], const float2 rr[4], int ch,
+                                            int rope_base) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    if (ch * 8 + 2 * e >= rope_base) {
+      const float a0 = v[2 * e], a1 = v[2 * e + 1];
+      v[2 * e] = a0 * rr[e].x - a1 * rr[e].y;
+      v[2 * e + 1] = a0 * rr[e].y + a1 * rr[e].x;
+    }
+  }
+}
+
 // m = 1 without overlap, gate or slot bias: the window of an entry is its own
 // token, whose softmax weight is exactly 1, so the entry is the token with
 // its rope slice rotated at pos0 + w.  A streaming pass: thread i takes the
@@ -254,20 +277,28 @@ __global__ __launch_bounds__(256) void rope_copy_kernel(
   const unsigned q = (n + kCopyUnroll - 1) / kCopyUnroll;
   const unsigned i0 = blockIdx.x * blockDim.x + threadIdx.x;
   if (i0 >= q) return;
+  const int rope_base = D - rope_dim;
   float v[kCopyUnroll][8];
+  float2 rr[kCopyUnroll][4];
+  bool rot[kCopyUnroll];
 #pragma unroll
   for (int u = 0; u < kCopyUnroll; ++u) {
     const unsigned i = i0 + u * q;
-    if (i < n) load8<BF16>(x, (long)i * 8, v[u]);   // row r, chunk c: element 8 (r D/8 + c)
+    rot[u] = false;
+    if (i < n) {
+      load8<BF16>(x, (long)i * 8, v[u]);   // row r, chunk c: element 8 (r D/8 + c)
+      const unsigned r = i / nchunk;
+      const int ch = (int)(i - r * nchunk);
+      rot[u] = ch * 8 + 8 > rope_base;
+      if (rot[u])
+        rope8_load(rr[u], ch, rope_base, rope_dim, cs, (long)pos0 + (long)(r % (unsigned)S));
+    }
   }
-  const int rope_base = D - rope_dim;
 #pragma unroll
   for (int u = 0; u < kCopyUnroll; ++u) {
     const unsigned i = i0 + u * q;
     if (i < n) {
-      const unsigned r = i / nchunk;
-      const int ch = (int)(i - r * nchunk);
-      rope8(v[u], ch, rope_base, rope_dim, cs, (long)pos0 + (long)(r % (unsigned)S));
+      if (rot[u]) rope8_apply(v[u], rr[u], (int)((i0 + u * q) % nchunk), rope_base);
       store8<BF16>(pool, (long)i * 8, v[u]);
     }
   }
@@ -295,6 +326,10 @@ __global__ __launch_bounds__(256) void compress_rows_kernel(
   const long w = (long)(e - (unsigned)b * T);
   const long first = (w - overlap) * m;            // token held by slot 0
   const long row0 = (long)b * S;
+  const int rope_base = D - rope_dim;
+  const bool rot = ch * 8 + 8 > rope_base;
+  float2 rr[4];
+  if (rot) rope8_load(rr, ch, rope_base, rope_dim, cs, (long)pos0 + w * m);
   float xv[NR][8], a[NR][8];
 #pragma unroll
   for (int r = 0; r < NR; ++r) {
@@ -332,7 +367,7 @@ __global__ __launch_bounds__(256) void compress_rows_kernel(
       }
     val[v] = ac / sm;
   }
-  rope8(val, ch, D - rope_dim, rope_dim, cs, (long)pos0 + w * m);
+  if (rot) rope8_apply(val, rr, ch, rope_base);
   store8<BF16>(pool, ((long)b * T + w) * D + ch * 8, val);
 }
 
