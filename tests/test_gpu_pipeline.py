@@ -10,7 +10,7 @@ import torch
 
 import oracle
 from parity import (BF16_ATOL, F32_ATOL, Inputs, assert_idx_rows_equivalent, gpu_pipeline,
-                    host, oracle_caches, oracle_rows, row_positions)
+                    host, oracle_caches, oracle_rows)
 from sparse_long_context_pool_amd.workloads import WORKLOADS
 
 pytestmark = pytest.mark.gpu
@@ -42,26 +42,31 @@ def _check_caches(wl, inp, g, caches, b):
             np.testing.assert_allclose(host(g["k_idx"][b]), k_idx, rtol=rel, atol=1e-5)
 
 
-def _compare_rows(wl, g, res, b, rows_local):
+def _compare_rows(wl, g, inp, caches, b, rows_local):
+    """Every sampled row: index sets equal up to near ties, scores within the
+    summation-order bound, and the attention output against the oracle's
+    attention over the GPU's own selection (so a row whose selection differs
+    by a near tie is still checked element by element)."""
     tol = BF16_ATOL if wl.dtype == "bf16" else F32_ATOL
-    same = np.ones(len(rows_local), bool)
+    gi = host(g["idx"][b]).astype(np.int32)[rows_local] if wl.n_idx_heads else None
+    rows = np.asarray(rows_local) + b * wl.S
+    res = oracle_rows(wl, inp, rows, caches, idx_override=gi)
     if wl.n_idx_heads:
-        gi = host(g["idx"][b]).astype(np.int32)[rows_local]
-        same = assert_idx_rows_equivalent(gi, res["idx"], res["scores"], res["t"], wl.topk,
-                                          wl.m, wl.T)
+        assert_idx_rows_equivalent(gi, res["idx"], res["scores"], res["t"], wl.topk, wl.m,
+                                   wl.T)
         # end to end, the GPU scores use the GPU's compressed index keys, which
-        # may differ from the oracle's by one bf16 ulp (2^-8 relative) per
-        # element: |dI| <= (2^-8 + 1e-5) * sum_j |w_j| sum_c |q_jc k_c|
+        # may differ from the oracle's by one bf16 ulp (at most 2^-7 relative,
+        # the compressor's own bound) per element:
+        # |dI| <= (2^-7 + 1e-5) * sum_j |w_j| sum_c |q_jc k_c|
         gs = host(g["scores"][b])[rows_local]
-        bound = (2.0 ** -8 + 1e-5) * res["abs_terms"] + 1e-6
+        bound = (2.0 ** -7 + 1e-5) * res["abs_terms"] + 1e-6
         for r, t in enumerate(res["t"]):
             R = oracle.ready_count(int(t), wl.m, wl.T)
             d = np.abs(gs[r, :R] - res["scores"][r, :R])
             assert np.all(d <= bound[r, :R]), (r, float(d.max()))
     go = host(g["out"][b])[rows_local]
-    err = np.abs(go[same] - res["out"][same]).max() if same.any() else 0.0
-    assert err <= tol, float(err)
-    assert same.mean() >= 0.9
+    err = float(np.abs(go - res["out"]).max())
+    assert err <= tol, err
     return err
 
 
@@ -78,7 +83,9 @@ def test_tiny_csa_f32_end_to_end(ops):
     same = assert_idx_rows_equivalent(gi, res["idx"], res["scores"], res["t"], wl.topk, wl.m,
                                       wl.T, tol=1e-5)
     assert same.mean() >= 0.99
-    err = np.abs(host(g["out"][0])[same] - res["out"][same]).max()
+    # every row's output against the oracle's attention over the GPU's selection
+    out = oracle_rows(wl, inp, rows, caches, idx_override=gi)["out"]
+    err = np.abs(host(g["out"][0]) - out).max()
     assert err <= F32_ATOL, float(err)
     # the top-k kernel alone, fed the oracle's fp32 scores, is bit-exact
     sc = torch.from_numpy(np.where(np.isfinite(res["scores"]), res["scores"], 0)).cuda()
@@ -97,12 +104,10 @@ def test_full_size_sampled(ops, name):
         seqs = [0, 1, 37, 63]
         for b in seqs:
             caches = oracle_caches(wl, inp, b)
-            res = oracle_rows(wl, inp, [b], caches)
-            _compare_rows(wl, g, res, b, [0])
+            _compare_rows(wl, g, inp, caches, b, [0])
         return
     caches = oracle_caches(wl, inp, 0)
     _check_caches(wl, inp, g, caches, 0)
     rows = _sample_rows(wl, 24)
     print(f"[{name}] oracle on {len(rows)} sampled rows", flush=True)
-    res = oracle_rows(wl, inp, rows, caches)
-    _compare_rows(wl, g, res, 0, rows)
+    _compare_rows(wl, g, inp, caches, 0, rows)

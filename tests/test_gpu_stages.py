@@ -111,7 +111,9 @@ def test_index_scores(ops, case):
 @pytest.mark.parametrize("T,k,m,qp,S", [
     (64, 16, 4, [0, 120], 37), (2048, 512, 4, [0, 6000], 70), (2048, 512, 1, [1000, 1500], 20),
     (32768, 2048, 4, [131071, 90000], 3), (40000, 2048, 1, [39990, 20000], 4),
-    (300, 300, 1, [0, 100], 9), (12000, 1024, 1, [11000, 6000], 130)])
+    (300, 300, 1, [0, 100], 9), (12000, 1024, 1, [11000, 6000], 130),
+    # 2048 < T <= 8192: the 512-thread register kernel with 16 keys per thread
+    (6000, 512, 4, [23000, 3000], 40), (8192, 2048, 1, [8000, 500], 10)])
 def test_topk_bit_exact(ops, T, k, m, qp, S):
     B = 2
     r = rng(T + k)
@@ -158,9 +160,14 @@ ATTN_CASES = {
     "hca_mfma_split": (1, 2, 64, 512, 512, 64, 520, 0, 128, 128, [70000], True, True, True),
     "dsa_mfma": (1, 150, 128, 576, 512, 64, 160, 40, 0, 1, [10], False, True, False),
     "dsa_mfma_split": (1, 24, 128, 576, 512, 64, 80, 40, 0, 1, [40], False, True, False),
-    "small_mfma_split": (2, 50, 16, 64, 64, 16, 30, 20, 16, 4, [0, 64], True, True, False),
-    "small_mfma": (1, 300, 16, 64, 64, 16, 40, 20, 16, 4, [0], True, True, False),
-    "small_mfma_latent": (1, 33, 32, 96, 64, 32, 40, 12, 0, 1, [5], False, True, False),
+    # sliding-window-only layers (no pool): hca_attn with T = 0
+    "swa_mfma": (1, 300, 64, 512, 512, 64, 0, 0, 128, 128, [5000], True, True, True),
+    "swa_mfma_split": (2, 1, 64, 512, 512, 64, 0, 0, 128, 128, [3000, 3], True, True, True),
+    "generic_swa_f32": (1, 40, 4, 64, 64, 16, 0, 0, 16, 4, [0], True, False, True),
+    # head counts and widths without a matrix-core kernel (H % 64 != 0, D = 64 / 96)
+    "generic_small_bf16": (1, 300, 16, 64, 64, 16, 40, 20, 16, 4, [0], True, True, False),
+    "generic_small_b2_bf16": (2, 50, 16, 64, 64, 16, 30, 20, 16, 4, [0, 64], True, True, False),
+    "generic_small_latent_bf16": (1, 33, 32, 96, 64, 32, 40, 12, 0, 1, [5], False, True, False),
     "generic_f32": (2, 45, 4, 64, 64, 16, 64, 16, 32, 4, [0, 200], True, False, False),
     "generic_bf16": (1, 30, 6, 40, 40, 8, 20, 8, 8, 4, [60], True, True, False),
     "generic_hca_f32": (1, 40, 3, 32, 24, 8, 10, 0, 5, 4, [0], False, False, True),
@@ -184,8 +191,9 @@ def test_attention(ops, name):
     zd = dev(z, torch.float32) if z is not None else None
     scale = 1.0 / math.sqrt(D)
     if dense:
-        out = ops.hca_attn(dev(q, dt), kvd, win_pos0, dev(pool, dt), zd, q_pos, m=m,
-                           rope_dim=rope, cs=cs, window=window, scale=scale, dv=dv)
+        # (T = 0: a sliding-window-only layer, no pool at all)
+        out = ops.hca_attn(dev(q, dt), kvd, win_pos0, dev(pool, dt) if T else None, zd, q_pos,
+                           m=m, rope_dim=rope, cs=cs, window=window, scale=scale, dv=dv)
     else:
         out = ops.csa_sparse_attn(dev(q, dt), kvd, win_pos0, dev(pool, dt), dev(idx, torch.int32),
                                   zd, q_pos, rope_dim=rope, cs=cs, window=window, scale=scale,

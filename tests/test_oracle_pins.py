@@ -174,6 +174,31 @@ def test_index_score_weights_linear_and_heads_additive(orc):
     np.testing.assert_allclose(sp[fin], s[fin], rtol=1e-5, atol=1e-5)
 
 
+def test_index_score_signed_weights_against_float64(orc):
+    """Several heads with weights of both signs, against the score written out
+    in float64 numpy: the head weight multiplies the ReLU'd dot product (a
+    negative weight makes a head's positive match lower the score; the ReLU
+    acts on the dot product alone, before the weight)."""
+    r = rng(23)
+    n, nI, cI, T = 9, 6, 32, 24
+    q = r.standard_normal((n, nI, cI)).astype(np.float32)
+    w = r.standard_normal((n, nI)).astype(np.float32)
+    w[:, 0] = -np.abs(w[:, 0]) - 0.5            # at least one negative head per row
+    w[:, 1] = np.abs(w[:, 1]) + 0.5             # and one positive
+    k = r.standard_normal((T, cI)).astype(np.float32)
+    t = np.array([95, 94, 40, 11, 7, 3, 60, 33, 200])
+    s = orc.index_scores(q, w, t, k, m=4)
+    dots = np.einsum("njc,wc->njw", q.astype(np.float64), k.astype(np.float64))
+    ref = np.einsum("nj,njw->nw", w.astype(np.float64), np.maximum(dots, 0.0))
+    for i in range(n):
+        R = brute.ready(int(t[i]), 4, T)
+        np.testing.assert_allclose(s[i, :R], ref[i, :R], rtol=1e-5, atol=1e-5)
+    # the data really separates the two orderings: w * ReLU(dot) differs from
+    # ReLU(w * dot) on many ready entries
+    alt = np.maximum(w.astype(np.float64)[:, :, None] * dots, 0.0).sum(1)
+    assert np.mean(np.abs(alt - ref) > 1e-2) > 0.5
+
+
 @pytest.mark.parametrize("cI", [32, 128])
 def test_index_score_hadamard_invariance(orc, cI):
     """An orthonormal transform applied to both q and k leaves the scores
@@ -436,6 +461,10 @@ def test_cache_state_is_causal_and_holds_the_last_tokens(orc):
         for p in range(max(0, count - W), count):
             row = win[p % W]
             assert np.array_equal(row[:D - R], x[p, :D - R])
+            # rotated at exactly its own position p (complex multiplication,
+            # written independently of the oracle's rotation)
+            np.testing.assert_allclose(row, brute.rope_complex(x[p], R, 1e4, p, +1),
+                                       rtol=1e-5, atol=1e-5)
             pr = row[D - R:].reshape(-1, 2)
             px = x[p, D - R:].reshape(-1, 2)
             np.testing.assert_allclose(np.hypot(pr[:, 0], pr[:, 1]),
@@ -444,3 +473,10 @@ def test_cache_state_is_causal_and_holds_the_last_tokens(orc):
     pool = orc.cache_state(x, None, count=S, m=m, overlap=0, rope_dim=0, W=0)[0]
     np.testing.assert_allclose(pool, x[:S // m * m].reshape(-1, m, D).mean(1), rtol=1e-6,
                                atol=1e-6)
+    # with no gate and RoPE, entry w is the mean of its (overlapping) window
+    # rotated at w m: positions count from the sequence's first token
+    pool = orc.cache_state(x, None, count=S, m=m, overlap=1, rope_dim=R, theta=1e4, W=0)[0]
+    for w in range(S // m):
+        lo = max(0, (w - 1) * m)
+        ref = brute.rope_complex(x[lo:(w + 1) * m].astype(np.float64).mean(0), R, 1e4, w * m)
+        np.testing.assert_allclose(pool[w], ref, rtol=1e-5, atol=1e-5)
