@@ -79,6 +79,27 @@ csa_status_t csa_rope_table(float *cs, int32_t n_pos, int32_t rope_dim, double t
                             void *stream);
 
 /*
+ * csa_rope_table_yarn -- the same table with YaRN-scaled frequencies.  Page
+ * "DeepSeek-V4", DeepseekV4Config (compress_rope_theta is used together with
+ * rope scaling for YaRN; rope_parameters carry the scaling for a longer
+ * max_position_embeddings).  The pages name the method only; the frequencies
+ * follow the published YaRN "NTK-by-parts" rule in its per-pair-index form:
+ * with f_i = theta^(-2i/rope_dim) and i(r) = rope_dim ln(L / (2 pi r)) /
+ * (2 ln theta) (L = original_max_pos), low = max(floor(i(beta_fast)), 0),
+ * high = min(ceil(i(beta_slow)), rope_dim - 1) (+0.001 if equal),
+ * ramp_i = clamp((i - low) / (high - low), 0, 1) and pair i turns at
+ *   f'_i = (f_i / factor) ramp_i + f_i (1 - ramp_i),
+ * i.e. fast pairs keep their frequency and slow pairs are stretched by the
+ * factor.  The table stays a pure rotation (|cs[p][i]| = 1); YaRN's logit
+ * temperature, a scalar, is the caller's to fold into the attention scale.
+ * With factor = 1 the table equals csa_rope_table's.
+ *   factor >= 1, original_max_pos >= 1, beta_fast > beta_slow > 0, theta > 1.
+ */
+csa_status_t csa_rope_table_yarn(float *cs, int32_t n_pos, int32_t rope_dim, double theta,
+                                 double factor, int32_t original_max_pos, double beta_fast,
+                                 double beta_slow, void *stream);
+
+/*
  * csa_compress -- the compressor: pools a token stream into one entry per m
  * tokens.  Page "DeepSeek-V4", "Hybrid attention" (CSA pool at rate m with
  * overlapping windows; HCA pool at rate m' with non-overlapping windows) and

@@ -18,6 +18,9 @@ function follows the Hugging Face Transformers model pages:
 * "DeepSeek-V3.2", section "DeepSeek Sparse Attention (DSA)": token-level
   indexer (m=1) and attention over the selected tokens.
 
+* "DeepSeek-V4", DeepseekV4Config: compress_rope_theta used with rope scaling
+  for YaRN (``yarn_freqs``: the published YaRN frequency interpolation).
+
 Functions without a pin on the pages are marked "parity unpinned" in
 ``csa_oracle.c``'s header (the ReLU of the index score, the compressor's gating
 form, the pool RoPE position, theta per layer, the softmax scale).
@@ -67,13 +70,16 @@ def _load():
         lib.orc_round_bf16.restype = cf
         lib.orc_round_bf16_array.argtypes = [f32p, cl]
         lib.orc_round_bf16_array.restype = None
-        lib.orc_rope_table.argtypes = [f32p, ci, ci, cd]
-        lib.orc_rope_table.restype = None
-        lib.orc_rope_apply.argtypes = [f32p, cl, ci, ci, cd, i64p, ci]
-        lib.orc_rope_apply.restype = None
-        lib.orc_compress.argtypes = [f32p, f32p, f32p, f32p, ci, ci, ci, ci, ci,
-                                     cd, cl, ci]
-        lib.orc_compress.restype = ci
+        f64p = ctypes.POINTER(ctypes.c_double)
+        lib.orc_rope_table_f.argtypes = [f32p, ci, ci, cd, f64p]
+        lib.orc_rope_table_f.restype = None
+        lib.orc_yarn_freqs.argtypes = [f64p, ci, cd, cd, cl, cd, cd]
+        lib.orc_yarn_freqs.restype = None
+        lib.orc_rope_apply_f.argtypes = [f32p, cl, ci, ci, cd, f64p, i64p, ci]
+        lib.orc_rope_apply_f.restype = None
+        lib.orc_compress_f.argtypes = [f32p, f32p, f32p, f32p, ci, ci, ci, ci, ci,
+                                       cd, f64p, cl, ci]
+        lib.orc_compress_f.restype = ci
         lib.orc_ready_count.argtypes = [cl, ci, ci]
         lib.orc_ready_count.restype = cl
         lib.orc_index_scores.argtypes = [f32p, f32p, i64p, ci, f32p, ci, ci, ci,
@@ -81,10 +87,10 @@ def _load():
         lib.orc_index_scores.restype = ci
         lib.orc_topk.argtypes = [f32p, i64p, ci, ci, ci, ci, i32p]
         lib.orc_topk.restype = ci
-        lib.orc_attention.argtypes = [f32p, i64p, ci, ci, ci, ci, f32p, cl, ci,
-                                      ci, f32p, ci, i32p, ci, ci, f32p, ci, cd,
-                                      cf, f32p]
-        lib.orc_attention.restype = ci
+        lib.orc_attention_f.argtypes = [f32p, i64p, ci, ci, ci, ci, f32p, cl, ci,
+                                        ci, f32p, ci, i32p, ci, ci, f32p, ci, cd,
+                                        f64p, cf, f32p]
+        lib.orc_attention_f.restype = ci
         _lib = lib
     return _lib
 
@@ -113,25 +119,47 @@ def round_bf16(a) -> np.ndarray:
     return out
 
 
-def rope_table(n_pos: int, rope_dim: int, theta: float) -> np.ndarray:
-    """cs[p, i, 0/1] = cos/sin(p * theta**(-2i/rope_dim)), fp64 angle, fp32 store."""
+def _freqs(freqs, rope_dim):
+    if freqs is None:
+        return None
+    f = np.ascontiguousarray(freqs, dtype=np.float64)
+    assert f.shape == (rope_dim // 2,)
+    return f
+
+
+def yarn_freqs(rope_dim: int, theta: float, factor: float, original_max_pos: int,
+               beta_fast: float = 32.0, beta_slow: float = 1.0) -> np.ndarray:
+    """Per-pair YaRN frequencies (fp64), see orc_yarn_freqs in csa_oracle.c."""
+    f = np.empty(rope_dim // 2, dtype=np.float64)
+    _load().orc_yarn_freqs(_ptr(f, ctypes.c_double), rope_dim, float(theta), float(factor),
+                           int(original_max_pos), float(beta_fast), float(beta_slow))
+    return f
+
+
+def rope_table(n_pos: int, rope_dim: int, theta: float, freqs=None) -> np.ndarray:
+    """cs[p, i, 0/1] = cos/sin(p * f_i), f_i = theta**(-2i/rope_dim) or freqs[i];
+    fp64 angle, fp32 store."""
     cs = np.empty((n_pos, rope_dim // 2, 2), dtype=np.float32)
-    _load().orc_rope_table(_ptr(cs), n_pos, rope_dim, float(theta))
+    f = _freqs(freqs, rope_dim)
+    _load().orc_rope_table_f(_ptr(cs), n_pos, rope_dim, float(theta),
+                             _ptr(f, ctypes.c_double))
     return cs
 
 
-def rope_apply(v, rope_dim: int, theta: float, pos, sign: int = +1) -> np.ndarray:
+def rope_apply(v, rope_dim: int, theta: float, pos, sign: int = +1,
+               freqs=None) -> np.ndarray:
     """Rotate the trailing rope_dim channels of the last axis of v.
 
     pos is a scalar or one position per leading row of v; sign=-1 rotates
-    at -pos."""
+    at -pos; freqs: per-pair frequencies (None: theta**(-2i/rope_dim))."""
     v = _f32(v).copy()
     D = v.shape[-1]
     flat = v.reshape(-1, D)
     pos = np.broadcast_to(np.asarray(pos, dtype=np.int64), (flat.shape[0],))
     pos = np.ascontiguousarray(pos)
-    _load().orc_rope_apply(_ptr(flat), flat.shape[0], D, rope_dim, float(theta),
-                           _ptr(pos, ctypes.c_long), int(sign))
+    f = _freqs(freqs, rope_dim)
+    _load().orc_rope_apply_f(_ptr(flat), flat.shape[0], D, rope_dim, float(theta),
+                             _ptr(f, ctypes.c_double), _ptr(pos, ctypes.c_long), int(sign))
     return flat.reshape(v.shape)
 
 
@@ -141,7 +169,7 @@ def ready_count(t: int, m: int, T: int) -> int:
 
 def compress(x, gate=None, slot_bias=None, *, m: int, overlap: int,
              rope_dim: int = 0, theta: float = 1.0, pos0: int = 0,
-             round_bf16: bool = False) -> np.ndarray:
+             round_bf16: bool = False, freqs=None) -> np.ndarray:
     """Pool one sequence x[S, D] into [S//m, D] (see csa_oracle.c)."""
     x = _f32(x)
     S, D = x.shape
@@ -152,9 +180,10 @@ def compress(x, gate=None, slot_bias=None, *, m: int, overlap: int,
     if slot_bias is not None:
         assert slot_bias.shape == ((1 + overlap) * m, D)
     pool = np.zeros((S // m, D), dtype=np.float32)
-    rc = _load().orc_compress(_ptr(x), _ptr(gate), _ptr(slot_bias), _ptr(pool), S, D,
-                              m, overlap, rope_dim, float(theta), int(pos0),
-                              1 if round_bf16 else 0)
+    f = _freqs(freqs, rope_dim)
+    rc = _load().orc_compress_f(_ptr(x), _ptr(gate), _ptr(slot_bias), _ptr(pool), S, D,
+                                m, overlap, rope_dim, float(theta), _ptr(f, ctypes.c_double),
+                                int(pos0), 1 if round_bf16 else 0)
     _check(rc, "compress")
     return pool
 
@@ -228,7 +257,8 @@ def topk(scores, tpos, *, k: int, m: int) -> np.ndarray:
 
 def attention(q, tpos, *, kv_win=None, win_pos0: int = 0, window: int = 0,
               pool=None, idx=None, m: int = 1, sink=None, rope_dim: int = 0,
-              theta: float = 1.0, scale: float, dv: int | None = None) -> np.ndarray:
+              theta: float = 1.0, scale: float, dv: int | None = None,
+              freqs=None) -> np.ndarray:
     """q[n, H, D] at positions tpos[n] -> out[n, H, dv].
 
     idx[n, k] selects pool rows (CSA/DSA); idx=None attends every ready pool
@@ -249,10 +279,11 @@ def attention(q, tpos, *, kv_win=None, win_pos0: int = 0, window: int = 0,
         k = idx.shape[1]
     sink = _f32(sink)
     out = np.empty((n, H, dv), dtype=np.float32)
-    rc = _load().orc_attention(
+    f = _freqs(freqs, rope_dim)
+    rc = _load().orc_attention_f(
         _ptr(q), _ptr(tpos, ctypes.c_long), n, H, D, dv, _ptr(kv_win), int(win_pos0),
         L_win, int(window), _ptr(pool), T,
         None if idx is None else _ptr(idx, ctypes.c_int32), k, int(m), _ptr(sink),
-        int(rope_dim), float(theta), float(scale), _ptr(out))
+        int(rope_dim), float(theta), _ptr(f, ctypes.c_double), float(scale), _ptr(out))
     _check(rc, "attention")
     return out

@@ -70,35 +70,81 @@ void orc_round_bf16_array(float *a, long n)
  * D-rope_dim+2i+1).  Its frequency is theta^(-2i/rope_dim); the angle at
  * position p is p times that frequency.
  * ------------------------------------------------------------------------- */
+/* freq: per-pair frequencies (e.g. YaRN's, below), or NULL for the plain
+ * theta^(-2i/rope_dim). */
 static void rope_cos_sin(double theta, int rope_dim, long pos, int i,
-                         float *c, float *s)
+                         const double *freqs, float *c, float *s)
 {
-    double freq = pow(theta, -2.0 * (double)i / (double)rope_dim);
+    double freq = freqs ? freqs[i] : pow(theta, -2.0 * (double)i / (double)rope_dim);
     double angle = (double)pos * freq;
     *c = (float)cos(angle);
     *s = (float)sin(angle);
 }
 
 /* cs[p][i][0] = cos, cs[p][i][1] = sin, for p in [0, n_pos). */
-void orc_rope_table(float *cs, int n_pos, int rope_dim, double theta)
+void orc_rope_table_f(float *cs, int n_pos, int rope_dim, double theta, const double *freqs)
 {
     int half = rope_dim / 2;
     for (long p = 0; p < n_pos; ++p)
         for (int i = 0; i < half; ++i)
-            rope_cos_sin(theta, rope_dim, p, i, &cs[(p * half + i) * 2],
+            rope_cos_sin(theta, rope_dim, p, i, freqs, &cs[(p * half + i) * 2],
                          &cs[(p * half + i) * 2 + 1]);
+}
+
+void orc_rope_table(float *cs, int n_pos, int rope_dim, double theta)
+{
+    orc_rope_table_f(cs, n_pos, rope_dim, theta, NULL);
+}
+
+/* ---------------------------------------------------------------------------
+ * YaRN-scaled frequencies ([V4-CFG] compress_rope_theta is used together with
+ * rope scaling for YaRN; rope_parameters carry the scaling for a longer
+ * max_position_embeddings).  The pages name the method only; its steps here
+ * are those of the published YaRN method ("NTK-by-parts" interpolation, Peng
+ * et al. 2023) in the per-pair-index form of the Transformers RoPE utilities:
+ *   1. f_i = theta^(-2i/d) for the d/2 pairs (d = rope_dim).
+ *   2. Over the original context L a pair turns L f_i / (2 pi) times; the
+ *      (fractional) pair index at which that count equals r is
+ *      i(r) = d ln(L / (2 pi r)) / (2 ln theta).
+ *   3. low = floor(i(beta_fast)) clamped at 0, high = ceil(i(beta_slow))
+ *      clamped at d - 1; if they coincide high is moved up by 0.001.
+ *   4. ramp_i = clamp((i - low) / (high - low), 0, 1).
+ *   5. f'_i = (f_i / factor) ramp_i + f_i (1 - ramp_i): fast pairs (many
+ *      turns over L) keep their frequency, slow pairs are interpolated by the
+ *      factor, the ones between blend linearly in i.
+ * The magnitude correction YaRN also defines is a scalar on the logits and is
+ * not part of the table (the table stays a pure rotation).
+ * ------------------------------------------------------------------------- */
+void orc_yarn_freqs(double *freqs, int rope_dim, double theta, double factor,
+                    long original_max_pos, double beta_fast, double beta_slow)
+{
+    const double two_pi = 2.0 * acos(-1.0);
+    double d = (double)rope_dim;
+    double i_fast = d * log((double)original_max_pos / (two_pi * beta_fast)) / (2.0 * log(theta));
+    double i_slow = d * log((double)original_max_pos / (two_pi * beta_slow)) / (2.0 * log(theta));
+    double low = floor(i_fast), high = ceil(i_slow);
+    if (low < 0.0) low = 0.0;
+    if (high > d - 1.0) high = d - 1.0;
+    if (high == low) high += 0.001;
+    for (int i = 0; i < rope_dim / 2; ++i) {
+        double f = pow(theta, -2.0 * (double)i / d);
+        double ramp = ((double)i - low) / (high - low);
+        if (ramp < 0.0) ramp = 0.0;
+        if (ramp > 1.0) ramp = 1.0;
+        freqs[i] = (f / factor) * ramp + f * (1.0 - ramp);
+    }
 }
 
 /* Rotate the trailing rope_dim channels of v (length D) by +pos (sign=+1) or
  * by -pos (sign=-1): the pair (a, b) becomes (a*c - b*s, a*s + b*c) with
  * s = sin(sign*angle). */
-static void rope_apply(float *v, int D, int rope_dim, double theta, long pos,
-                       int sign)
+static void rope_apply(float *v, int D, int rope_dim, double theta, const double *freqs,
+                       long pos, int sign)
 {
     int base = D - rope_dim;
     for (int i = 0; i < rope_dim / 2; ++i) {
         float c, s;
-        rope_cos_sin(theta, rope_dim, pos, i, &c, &s);
+        rope_cos_sin(theta, rope_dim, pos, i, freqs, &c, &s);
         if (sign < 0) s = -s;
         float a = v[base + 2 * i];
         float b = v[base + 2 * i + 1];
@@ -111,11 +157,17 @@ static void rope_apply(float *v, int D, int rope_dim, double theta, long pos,
 
 /* Public helper so the tests can pin the rotation itself: n rows of length
  * D, row r rotated at sign*pos[r]. */
+void orc_rope_apply_f(float *v, long n, int D, int rope_dim, double theta,
+                      const double *freqs, const long *pos, int sign)
+{
+    for (long r = 0; r < n; ++r)
+        rope_apply(v + r * D, D, rope_dim, theta, freqs, pos[r], sign);
+}
+
 void orc_rope_apply(float *v, long n, int D, int rope_dim, double theta,
                     const long *pos, int sign)
 {
-    for (long r = 0; r < n; ++r)
-        rope_apply(v + r * D, D, rope_dim, theta, pos[r], sign);
+    orc_rope_apply_f(v, n, D, rope_dim, theta, NULL, pos, sign);
 }
 
 /* ---------------------------------------------------------------------------
@@ -131,9 +183,9 @@ void orc_rope_apply(float *v, long n, int D, int rope_dim, double theta,
  * Then the trailing rope_dim channels are rotated to position pos0 + w*m,
  * then the entry is rounded to bf16 if round_bf16 is set.
  * ------------------------------------------------------------------------- */
-int orc_compress(const float *x, const float *gate, const float *slot_bias,
-                 float *pool, int S, int D, int m, int overlap, int rope_dim,
-                 double theta, long pos0, int round_bf16)
+int orc_compress_f(const float *x, const float *gate, const float *slot_bias,
+                   float *pool, int S, int D, int m, int overlap, int rope_dim,
+                   double theta, const double *freqs, long pos0, int round_bf16)
 {
     if (m < 1 || S < 0 || D < 1 || (overlap != 0 && overlap != 1) ||
         rope_dim < 0 || rope_dim > D || (rope_dim & 1))
@@ -167,12 +219,20 @@ int orc_compress(const float *x, const float *gate, const float *slot_bias,
             out[c] = acc;
         }
         if (rope_dim > 0)
-            rope_apply(out, D, rope_dim, theta, pos0 + (long)w * m, +1);
+            rope_apply(out, D, rope_dim, theta, freqs, pos0 + (long)w * m, +1);
         if (round_bf16)
             for (int c = 0; c < D; ++c) out[c] = round_to_bf16(out[c]);
         free(logit);
     }
     return ORC_OK;
+}
+
+int orc_compress(const float *x, const float *gate, const float *slot_bias,
+                 float *pool, int S, int D, int m, int overlap, int rope_dim,
+                 double theta, long pos0, int round_bf16)
+{
+    return orc_compress_f(x, gate, slot_bias, pool, S, D, m, overlap, rope_dim, theta,
+                          NULL, pos0, round_bf16);
 }
 
 /* ---------------------------------------------------------------------------
@@ -300,11 +360,11 @@ int orc_topk(const float *scores, const long *tpos, int n_rows, int T, int k,
  * if dv == D the trailing rope_dim channels of o are rotated at -t.
  * A row with no visible key and no sink gives o = 0.
  * ------------------------------------------------------------------------- */
-int orc_attention(const float *q, const long *tpos, int n_rows, int H, int D,
-                  int dv, const float *kv_win, long win_pos0, int L_win,
-                  int window, const float *pool, int T, const int *idx, int k,
-                  int m, const float *sink, int rope_dim, double theta,
-                  float scale, float *out)
+int orc_attention_f(const float *q, const long *tpos, int n_rows, int H, int D,
+                    int dv, const float *kv_win, long win_pos0, int L_win,
+                    int window, const float *pool, int T, const int *idx, int k,
+                    int m, const float *sink, int rope_dim, double theta,
+                    const double *freqs, float scale, float *out)
 {
     if (H < 1 || D < 1 || (dv != D && dv != D - rope_dim) || rope_dim < 0 ||
         rope_dim > D || (rope_dim & 1) || window < 0 || m < 1 || T < 0)
@@ -341,7 +401,7 @@ int orc_attention(const float *q, const long *tpos, int n_rows, int H, int D,
             float *logit = (float *)malloc(sizeof(float) * (nk > 0 ? nk : 1));
             float *o = (float *)malloc(sizeof(float) * D);
             memcpy(qr, q + ((long)r * H + h) * D, sizeof(float) * D);
-            if (rope_dim > 0) rope_apply(qr, D, rope_dim, theta, t, +1);
+            if (rope_dim > 0) rope_apply(qr, D, rope_dim, theta, freqs, t, +1);
 
             float M = sink ? sink[h] : -INFINITY;
             for (long j = 0; j < nk; ++j) {
@@ -361,7 +421,7 @@ int orc_attention(const float *q, const long *tpos, int n_rows, int H, int D,
                     for (int c = 0; c < dv; ++c) o[c] += p * keys[j][c];
                 }
             }
-            if (dv == D && rope_dim > 0) rope_apply(o, D, rope_dim, theta, t, -1);
+            if (dv == D && rope_dim > 0) rope_apply(o, D, rope_dim, theta, freqs, t, -1);
             memcpy(out + ((long)r * H + h) * dv, o, sizeof(float) * dv);
             free(qr);
             free(logit);
@@ -370,4 +430,14 @@ int orc_attention(const float *q, const long *tpos, int n_rows, int H, int D,
         }
     }
     return ORC_OK;
+}
+
+int orc_attention(const float *q, const long *tpos, int n_rows, int H, int D,
+                  int dv, const float *kv_win, long win_pos0, int L_win,
+                  int window, const float *pool, int T, const int *idx, int k,
+                  int m, const float *sink, int rope_dim, double theta,
+                  float scale, float *out)
+{
+    return orc_attention_f(q, tpos, n_rows, H, D, dv, kv_win, win_pos0, L_win, window,
+                           pool, T, idx, k, m, sink, rope_dim, theta, NULL, scale, out);
 }

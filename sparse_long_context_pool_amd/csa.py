@@ -31,6 +31,7 @@ def lib():
             "csa_last_error": ([], ctypes.c_char_p),
             "csa_version": ([], ctypes.c_char_p),
             "csa_rope_table": ([vp, i32, i32, f64, vp], ctypes.c_int),
+            "csa_rope_table_yarn": ([vp, i32, i32, f64, f64, i32, f64, f64, vp], ctypes.c_int),
             "csa_compress": ([vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp, i32, i32,
                               i32, vp], ctypes.c_int),
             "csa_cache_append": ([vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
@@ -54,7 +55,8 @@ def lib():
     return _lib
 
 
-EXPORTS = ("csa_last_error", "csa_version", "csa_rope_table", "csa_compress",
+EXPORTS = ("csa_last_error", "csa_version", "csa_rope_table", "csa_rope_table_yarn",
+           "csa_compress",
            "csa_cache_append",
            "csa_index_scores", "csa_topk", "csa_sparse_attn",
            "csa_sparse_attn_workspace_size", "hca_attn", "hca_attn_workspace_size")
@@ -98,6 +100,19 @@ def csa_rope_table(n_pos: int, rope_dim: int, theta: float, device=None) -> torc
                      device=device or torch.device("cuda"))
     _check(lib().csa_rope_table(_ptr(cs), n_pos, rope_dim, float(theta), _stream()),
            "csa_rope_table")
+    return cs
+
+
+def csa_rope_table_yarn(n_pos: int, rope_dim: int, theta: float, factor: float,
+                        original_max_pos: int, beta_fast: float = 32.0, beta_slow: float = 1.0,
+                        device=None) -> torch.Tensor:
+    """cos/sin table [n_pos, rope_dim/2, 2] fp32 with YaRN-scaled pair frequencies."""
+    cs = torch.empty((n_pos, rope_dim // 2, 2), dtype=torch.float32,
+                     device=device or torch.device("cuda"))
+    _check(lib().csa_rope_table_yarn(_ptr(cs), n_pos, rope_dim, float(theta), float(factor),
+                                     int(original_max_pos), float(beta_fast), float(beta_slow),
+                                     _stream()),
+           "csa_rope_table_yarn")
     return cs
 
 

@@ -5,6 +5,7 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+
 #include "../../include/csa.h"
 #include "csa_device.hpp"
 
@@ -140,8 +141,30 @@ csa_status_t csa_rope_table(float* cs, int32_t n_pos, int32_t rope_dim, double t
                 "csa_rope_table: need n_pos >= 1, even rope_dim >= 2, theta > 0 "
                 "(n_pos=%d rope_dim=%d theta=%g)",
                 n_pos, rope_dim, theta);
-  return launched(csa::launch_rope_table(cs, n_pos, rope_dim, theta, as_stream(stream)),
-                  "csa_rope_table");
+  return launched(
+      csa::launch_rope_table(cs, n_pos, rope_dim, theta, 1.0, 1, 32.0, 1.0, as_stream(stream)),
+      "csa_rope_table");
+}
+
+csa_status_t csa_rope_table_yarn(float* cs, int32_t n_pos, int32_t rope_dim, double theta,
+                                 double factor, int32_t original_max_pos, double beta_fast,
+                                 double beta_slow, void* stream) {
+  if (!cs) return fail(CSA_ERR_INVALID, "csa_rope_table_yarn: cs is NULL");
+  if (n_pos < 1 || rope_dim < 2 || (rope_dim & 1) || !(theta > 1.0))
+    return fail(CSA_ERR_INVALID,
+                "csa_rope_table_yarn: need n_pos >= 1, even rope_dim >= 2, theta > 1 "
+                "(n_pos=%d rope_dim=%d theta=%g)",
+                n_pos, rope_dim, theta);
+  if (!(factor >= 1.0) || original_max_pos < 1 || !(beta_slow > 0.0) ||
+      !(beta_fast > beta_slow))
+    return fail(CSA_ERR_INVALID,
+                "csa_rope_table_yarn: need factor >= 1, original_max_pos >= 1 and "
+                "beta_fast > beta_slow > 0 (factor=%g original_max_pos=%d beta_fast=%g "
+                "beta_slow=%g)",
+                factor, original_max_pos, beta_fast, beta_slow);
+  return launched(csa::launch_rope_table(cs, n_pos, rope_dim, theta, factor, original_max_pos,
+                                         beta_fast, beta_slow, as_stream(stream)),
+                  "csa_rope_table_yarn");
 }
 
 csa_status_t csa_compress(const void* x, const void* gate, const float* slot_bias,

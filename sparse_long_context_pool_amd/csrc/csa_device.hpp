@@ -137,8 +137,9 @@ __device__ __forceinline__ float xgroup_sum(float v) {
 // Each returns hipSuccess or the launch error.
 namespace csa {
 
-hipError_t launch_rope_table(float* cs, int n_pos, int rope_dim, double theta,
-                             hipStream_t s);
+// factor <= 1: plain RoPE; factor > 1: YaRN-scaled frequencies
+hipError_t launch_rope_table(float* cs, int n_pos, int rope_dim, double theta, double factor,
+                             int orig_len, double beta_fast, double beta_slow, hipStream_t s);
 
 hipError_t launch_compress(const void* x, const void* gate, const float* slot_bias,
                            void* pool, int B, int S, int D, int m, int overlap,

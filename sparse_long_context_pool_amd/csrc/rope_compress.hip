@@ -24,16 +24,46 @@
 namespace csa {
 namespace {
 
+// Frequency scaling of the table.  factor <= 1: plain RoPE, pair i turns at
+// theta^(-2i/d).  factor > 1: YaRN (DeepseekV4Config: compress_rope_theta is
+// used together with rope scaling for YaRN; the method's published
+// "NTK-by-parts" rule): over the original context L pair i turns
+// L f_i / (2 pi) times, which is r turns at the fractional pair index
+// i(r) = d ln(L / (2 pi r)) / (2 ln theta); pairs up to low = floor(i(beta_fast))
+// keep f_i, pairs from high = ceil(i(beta_slow)) run at f_i / factor, and the
+// pairs between blend the two with a weight linear in i.  Only the angle
+// changes: the table stays a pure rotation.
+struct RopeScaling {
+  double factor;               // <= 1: plain RoPE
+  double orig_len, beta_fast, beta_slow;
+};
+
 __global__ __launch_bounds__(256) void rope_table_kernel(float2* __restrict__ cs, int n_pos,
-                                                         int rope_dim, double theta) {
+                                                         int rope_dim, double theta,
+                                                         RopeScaling sc) {
   const int half = rope_dim / 2;
   const long n = (long)n_pos * half;
+  const double d = (double)rope_dim;
+  const bool yarn = sc.factor > 1.0;
+  double low = 0.0, high = 1.0;
+  if (yarn) {
+    // (every thread forms the two ramp ends itself: fp64 logs, once)
+    const double two_pi = 6.283185307179586;
+    low = fmax(floor(d * log(sc.orig_len / (two_pi * sc.beta_fast)) / (2.0 * log(theta))), 0.0);
+    high = fmin(ceil(d * log(sc.orig_len / (two_pi * sc.beta_slow)) / (2.0 * log(theta))),
+                d - 1.0);
+    if (high == low) high += 0.001;
+  }
   for (long e = blockIdx.x * (long)blockDim.x + threadIdx.x; e < n;
        e += (long)gridDim.x * blockDim.x) {
     const long p = e / half;
     const int i = (int)(e - p * half);
-    const double freq = pow(theta, -2.0 * (double)i / (double)rope_dim);
-    const double ang = (double)p * freq;
+    double f = pow(theta, -2.0 * (double)i / d);
+    if (yarn) {
+      const double ramp = fmin(fmax(((double)i - low) / (high - low), 0.0), 1.0);
+      f = (f / sc.factor) * ramp + f * (1.0 - ramp);
+    }
+    const double ang = (double)p * f;
     cs[e] = make_float2((float)cos(ang), (float)sin(ang));
   }
 }
@@ -545,13 +575,14 @@ __global__ __launch_bounds__(256) void cache_one_kernel(
 
 }  // namespace
 
-hipError_t launch_rope_table(float* cs, int n_pos, int rope_dim, double theta,
-                             hipStream_t s) {
+hipError_t launch_rope_table(float* cs, int n_pos, int rope_dim, double theta, double factor,
+                             int orig_len, double beta_fast, double beta_slow, hipStream_t s) {
   const long n = (long)n_pos * (rope_dim / 2);
   long blocks = (n + 255) / 256;
   if (blocks > 65536) blocks = 65536;
+  RopeScaling sc{factor, (double)orig_len, beta_fast, beta_slow};
   hipLaunchKernelGGL(rope_table_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
-                     reinterpret_cast<float2*>(cs), n_pos, rope_dim, theta);
+                     reinterpret_cast<float2*>(cs), n_pos, rope_dim, theta, sc);
   return hipGetLastError();
 }
 

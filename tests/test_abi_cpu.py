@@ -47,6 +47,11 @@ def test_library_exports_every_declared_symbol(L):
 
 def test_invalid_arguments_are_rejected_on_the_host(L):
     nul = None
+    # YaRN table: factor below 1, beta_fast not above beta_slow
+    dummy = ctypes.c_void_p(16)
+    assert L.csa_rope_table_yarn(dummy, 10, 64, 1e4, 0.5, 4096, 32.0, 1.0, nul) == 1
+    assert b"factor" in L.csa_last_error()
+    assert L.csa_rope_table_yarn(dummy, 10, 64, 1e4, 4.0, 4096, 1.0, 1.0, nul) == 1
     # unknown dtype
     assert L.csa_compress(nul, nul, nul, nul, 1, 8, 8, 4, 1, 0, nul, 0, 0, 7, nul) == 1
     assert b"dtype" in L.csa_last_error()

@@ -40,6 +40,49 @@ def test_rope_table(ops, theta, rope_dim):
     assert np.max(np.abs(g - o)) <= 1.2e-7
 
 
+@pytest.mark.parametrize("factor,orig,theta,rope_dim", [
+    (16.0, 65536, 160000.0, 64), (4.0, 4096, 10000.0, 64), (1.0, 65536, 160000.0, 64),
+    (40.0, 4096, 10000.0, 128)])
+def test_rope_table_yarn(ops, factor, orig, theta, rope_dim):
+    n = 131073
+    g = host(ops.csa_rope_table_yarn(n, rope_dim, theta, factor, orig, 32.0, 1.0))
+    o = oracle.rope_table(n, rope_dim, theta,
+                          freqs=oracle.yarn_freqs(rope_dim, theta, factor, orig, 32.0, 1.0))
+    assert np.max(np.abs(g - o)) <= 1.2e-7
+
+
+def test_attention_with_yarn_table(ops):
+    """The attention kernels take every angle from the table: a CSA case on the
+    matrix-core kernel with a YaRN table (16x extension) against the oracle
+    with the same frequencies."""
+    B, S, H, D, dv, rope, T, k, window, m, qp, sink, bf16, dense = ATTN_CASES["csa_mfma"]
+    # (inputs drawn for rows at t >= 400, where all T entries are ready, as at
+    # the positions used below)
+    q, kv, pool, z, idx = _attn_case(411, B, S, H, D, dv, rope, T, k, window, m, [400, 400],
+                                     sink, bf16, dense)
+    qp = [70000, 100000]
+    theta, factor, orig = 160000.0, 16.0, 65536
+    cs = ops.csa_rope_table_yarn(max(qp) + S + 1, rope, theta, factor, orig)
+    fr = oracle.yarn_freqs(rope, theta, factor, orig)
+    dt = torch.bfloat16
+    # the window rows of positions qp - window .. qp + S - 1
+    lo = [p - window for p in qp]
+    kvw = np.ascontiguousarray(kv[:, :S + window])
+    out = host(ops.csa_sparse_attn(dev(q, dt), dev(kvw, dt),
+                                   torch.tensor(lo, dtype=torch.int32, device="cuda"),
+                                   dev(pool, dt), dev(idx, torch.int32), dev(z, torch.float32),
+                                   torch.tensor(qp, dtype=torch.int32, device="cuda"),
+                                   rope_dim=rope, cs=cs, window=window,
+                                   scale=1.0 / math.sqrt(D), dv=dv))
+    for b in range(B):
+        t = qp[b] + np.arange(S)
+        ref = oracle.attention(q[b], t, kv_win=kvw[b], win_pos0=lo[b], window=window,
+                               pool=pool[b], idx=idx[b], m=m, sink=z, rope_dim=rope,
+                               theta=theta, scale=1.0 / math.sqrt(D), dv=dv, freqs=fr)
+        err = np.abs(out[b] - ref).max()
+        assert err <= BF16_ATOL, (b, float(err))
+
+
 # ------------------------------------------------------------------ compressor
 @pytest.mark.parametrize("bf16", [False, True])
 @pytest.mark.parametrize("m,ov,D,rope,gate,bias", [

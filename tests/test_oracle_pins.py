@@ -68,6 +68,68 @@ def test_rope_relative_position(orc):
     assert abs(d1 - d2) < 1e-3
 
 
+# ----------------------------------------------------------------- YaRN
+# DeepseekV4Config: compress_rope_theta is used with rope scaling for YaRN; the
+# parameters below are the published YaRN defaults (beta_fast 32, beta_slow 1)
+# at a 16x extension of a 65536-token context.
+YARN = dict(rope_dim=64, theta=160000.0, factor=16.0, original_max_pos=65536)
+
+
+def _plain_freqs(orc, rope_dim, theta):
+    """Pair frequencies read back from the (already pinned) plain table: the
+    angle at position 1 is the frequency itself (all are below pi)."""
+    cs = orc.rope_table(2, rope_dim, theta).astype(np.float64)
+    return np.arctan2(cs[1, :, 1], cs[1, :, 0])
+
+
+def test_yarn_factor_one_is_plain_rope(orc):
+    f = orc.yarn_freqs(64, 160000.0, 1.0, 65536)
+    p = np.arange(0, 131073, 97)
+    a = orc.rope_table(131073, 64, 160000.0, freqs=f)[p]
+    b = orc.rope_table(131073, 64, 160000.0)[p]
+    np.testing.assert_allclose(a, b, atol=1e-7)
+
+
+def test_yarn_frequencies_by_turns(orc):
+    """Pairs that turn many times over the original context (at least beta_fast
+    times, with a pair of margin) keep their frequency; pairs that turn at most
+    beta_slow times (with a pair of margin) are slowed down by the factor; the
+    pairs between blend the two with a weight linear in the pair index."""
+    d, theta, s, L = YARN["rope_dim"], YARN["theta"], YARN["factor"], YARN["original_max_pos"]
+    f = _plain_freqs(orc, d, theta)
+    fy = orc.yarn_freqs(d, theta, s, L, 32.0, 1.0)
+    turns = L * f / (2 * np.pi)
+    step = theta ** (2.0 / d)                 # turn ratio of neighbouring pairs
+    fast = turns >= 32.0 * step
+    slow = turns <= 1.0 / step
+    assert fast.sum() >= 4 and slow.sum() >= 4 and (~fast & ~slow).sum() >= 4
+    np.testing.assert_allclose(fy[fast], f[fast], rtol=1e-6)
+    np.testing.assert_allclose(fy[slow], f[slow] / s, rtol=1e-6)
+    ramp = (f - fy) / (f - f / s)
+    assert np.all(ramp > -1e-6) and np.all(ramp < 1 + 1e-6)
+    assert np.all(np.diff(ramp) > -1e-6)      # monotone: slower pairs interpolate more
+    inner = np.nonzero((ramp > 1e-6) & (ramp < 1 - 1e-6))[0]
+    assert len(inner) >= 4
+    steps = np.diff(ramp[inner])
+    np.testing.assert_allclose(steps, steps[0], rtol=1e-4)
+
+
+def test_yarn_interpolated_pairs_stretch_positions(orc):
+    """An interpolated (slow) pair at position factor * p has the angle the
+    plain pair has at p: the original context, stretched by the factor."""
+    d, theta, s, L = YARN["rope_dim"], YARN["theta"], YARN["factor"], YARN["original_max_pos"]
+    fy = orc.yarn_freqs(d, theta, s, L)
+    f = _plain_freqs(orc, d, theta)
+    slow = np.nonzero(L * f / (2 * np.pi) <= 1.0 / theta ** (2.0 / d))[0]
+    p = np.arange(0, 8000, 7)
+    ty = orc.rope_table(int(s) * 8000, d, theta, freqs=fy)
+    tp = orc.rope_table(8000, d, theta)
+    np.testing.assert_allclose(ty[int(s) * p][:, slow], tp[p][:, slow], atol=1e-6)
+    # and the fast pairs are untouched at every position
+    fast = np.nonzero(L * f / (2 * np.pi) >= 32.0 * theta ** (2.0 / d))[0]
+    np.testing.assert_array_equal(ty[:8000][:, fast], tp[:, fast])
+
+
 # ----------------------------------------------------------------- compressor
 def test_compress_null_gate_is_window_mean(orc):
     S, D, m = 37, 24, 4
