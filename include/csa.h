@@ -232,6 +232,28 @@ csa_status_t csa_sparse_attn(const void *q, const void *kv_win, const int32_t *w
                              int32_t window, float scale, void *workspace, size_t ws_bytes,
                              int32_t dtype, void *stream);
 
+/*
+ * csa_sparse_attn_noalloc -- csa_sparse_attn without a workspace argument, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation).  Same arguments,
+ * result and kernels as csa_sparse_attn given a workspace of
+ * csa_sparse_attn_workspace_size bytes; the split partials go to a 48 MiB
+ * device array of the library instead (one per GPU, held until the process
+ * ends; its address is looked up on the first call on each device).  The call
+ * allocates nothing.  A shape whose split needs more than 48 MiB returns
+ * CSA_ERR_UNSUPPORTED.  Every call on one GPU shares that array: calls that
+ * overlap in time on one GPU (other streams, other host threads) race and
+ * must be serialized by the caller.  The array needs no clearing (every
+ * partial a call reads was written earlier in the same call).
+ */
+csa_status_t csa_sparse_attn_noalloc(const void *q, const void *kv_win,
+                                     const int32_t *win_pos0, int32_t L_win, const void *pool,
+                                     int32_t T, const int32_t *idx, int32_t k,
+                                     const float *sink, void *out, const int32_t *q_pos,
+                                     int32_t B, int32_t S, int32_t H, int32_t D, int32_t dv,
+                                     int32_t rope_dim, const float *cs, int32_t n_pos,
+                                     int32_t window, float scale, int32_t dtype, void *stream);
+
 /* Bytes of workspace csa_sparse_attn uses for this shape on the current
  * device (0 = it never splits this shape). */
 size_t csa_sparse_attn_workspace_size(int32_t B, int32_t S, int32_t H, int32_t D,

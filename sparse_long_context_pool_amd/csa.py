@@ -42,6 +42,9 @@ def lib():
             "csa_sparse_attn": ([vp, vp, vp, i32, vp, i32, vp, i32, vp, vp, vp, i32, i32,
                                  i32, i32, i32, i32, vp, i32, i32, f32, vp, sz, i32, vp],
                                 ctypes.c_int),
+            "csa_sparse_attn_noalloc": ([vp, vp, vp, i32, vp, i32, vp, i32, vp, vp, vp, i32,
+                                         i32, i32, i32, i32, i32, vp, i32, i32, f32, i32, vp],
+                                        ctypes.c_int),
             "csa_sparse_attn_workspace_size": ([i32] * 9, sz),
             "hca_attn": ([vp, vp, vp, i32, vp, i32, i32, vp, vp, vp, i32, i32, i32, i32,
                           i32, i32, vp, i32, i32, f32, vp, sz, i32, vp], ctypes.c_int),
@@ -58,7 +61,7 @@ def lib():
 EXPORTS = ("csa_last_error", "csa_version", "csa_rope_table", "csa_rope_table_yarn",
            "csa_compress",
            "csa_cache_append",
-           "csa_index_scores", "csa_topk", "csa_sparse_attn",
+           "csa_index_scores", "csa_topk", "csa_sparse_attn", "csa_sparse_attn_noalloc",
            "csa_sparse_attn_workspace_size", "hca_attn", "hca_attn_workspace_size")
 
 
@@ -209,6 +212,27 @@ def csa_sparse_attn(q, kv_win, win_pos0, pool, idx, sink, q_pos, *, rope_dim: in
                                  dv, rope_dim, _ptr(cs), n_pos, window, float(scale),
                                  _ptr(ws), ws_bytes, dt, _stream()),
            "csa_sparse_attn")
+    return out
+
+
+def csa_sparse_attn_noalloc(q, kv_win, win_pos0, pool, idx, sink, q_pos, *, rope_dim: int, cs,
+                            window: int, scale: float, dv: int | None = None,
+                            out=None) -> torch.Tensor:
+    """csa_sparse_attn with the split workspace in the library's own device array
+    (the C call allocates nothing; `out` is allocated here when None)."""
+    B, S, H, D = q.shape
+    dv = D if dv is None else dv
+    L = 0 if kv_win is None else kv_win.shape[1]
+    T = 0 if pool is None else pool.shape[1]
+    k = 0 if idx is None else idx.shape[2]
+    if out is None:
+        out = torch.empty((B, S, H, dv), dtype=q.dtype, device=q.device)
+    n_pos = 0 if cs is None else cs.shape[0]
+    _check(lib().csa_sparse_attn_noalloc(_ptr(q), _ptr(kv_win), _ptr(win_pos0), L, _ptr(pool),
+                                         T, _ptr(idx), k, _ptr(sink), _ptr(out), _ptr(q_pos), B,
+                                         S, H, D, dv, rope_dim, _ptr(cs), n_pos, window,
+                                         float(scale), _dtype(q), _stream()),
+           "csa_sparse_attn_noalloc")
     return out
 
 

@@ -5,6 +5,7 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <mutex>
 
 #include "../../include/csa.h"
 #include "csa_device.hpp"
@@ -123,6 +124,39 @@ csa_status_t run_attn(const char* fn, const csa::AttnParams& p, int npool_max,
     else plan.nsplit = 1;
   }
   return launched(csa::launch_attention(p, plan, ws, s), fn);
+}
+
+// ---- the workspace of csa_sparse_attn_noalloc: a device array of the library
+// (each GPU the library runs on holds its own copy until the process ends).
+// Host code never uses the array's name as an address: the device address of
+// each GPU's copy comes from hipGetSymbolAddress, once per device, with that
+// device current, and only that address is passed to kernels.
+constexpr size_t kScratchBytes = size_t(48) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+csa_status_t scratch_on_current_device(const char* fn, void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess)
+    return fail(CSA_ERR_LAUNCH, "%s: hipGetDevice failed: %s", fn, hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(CSA_ERR_UNSUPPORTED, "%s: device %d beyond the %d the library serves", fn, dev,
+                kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr)
+      return fail(CSA_ERR_LAUNCH, "%s: hipGetSymbolAddress(scratch) failed on device %d: %s",
+                  fn, dev, hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return CSA_OK;
 }
 
 }  // namespace
@@ -311,6 +345,46 @@ csa_status_t csa_sparse_attn(const void* q, const void* kv_win, const int32_t* w
     p.dense = 0;
   }
   return run_attn(fn, p, p.k, workspace, ws_bytes, as_stream(stream));
+}
+
+csa_status_t csa_sparse_attn_noalloc(const void* q, const void* kv_win,
+                                     const int32_t* win_pos0, int32_t L_win, const void* pool,
+                                     int32_t T, const int32_t* idx, int32_t k,
+                                     const float* sink, void* out, const int32_t* q_pos,
+                                     int32_t B, int32_t S, int32_t H, int32_t D, int32_t dv,
+                                     int32_t rope_dim, const float* cs, int32_t n_pos,
+                                     int32_t window, float scale, int32_t dtype,
+                                     void* stream) {
+  const char* fn = "csa_sparse_attn_noalloc";
+  csa_status_t st = check_attn(fn, q, kv_win, win_pos0, L_win, pool, T, out, q_pos, B, S, H,
+                               D, dv, rope_dim, cs, n_pos, window, scale, dtype);
+  if (st != CSA_OK) return st;
+  if (k < 0) return fail(CSA_ERR_INVALID, "%s: k=%d must be >= 0", fn, k);
+  if ((long)B * S == 0) return CSA_OK;
+  if (k > 0 && !idx) return fail(CSA_ERR_INVALID, "%s: idx is required when k > 0", fn);
+  csa::AttnParams p = make_params(q, kv_win, win_pos0, L_win, pool, T, idx, k, 1, sink, out,
+                                  q_pos, B, S, H, D, dv, rope_dim, cs, n_pos, window, scale,
+                                  dtype);
+  if (k == 0) {
+    p.idx = nullptr;
+    p.k = 0;
+    p.dense = 0;
+  }
+  // the same plan as csa_sparse_attn with a large enough workspace
+  const csa::AttnPlan plan =
+      csa::plan_attention(p.B, p.S, p.H, p.D, p.dv, p.rope_dim, p.window, p.k, p.bf16,
+                          std::max<long>(p.L_win, p.T), p.k);
+  void* ws = nullptr;
+  if (plan.nsplit > 1) {
+    if (plan.ws_bytes > kScratchBytes)
+      return fail(CSA_ERR_UNSUPPORTED,
+                  "%s: this shape needs %zu bytes of scratch, more than the library's "
+                  "%zu (use csa_sparse_attn with a workspace)",
+                  fn, plan.ws_bytes, kScratchBytes);
+    st = scratch_on_current_device(fn, &ws);
+    if (st != CSA_OK) return st;
+  }
+  return launched(csa::launch_attention(p, plan, ws, as_stream(stream)), fn);
 }
 
 csa_status_t hca_attn(const void* q, const void* kv_win, const int32_t* win_pos0,
