@@ -351,6 +351,50 @@ def run_workload(name, steps, warmup, csa, torch, synth, WORKLOADS):
     return wl, res
 
 
+def run_out_proj(steps, warmup, csa, torch, synth, S=8192, H=64, dv=512, groups=8, rank=1024,
+                 hidden=4096):
+    """The grouped low-rank output projection (o_groups 8 -> o_lora_rank 1024
+    -> hidden 4096) of the prefill workload's attention output [S, H, dv],
+    with synthetic weights; timed on its own (it is the step after the
+    attention, not part of the hot-path step): `warmup` untimed launches, then
+    `steps` launches between two events."""
+    dev = "cuda"
+    bf = torch.bfloat16
+    Kg = H * dv // groups
+    o = synth.normal_torch(0, "attn_out", S, (H * dv,), scale=0.5, dtype=bf).to(dev)
+    w_a = synth.normal_torch(0, "o_a_proj", groups * rank, (Kg,), scale=Kg ** -0.5,
+                             dtype=bf).to(dev).view(groups, rank, Kg)
+    w_b = synth.normal_torch(0, "o_b_proj", hidden, (groups * rank,),
+                             scale=(groups * rank) ** -0.5, dtype=bf).to(dev)
+    mid = torch.empty((S, groups * rank), dtype=bf, device=dev)
+    out = torch.empty((S, hidden), dtype=bf, device=dev)
+
+    def fn():
+        csa.csa_grouped_out_proj(o, w_a, w_b, mid=mid, out=out)
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    torch.cuda._sleep(1 << 22)
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(steps):
+        fn()
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / steps
+    flops = 2 * S * (groups * rank * Kg + hidden * groups * rank)
+    achieved = flops / (ms * 1e-3) / 1e12
+    rep = {"workload": f"grouped output projection of csa_prefill_bf16's attention output: "
+                       f"[{S}, {H}x{dv}] -> {groups} groups x {rank} -> {hidden}",
+           "ms": round(ms, 5), "bound": "mfma", "achieved": round(achieved, 2),
+           "peak": PEAK["mfma"][0], "unit": "TFLOP/s",
+           "frac": round(achieved / PEAK["mfma"][0], 4), "work": flops}
+    print(f"[bench] out_proj: {ms * 1e3:.1f}us {100 * rep['frac']:.1f}%", file=sys.stderr,
+          flush=True)
+    return rep
+
+
 def roofline_of(wl_name, res):
     dom = res["dominant"]
     st = res["stages"][dom]
@@ -405,6 +449,7 @@ DOMINANT = {                # stage -> kernels that make it (name prefixes)
                   "csa::(anonymous namespace)::attn_generic_kernel"),
     "index_scores": ("csa::(anonymous namespace)::index_scores",),
     "topk": ("csa::(anonymous namespace)::topk_",),
+    "out_proj": ("csa::(anonymous namespace)::gemm_nt",),
 }
 
 
@@ -487,6 +532,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workloads", default="csa_prefill_bf16,csa_decode_bf16,hca_bf16,dsa_bf16")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-next", action="store_true",
+                    help="skip the rows measured beside the step (output projection)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain copy of known size (for counter calibration)")
     ap.add_argument("--traffic", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
@@ -542,6 +589,10 @@ def main():
         else:
             entry["tokens_per_s"] = r2["tokens_per_s"]
         line[key] = entry
+    if "csa_prefill_bf16" in names and not args.no_next:
+        # the rows after the hot path, each measured on its own
+        line["next_rows"] = {"out_proj": run_out_proj(args.steps, args.warmup, csa, torch,
+                                                      synth)}
     if args.calib_copy:
         calib_copy(torch)
     if not args.no_cpu:

@@ -279,6 +279,31 @@ csa_status_t hca_attn(const void *q, const void *kv_win, const int32_t *win_pos0
 size_t hca_attn_workspace_size(int32_t B, int32_t S, int32_t H, int32_t D, int32_t dv,
                                int32_t rope_dim, int32_t T, int32_t window, int32_t dtype);
 
+/*
+ * csa_grouped_out_proj -- grouped low-rank output projection of the attention
+ * output.  Page "DeepSeek-V4", "Hybrid attention (§2.3)" (the heads are split
+ * into o_groups groups; each group goes through its own projection to
+ * o_lora_rank values (o_a_proj), the concatenated groups through one more
+ * linear map to hidden_size (o_b_proj)) and DeepseekV4Config (o_groups = 8,
+ * o_lora_rank = 1024, hidden_size = 4096, attention_bias = False).
+ *   o     [M][groups * group_in] dtype   attention output rows (the [S][H][dv]
+ *                                        output of csa_sparse_attn / hca_attn
+ *                                        with group_in = H dv / groups: group g
+ *                                        holds heads g H/groups .. (g+1) H/groups - 1)
+ *   w_a   [groups][rank][group_in] dtype  per-group projection (rows = outputs)
+ *   w_b   [hidden][groups * rank] dtype   the second projection
+ *   mid   [M][groups * rank] dtype, out:  mid[m][g rank + j] =
+ *             sum_c o[m][g group_in + c] * w_a[g][j][c]   (stored in dtype)
+ *   out   [M][hidden] dtype, out:         out[m][n] = sum_i mid[m][i] * w_b[n][i]
+ *   Products accumulate in fp32; bf16 results are rounded to nearest even.
+ *   The stored mid (bf16 for bf16) is what the second product reads.
+ *   group_in, rank, hidden must be multiples of 8; tensors 16-byte aligned.
+ *   Two kernels in stream order.
+ */
+csa_status_t csa_grouped_out_proj(const void *o, const void *w_a, const void *w_b, void *mid,
+                                  void *out, int32_t M, int32_t groups, int32_t group_in,
+                                  int32_t rank, int32_t hidden, int32_t dtype, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

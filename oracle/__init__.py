@@ -20,6 +20,8 @@ function follows the Hugging Face Transformers model pages:
 
 * "DeepSeek-V4", DeepseekV4Config: compress_rope_theta used with rope scaling
   for YaRN (``yarn_freqs``: the published YaRN frequency interpolation).
+* "DeepSeek-V4", section "Hybrid attention (§2.3)", grouped low-rank output
+  projection (o_groups, o_lora_rank): ``grouped_out_proj`` (float64 numpy).
 
 Functions without a pin on the pages are marked "parity unpinned" in
 ``csa_oracle.c``'s header (the ReLU of the index score, the compressor's gating
@@ -287,3 +289,34 @@ def attention(q, tpos, *, kv_win=None, win_pos0: int = 0, window: int = 0,
         int(rope_dim), float(theta), _ptr(f, ctypes.c_double), float(scale), _ptr(out))
     _check(rc, "attention")
     return out
+
+
+def grouped_out_proj(o, w_a, w_b, *, round_mid_bf16: bool = False, mid=None):
+    """Grouped low-rank output projection ("DeepSeek-V4", section "Hybrid
+    attention (§2.3)": the heads split into o_groups groups, each group's
+    concatenated head outputs projected to o_lora_rank values by its own map
+    (o_a_proj), the groups concatenated and mapped to hidden_size (o_b_proj);
+    DeepseekV4Config: no bias).
+
+    o [M, G*Kg] (heads g*H/G .. (g+1)*H/G - 1 of each row form group g),
+    w_a [G, r, Kg], w_b [hidden, G*r] -> (mid [M, G*r], out [M, hidden]) in
+    float64.  round_mid_bf16 rounds mid to bf16 before the second product, as
+    a bf16 pipeline stores it.  Given `mid` (e.g. another implementation's
+    stored mid), only the second product is taken (o and w_a are unused)."""
+    w_b = np.asarray(w_b, np.float64)
+    if mid is not None:
+        mid = np.asarray(mid, np.float64)
+        return mid, mid @ w_b.T
+    o = np.asarray(o, np.float64)
+    w_a = np.asarray(w_a, np.float64)
+    M = o.shape[0]
+    G, r, Kg = w_a.shape
+    assert o.shape == (M, G * Kg) and w_b.shape[1] == G * r
+    mid = np.empty((M, G * r), np.float64)
+    for g in range(G):
+        # group g: its own input columns, its own projection
+        mid[:, g * r:(g + 1) * r] = o[:, g * Kg:(g + 1) * Kg] @ w_a[g].T
+    if round_mid_bf16:
+        mid = round_bf16(mid.astype(np.float32)).astype(np.float64)
+    out = mid @ w_b.T
+    return mid, out

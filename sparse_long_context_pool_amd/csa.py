@@ -49,6 +49,8 @@ def lib():
             "hca_attn": ([vp, vp, vp, i32, vp, i32, i32, vp, vp, vp, i32, i32, i32, i32,
                           i32, i32, vp, i32, i32, f32, vp, sz, i32, vp], ctypes.c_int),
             "hca_attn_workspace_size": ([i32] * 9, sz),
+            "csa_grouped_out_proj": ([vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp],
+                                     ctypes.c_int),
         }
         for name, (args, res) in sig.items():
             fn = getattr(L, name)
@@ -62,7 +64,8 @@ EXPORTS = ("csa_last_error", "csa_version", "csa_rope_table", "csa_rope_table_ya
            "csa_compress",
            "csa_cache_append",
            "csa_index_scores", "csa_topk", "csa_sparse_attn", "csa_sparse_attn_noalloc",
-           "csa_sparse_attn_workspace_size", "hca_attn", "hca_attn_workspace_size")
+           "csa_sparse_attn_workspace_size", "hca_attn", "hca_attn_workspace_size",
+           "csa_grouped_out_proj")
 
 
 def _check(status: int, fn: str):
@@ -256,3 +259,21 @@ def hca_attn(q, kv_win, win_pos0, pool, sink, q_pos, *, m: int, rope_dim: int, c
                           _stream()),
            "hca_attn")
     return out
+
+
+def csa_grouped_out_proj(o, w_a, w_b, *, mid=None, out=None):
+    """o [M, groups*group_in] (or [B, S, H, dv], flattened), w_a [groups, rank, group_in],
+    w_b [hidden, groups*rank] -> (mid [M, groups*rank], out [M, hidden])."""
+    groups, rank, group_in = w_a.shape
+    hidden = w_b.shape[0]
+    M = o.numel() // (groups * group_in)
+    assert o.numel() == M * groups * group_in and w_b.shape[1] == groups * rank
+    assert w_a.dtype == o.dtype and w_b.dtype == o.dtype
+    if mid is None:
+        mid = torch.empty((M, groups * rank), dtype=o.dtype, device=o.device)
+    if out is None:
+        out = torch.empty((M, hidden), dtype=o.dtype, device=o.device)
+    _check(lib().csa_grouped_out_proj(_ptr(o), _ptr(w_a), _ptr(w_b), _ptr(mid), _ptr(out), M,
+                                      groups, group_in, rank, hidden, _dtype(o), _stream()),
+           "csa_grouped_out_proj")
+    return mid, out

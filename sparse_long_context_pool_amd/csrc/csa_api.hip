@@ -387,6 +387,32 @@ csa_status_t csa_sparse_attn_noalloc(const void* q, const void* kv_win,
   return launched(csa::launch_attention(p, plan, ws, as_stream(stream)), fn);
 }
 
+csa_status_t csa_grouped_out_proj(const void* o, const void* w_a, const void* w_b, void* mid,
+                                  void* out, int32_t M, int32_t groups, int32_t group_in,
+                                  int32_t rank, int32_t hidden, int32_t dtype, void* stream) {
+  const char* fn = "csa_grouped_out_proj";
+  if (!dtype_ok(dtype)) return fail(CSA_ERR_INVALID, "%s: unknown dtype %d", fn, dtype);
+  if (M < 0 || groups < 1 || group_in < 1 || rank < 1 || hidden < 1)
+    return fail(CSA_ERR_INVALID,
+                "%s: bad sizes (M=%d groups=%d group_in=%d rank=%d hidden=%d)", fn, M, groups,
+                group_in, rank, hidden);
+  if (group_in % 8 != 0 || rank % 8 != 0 || hidden % 8 != 0)
+    return fail(CSA_ERR_INVALID, "%s: group_in, rank and hidden must be multiples of 8", fn);
+  const long elems_o = (long)groups * group_in, elems_mid = (long)groups * rank;
+  if ((long)M * elems_o >= (1L << 31) || (long)M * elems_mid >= (1L << 31) ||
+      (long)M * hidden >= (1L << 31) || (long)hidden * elems_mid >= (1L << 31) ||
+      (long)groups * rank * group_in >= (1L << 31))
+    return fail(CSA_ERR_UNSUPPORTED, "%s: tensors of 2^31 elements or more", fn);
+  if (M == 0) return CSA_OK;
+  if (!o || !w_a || !w_b || !mid || !out)
+    return fail(CSA_ERR_INVALID, "%s: o, w_a, w_b, mid and out are required", fn);
+  if (!aligned16(o) || !aligned16(w_a) || !aligned16(w_b) || !aligned16(mid) || !aligned16(out))
+    return fail(CSA_ERR_INVALID, "%s: tensors must be 16-byte aligned", fn);
+  return launched(csa::launch_out_proj(o, w_a, w_b, mid, out, M, groups, group_in, rank, hidden,
+                                       dtype == CSA_BF16, as_stream(stream)),
+                  fn);
+}
+
 csa_status_t hca_attn(const void* q, const void* kv_win, const int32_t* win_pos0,
                       int32_t L_win, const void* pool, int32_t T, int32_t m,
                       const float* sink, void* out, const int32_t* q_pos, int32_t B,

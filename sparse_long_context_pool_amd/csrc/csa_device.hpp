@@ -160,6 +160,13 @@ hipError_t launch_index_scores(const void* q_idx, const float* w_idx, const void
 hipError_t launch_topk(const float* scores, int* idx, const int* q_pos, int B, int S,
                        int T, int k, int m, hipStream_t s);
 
+// Grouped low-rank output projection: mid = grouped(o, w_a), out = mid w_b^T
+// (two GEMMs with both operands contiguous along the reduction).
+bool gemm_nt_mfma_shape(int N, int K, int G, int ldx, int ldc, int M);
+hipError_t launch_out_proj(const void* o, const void* w_a, const void* w_b, void* mid,
+                           void* out, int M, int G, int Kg, int r, int hidden, bool bf16,
+                           hipStream_t s);
+
 struct AttnParams {
   const void* q;          // [B][S][H][D]
   const void* kv_win;     // [B][L_win][D]

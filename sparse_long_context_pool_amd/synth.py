@@ -25,6 +25,8 @@ TID = {
     # decode caches: compressor buffers and the step's new token
     "ring_x": 15, "ring_g": 16, "ring_xi": 17, "ring_gi": 18, "x_new": 19, "g_new": 20,
     "xi_new": 21, "gi_new": 22,
+    # grouped output projection: the attention output and the two weights
+    "attn_out": 23, "o_a_proj": 24, "o_b_proj": 25,
 }
 
 

@@ -1,0 +1,59 @@
+"""GPU parity of the grouped low-rank output projection (csa_grouped_out_proj)
+against the oracle, stage by stage: mid against the oracle's grouped product,
+then out against the oracle's second product of the GPU's own stored mid.
+
+Bounds: a sum of K fp32 products in any order is within K 2^-24 sum |a b| of
+the exact sum; a bf16 store rounds to within 2^-8 relative, and two roundings
+of nearby sums land at most one bf16 ulp (2^-7 relative) apart."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from parity import dev, host
+
+pytestmark = pytest.mark.gpu
+
+CASES = {
+    # name: (dtype, M, G, Kg, rank, hidden)
+    "v4_prefill_rows_bf16": ("bf16", 300, 8, 4096, 1024, 4096),   # 8 groups of 8 heads x 512
+    "v4_decode_bf16": ("bf16", 64, 8, 4096, 1024, 4096),
+    "small_groups_bf16": ("bf16", 50, 4, 64, 256, 256),
+    "generic_bf16": ("bf16", 20, 2, 40, 24, 16),
+    "generic_f32": ("f32", 37, 2, 48, 40, 24),
+}
+
+
+@pytest.mark.parametrize("name", sorted(CASES))
+def test_grouped_out_proj(name):
+    from sparse_long_context_pool_amd import csa
+    dt_s, M, G, Kg, rank, hidden = CASES[name]
+    bf16 = dt_s == "bf16"
+    r = np.random.default_rng(len(name) * 7919 + M)
+
+    def draw(shape, scale):
+        a = (r.standard_normal(shape) * scale).astype(np.float32)
+        return oracle.round_bf16(a) if bf16 else a
+    o = draw((M, G * Kg), 1.0)
+    w_a = draw((G, rank, Kg), 1.0 / np.sqrt(Kg))
+    w_b = draw((hidden, G * rank), 1.0 / np.sqrt(G * rank))
+    dt = torch.bfloat16 if bf16 else torch.float32
+    mid_g, out_g = csa.csa_grouped_out_proj(dev(o, dt), dev(w_a, dt), dev(w_b, dt))
+    mid_g, out_g = host(mid_g), host(out_g)
+    u = 2.0 ** -24
+    # stage 1
+    mid_o, _ = oracle.grouped_out_proj(o, w_a, w_b, round_mid_bf16=bf16)
+    absum = np.concatenate([np.abs(o[:, g * Kg:(g + 1) * Kg]).astype(np.float64)
+                            @ np.abs(w_a[g]).astype(np.float64).T for g in range(G)], axis=1)
+    b1 = Kg * u * absum + (2.0 ** -7 * np.abs(mid_o) if bf16 else 0.0) + 1e-30
+    d1 = np.abs(mid_g - mid_o)
+    assert np.all(d1 <= b1), (name, float((d1 / b1).max()))
+    # stage 2, from the GPU's stored mid
+    _, out_o = oracle.grouped_out_proj(None, None, w_b, mid=mid_g)
+    K2 = G * rank
+    absum2 = np.abs(mid_g).astype(np.float64) @ np.abs(w_b).astype(np.float64).T
+    b2 = K2 * u * absum2 + (2.0 ** -8 * np.abs(out_o) if bf16 else 0.0) + 1e-30
+    d2 = np.abs(out_g - out_o)
+    assert np.all(d2 <= b2), (name, float((d2 / b2).max()))
+    # and the result is not trivially small
+    assert np.abs(out_o).mean() > 0.1

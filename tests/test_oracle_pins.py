@@ -542,3 +542,45 @@ def test_cache_state_is_causal_and_holds_the_last_tokens(orc):
         lo = max(0, (w - 1) * m)
         ref = brute.rope_complex(x[lo:(w + 1) * m].astype(np.float64).mean(0), R, 1e4, w * m)
         np.testing.assert_allclose(pool[w], ref, rtol=1e-5, atol=1e-5)
+
+
+# ----------------------------------------------------------------- output projection
+def test_grouped_out_proj_is_block_diagonal_map(orc):
+    """The grouped projection equals one dense map whose matrix holds the
+    group maps on its diagonal blocks (zero elsewhere): group g reads only its
+    own heads' columns and writes only its own rank slice."""
+    r = rng(31)
+    M, H, dv, G, rank, hidden = 7, 8, 6, 4, 5, 9
+    Kg = H * dv // G
+    o = r.standard_normal((M, H, dv))
+    w_a = r.standard_normal((G, rank, Kg))
+    w_b = r.standard_normal((hidden, G * rank))
+    mid, out = orc.grouped_out_proj(o.reshape(M, H * dv), w_a, w_b)
+    dense = scipy.linalg.block_diag(*[w_a[g] for g in range(G)])     # [G*rank, H*dv]
+    np.testing.assert_allclose(mid, o.reshape(M, H * dv) @ dense.T, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(out, (o.reshape(M, H * dv) @ dense.T) @ w_b.T, rtol=1e-12,
+                               atol=1e-12)
+    # a head of group 1 changes only group 1's slice of mid
+    o2 = o.copy()
+    o2[:, H // G + 1, :] += 1.0
+    mid2, _ = orc.grouped_out_proj(o2.reshape(M, H * dv), w_a, w_b)
+    changed = np.any(np.abs(mid2 - mid) > 1e-9, axis=0).reshape(G, rank)
+    assert changed[1].all() and not changed[[0, 2, 3]].any()
+
+
+def test_grouped_out_proj_one_group_is_two_plain_products(orc):
+    r = rng(32)
+    o = r.standard_normal((5, 12))
+    w_a = r.standard_normal((1, 4, 12))
+    w_b = r.standard_normal((3, 4))
+    mid, out = orc.grouped_out_proj(o, w_a, w_b)
+    ref_mid = np.einsum("mc,jc->mj", o, w_a[0])
+    np.testing.assert_allclose(mid, ref_mid, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(out, np.einsum("mj,nj->mn", ref_mid, w_b), rtol=1e-12, atol=1e-12)
+    # bf16 storage of mid: the second product reads the rounded values
+    mid_b, out_b = orc.grouped_out_proj(o, w_a, w_b, round_mid_bf16=True)
+    assert np.array_equal(mid_b, orc.round_bf16(ref_mid.astype(np.float32)))
+    np.testing.assert_allclose(out_b, mid_b @ w_b.T, rtol=1e-12, atol=1e-12)
+    # the second product alone, from a given mid
+    _, out_c = orc.grouped_out_proj(None, None, w_b, mid=mid_b)
+    assert np.array_equal(out_c, out_b)
