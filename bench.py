@@ -79,6 +79,8 @@ def work_counts(wl):
         else:
             w["index_scores"] = ("mfma", pairs * wl.n_idx_heads * (2 * wl.idx_dim + 2))
         w["topk"] = ("hbm", pairs * 4 + B * wl.S * wl.topk * 4)
+        # scores and top-k in one kernel: the scores stay on chip
+        w["index_topk"] = ("mfma", pairs * wl.n_idx_heads * (2 * wl.idx_dim + 2))
         keys = (visible_window(wl, t) + np.minimum(R, wl.topk)).sum() * B
     else:
         keys = (visible_window(wl, t) + R).sum() * B
@@ -95,9 +97,14 @@ class Runner:
     def __init__(self, wl, csa, torch):
         self.wl, self.csa, self.torch = wl, csa, torch
         self.stages = []          # (name, launch fn)
+        self.extra = []           # (name, launch fn) timed beside the step
 
     def add(self, name, fn):
         self.stages.append((name, fn))
+
+    def beside(self, name, fn):
+        """A launch timed on its own, after the step (not part of it)."""
+        self.extra.append((name, fn))
 
     def _capture(self, fns):
         """A HIP graph of the launches of `fns` (launched once on the capture
@@ -173,6 +180,21 @@ class Runner:
                 ev[name].append((a, b))
         torch.cuda.synchronize()
         avg = {n: float(np.mean([a.elapsed_time(b) for a, b in v])) for n, v in ev.items()}
+        beside = {}
+        for name, fn in self.extra:
+            for _ in range(warmup):
+                fn()
+            torch.cuda.synchronize()
+            torch.cuda._sleep(1 << 22)
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            for _ in range(steps):
+                fn()
+            b.record()
+            torch.cuda.synchronize()
+            beside[name] = a.elapsed_time(b) / steps
+        self.beside_ms = beside
         return total_ms / steps, avg
 
 
@@ -252,11 +274,18 @@ def setup(wl, csa, torch, synth):
         q_idx = gen("q_idx", B * S, (wl.n_idx_heads, wl.idx_dim)).view(B, S, wl.n_idx_heads,
                                                                        wl.idx_dim)
         w_idx = gen("w_idx", B * S, (wl.n_idx_heads,), torch.float32).view(B, S, wl.n_idx_heads)
-        scores = torch.empty((B, S, wl.T), dtype=torch.float32, device=dev)
         idx = torch.empty((B, S, wl.topk), dtype=torch.int32, device=dev)
-        r.add("index_scores", lambda: csa.csa_index_scores(q_idx, w_idx, k_idx, q_pos, m=wl.m,
-                                                           out=scores))
+        scores = torch.empty((B, S, wl.T), dtype=torch.float32, device=dev)
+        r.add("index_scores", lambda: csa.csa_index_scores(q_idx, w_idx, k_idx, q_pos,
+                                                           m=wl.m, out=scores))
         r.add("topk", lambda: csa.csa_topk(scores, q_pos, k=wl.topk, m=wl.m, out=idx))
+        if csa.lib().csa_index_topk_workspace_size(B, S, wl.T, wl.n_idx_heads, wl.idx_dim,
+                                                   wl.topk, wl.m, 1) == 0:
+            # the fused call (scores kept on chip) is timed beside the step, on the
+            # same inputs, with its own output
+            idx_f = torch.empty_like(idx)
+            r.beside("index_topk", lambda: csa.csa_index_topk(q_idx, w_idx, k_idx, q_pos,
+                                                              k=wl.topk, m=wl.m, out=idx_f))
         need = csa.lib().csa_sparse_attn_workspace_size(B, S, wl.H, wl.D, wl.dv, wl.rope_dim,
                                                         wl.topk, wl.window, 1)
         ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
@@ -337,15 +366,18 @@ def run_workload(name, steps, warmup, csa, torch, synth, WORKLOADS):
     ms_step, avg = r.run(steps, warmup, flush)
     work, keys = work_counts(wl)
     stages = stage_report(wl, avg, work)
+    beside = stage_report(wl, r.beside_ms, work) if r.beside_ms else {}
     dom = max(stages, key=lambda n: stages[n]["ms"])
     print(f"[bench] {name}: {ms_step:.3f} ms/step (setup {time.time() - t0:.1f}s); "
-          + ", ".join(f"{n} {v['ms']*1e3:.1f}us {100*v['frac']:.1f}%" for n, v in stages.items()),
+          + ", ".join(f"{n} {v['ms']*1e3:.1f}us {100*v['frac']:.1f}%" for n, v in stages.items())
+          + "".join(f"; beside the step: {n} {v['ms']*1e3:.1f}us {100*v['frac']:.1f}%"
+                    for n, v in beside.items()),
           file=sys.stderr, flush=True)
     res = {"workload": name, "ms_per_step": round(ms_step, 5),
            "setup_ms": {k: round(v, 5) for k, v in r.setup_ms.items()},
            "tokens_per_s": round(wl.B * wl.S / (ms_step * 1e-3), 1),
            "us_per_step": round(ms_step * 1e3, 2), "stages": stages, "dominant": dom,
-           "attended_keys": keys}
+           "attended_keys": keys, "beside_step": beside}
     del r
     torch.cuda.empty_cache()
     return wl, res
@@ -434,7 +466,16 @@ def cpu_baseline(WORKLOADS, synth, n_rows=8192):
     t2 = time.perf_counter()
     total = (t1 - t0) + (t2 - t1) * wl.S / n_rows
     cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    cpu = "unknown"
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                cpu = ln.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
     return {"value": round(wl.S / total, 2), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "cpu": cpu,
             "sample": (f"csa_prefill_bf16: compression of all {wl.ctx} tokens "
                        f"({t1 - t0:.2f}s) + {n_rows} of {wl.S} query rows, evenly spaced "
                        f"({t2 - t1:.2f}s), scaled to {wl.S} rows"),
@@ -449,6 +490,7 @@ DOMINANT = {                # stage -> kernels that make it (name prefixes)
                   "csa::(anonymous namespace)::attn_generic_kernel"),
     "index_scores": ("csa::(anonymous namespace)::index_scores",),
     "topk": ("csa::(anonymous namespace)::topk_",),
+    "index_topk": ("csa::(anonymous namespace)::index_topk_fused",),
     "out_proj": ("csa::(anonymous namespace)::gemm_nt",),
 }
 
@@ -524,6 +566,62 @@ def write_traffic(fetch_db, write_db, workload, out=None):
     return doc
 
 
+# ------------------------------------------------------------------ profile summaries
+def _short_kernel(name):
+    name = name[5:] if name.startswith("void ") else name
+    name = name.replace("csa::(anonymous namespace)::", "").replace("(anonymous namespace)::", "")
+    return name.split("(")[0]
+
+
+def summarize_trace(csv_path, timed):
+    """Markdown table of a rocprofv3 kernel trace (`--kernel-trace -f csv`): per
+    kernel the number of dispatches and the average duration over all of them
+    and over the last `timed` of them (the benchmark's timed eager steps come
+    last for every stage kernel)."""
+    import csv
+    per = {}
+    for r in csv.DictReader(open(csv_path)):
+        dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3   # us
+        per.setdefault(_short_kernel(r["Kernel_Name"]), []).append((int(r["Start_Timestamp"]), dur))
+    rows = ["| kernel | dispatches | average, all (us) | average, last %d (us) |" % timed,
+            "|---|---:|---:|---:|"]
+    for k, v in sorted(per.items(), key=lambda kv: -sum(d for _, d in kv[1])):
+        v.sort()
+        last = [d for _, d in v[-timed:]]
+        rows.append(f"| `{k}` | {len(v)} | {sum(d for _, d in v) / len(v):.1f} | "
+                    f"{sum(last) / len(last):.1f} |")
+    return "\n".join(rows)
+
+
+def summarize_pmc(csv_paths):
+    """Markdown table of rocprofv3 counter runs (`--pmc ... -f csv`): per kernel
+    the mean over its dispatches of MFMA busy (SQ_VALU_MFMA_BUSY_CYCLES over
+    GRBM_GUI_ACTIVE of one XCD times the 1024 SIMDs), LDS busy and bank-conflict
+    share, and the raw means of every counter taken."""
+    import csv
+    vals = {}
+    for path in csv_paths:
+        for r in csv.DictReader(open(path)):
+            k = _short_kernel(r["Kernel_Name"])
+            vals.setdefault(k, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    out = []
+    for k, d in vals.items():
+        mean = {c: sum(v) / len(v) for c, v in d.items()}
+        line = f"- `{k}`:"
+        gui = mean.get("GRBM_GUI_ACTIVE")
+        if gui and "SQ_VALU_MFMA_BUSY_CYCLES" in mean:
+            # GRBM_GUI_ACTIVE sums the 8 XCDs: one XCD's active cycles are 1/8
+            line += f" MFMA busy {mean['SQ_VALU_MFMA_BUSY_CYCLES'] / (gui / 8 * 1024):.3f};"
+        if gui and "SQ_LDS_IDX_ACTIVE" in mean:
+            line += f" LDS busy {mean['SQ_LDS_IDX_ACTIVE'] / (gui / 8 * 256):.3f};"
+            if "SQ_LDS_BANK_CONFLICT" in mean:
+                line += (f" bank-conflict cycles / LDS busy "
+                         f"{mean['SQ_LDS_BANK_CONFLICT'] / max(mean['SQ_LDS_IDX_ACTIVE'], 1):.3f};")
+        line += " raw means: " + ", ".join(f"{c} {v:.4g}" for c, v in sorted(mean.items()))
+        out.append(line)
+    return "\n".join(out)
+
+
 # ------------------------------------------------------------------ main
 def main():
     ap = argparse.ArgumentParser()
@@ -539,7 +637,17 @@ def main():
     ap.add_argument("--traffic", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
                     help="write profiles/hbm_traffic.json from two counter databases of "
                          "one --workloads run, then exit (no GPU)")
+    ap.add_argument("--summarize-trace", nargs=2, metavar=("KERNEL_TRACE_CSV", "TIMED"),
+                    help="print a markdown table of a rocprofv3 kernel trace, then exit (no GPU)")
+    ap.add_argument("--summarize-pmc", nargs="+", metavar="COUNTER_CSV",
+                    help="print per-kernel summaries of rocprofv3 counter runs, then exit")
     args = ap.parse_args()
+    if args.summarize_trace:
+        print(summarize_trace(args.summarize_trace[0], int(args.summarize_trace[1])))
+        return
+    if args.summarize_pmc:
+        print(summarize_pmc(args.summarize_pmc))
+        return
     if args.traffic:
         names = [n for n in args.workloads.split(",") if n]
         if len(names) != 1:
@@ -593,6 +701,9 @@ def main():
         # the rows after the hot path, each measured on its own
         line["next_rows"] = {"out_proj": run_out_proj(args.steps, args.warmup, csa, torch,
                                                       synth)}
+        for n, v in res.get("beside_step", {}).items():
+            line["next_rows"][n] = dict(v, workload=f"{main_name}: scores and top-k in one "
+                                                    f"call (replaces index_scores + topk)")
     if args.calib_copy:
         calib_copy(torch)
     if not args.no_cpu:

@@ -197,6 +197,31 @@ csa_status_t csa_topk(const float *scores, int32_t *idx, const int32_t *q_pos, i
                       int32_t S, int32_t T, int32_t k, int32_t m, void *stream);
 
 /*
+ * csa_index_topk -- csa_index_scores followed by csa_topk as one call, the
+ * scores kept on chip.  Page "DeepSeek-V3.2", "DeepSeek Sparse Attention"
+ * (the indexer scores each query against the earlier keys and only the top-k
+ * tokens go on to attention; the indexer is cheap next to the attention) and
+ * page "DeepSeek-V4", "Hybrid attention" (the Lightning Indexer picks the
+ * index_topk compressed entries per query).
+ *   Arguments as csa_index_scores and csa_topk; idx [B][S][k] int32, out,
+ *   exactly as csa_topk(csa_index_scores(...)) writes it (the same scores, so
+ *   the same selection); no scores are written.
+ *   bf16 with 64 x 128 indexer heads, S >= 16, T <= 2048 and m >= 2 (CSA
+ *   prefill) runs one kernel: each workgroup scores 4 query rows into LDS and selects
+ *   from there (workspace unused).  Every other shape computes the scores into
+ *   the caller's workspace (csa_index_topk_workspace_size bytes) and selects
+ *   from it; a missing or small workspace is CSA_ERR_INVALID.
+ */
+csa_status_t csa_index_topk(const void *q_idx, const float *w_idx, const void *k_pool,
+                            int32_t *idx, const int32_t *q_pos, int32_t B, int32_t S, int32_t T,
+                            int32_t n_heads, int32_t head_dim, int32_t k, int32_t m,
+                            void *workspace, size_t ws_bytes, int32_t dtype, void *stream);
+
+/* Bytes of workspace csa_index_topk needs for this shape (0: fused on chip). */
+size_t csa_index_topk_workspace_size(int32_t B, int32_t S, int32_t T, int32_t n_heads,
+                                     int32_t head_dim, int32_t k, int32_t m, int32_t dtype);
+
+/*
  * csa_sparse_attn -- core attention of a CSA (or DSA) layer.  Page
  * "DeepSeek-V4", "Hybrid attention": multi-query attention with one shared
  * K=V head, partial RoPE on q, the output's rope slice rotated at position
@@ -237,10 +262,10 @@ csa_status_t csa_sparse_attn(const void *q, const void *kv_win, const int32_t *w
  * callers that cannot allocate device memory (code under HIP graph capture,
  * tight serving loops, harnesses that forbid allocation).  Same arguments,
  * result and kernels as csa_sparse_attn given a workspace of
- * csa_sparse_attn_workspace_size bytes; the split partials go to a 48 MiB
+ * csa_sparse_attn_workspace_size bytes; the split partials go to a 24 MiB
  * device array of the library instead (one per GPU, held until the process
  * ends; its address is looked up on the first call on each device).  The call
- * allocates nothing.  A shape whose split needs more than 48 MiB returns
+ * allocates nothing.  A shape whose split needs more than 24 MiB returns
  * CSA_ERR_UNSUPPORTED.  Every call on one GPU shares that array: calls that
  * overlap in time on one GPU (other streams, other host threads) race and
  * must be serialized by the caller.  The array needs no clearing (every

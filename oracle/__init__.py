@@ -257,6 +257,13 @@ def topk(scores, tpos, *, k: int, m: int) -> np.ndarray:
     return idx
 
 
+def index_topk(qI, wI, tpos, kI, *, k: int, m: int) -> np.ndarray:
+    """The fused indexer step ("DeepSeek-V3.2", section "DeepSeek Sparse
+    Attention": score every earlier key, keep the top-k): top-k of the index
+    scores, by definition the composition of the two."""
+    return topk(index_scores(qI, wI, tpos, kI, m=m), tpos, k=k, m=m)
+
+
 def attention(q, tpos, *, kv_win=None, win_pos0: int = 0, window: int = 0,
               pool=None, idx=None, m: int = 1, sink=None, rope_dim: int = 0,
               theta: float = 1.0, scale: float, dv: int | None = None,

@@ -39,6 +39,9 @@ def lib():
             "csa_index_scores": ([vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
                                   vp], ctypes.c_int),
             "csa_topk": ([vp, vp, vp, i32, i32, i32, i32, i32, vp], ctypes.c_int),
+            "csa_index_topk": ([vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, vp, sz,
+                                i32, vp], ctypes.c_int),
+            "csa_index_topk_workspace_size": ([i32] * 8, sz),
             "csa_sparse_attn": ([vp, vp, vp, i32, vp, i32, vp, i32, vp, vp, vp, i32, i32,
                                  i32, i32, i32, i32, vp, i32, i32, f32, vp, sz, i32, vp],
                                 ctypes.c_int),
@@ -63,7 +66,8 @@ def lib():
 EXPORTS = ("csa_last_error", "csa_version", "csa_rope_table", "csa_rope_table_yarn",
            "csa_compress",
            "csa_cache_append",
-           "csa_index_scores", "csa_topk", "csa_sparse_attn", "csa_sparse_attn_noalloc",
+           "csa_index_scores", "csa_topk", "csa_index_topk", "csa_index_topk_workspace_size",
+           "csa_sparse_attn", "csa_sparse_attn_noalloc",
            "csa_sparse_attn_workspace_size", "hca_attn", "hca_attn_workspace_size",
            "csa_grouped_out_proj")
 
@@ -183,6 +187,24 @@ def csa_topk(scores, q_pos, *, k: int, m: int, out=None) -> torch.Tensor:
         out = torch.empty((B, S, k), dtype=torch.int32, device=scores.device)
     _check(lib().csa_topk(_ptr(scores), _ptr(out), _ptr(q_pos), B, S, T, k, m, _stream()),
            "csa_topk")
+    return out
+
+
+def csa_index_topk(q_idx, w_idx, k_pool, q_pos, *, k: int, m: int, out=None,
+                   workspace=None) -> torch.Tensor:
+    """csa_topk(csa_index_scores(...)) in one call -> idx [B, S, k] int32."""
+    B, S, nI, cI = q_idx.shape
+    T = k_pool.shape[1]
+    assert w_idx.dtype == torch.float32 and k_pool.dtype == q_idx.dtype
+    assert q_pos.dtype == torch.int32 and q_pos.numel() == B
+    if out is None:
+        out = torch.empty((B, S, k), dtype=torch.int32, device=q_idx.device)
+    dt = _dtype(q_idx)
+    need = lib().csa_index_topk_workspace_size(B, S, T, nI, cI, k, m, dt)
+    ws, ws_bytes = _ws(need, q_idx.device, workspace)
+    _check(lib().csa_index_topk(_ptr(q_idx), _ptr(w_idx), _ptr(k_pool), _ptr(out), _ptr(q_pos),
+                                B, S, T, nI, cI, k, m, _ptr(ws), ws_bytes, dt, _stream()),
+           "csa_index_topk")
     return out
 
 

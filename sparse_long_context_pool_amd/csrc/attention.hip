@@ -217,8 +217,8 @@ struct KTile {
   static constexpr int TBYTES = TAIL ? 4 * TBLK : 16;
 };
 
-// Split workspace (fp32): [rows][nsplit][H][2] running (max, sum) in the log2
-// domain, then [rows][nsplit][H][dv] unnormalised partial outputs.
+// Split workspace: [rows][nsplit][H][2] fp32 running (max, sum) in the log2
+// domain, then [rows][nsplit][H][dv] unnormalised partial outputs in bf16.
 //
 // Work items: (query row, split of its key list, group of 64 heads).  The
 // grid is persistent (one workgroup per compute unit) and workgroup w takes
@@ -932,14 +932,17 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(MfmaArgs args) {
   // .. +3 of each block)
   auto output = [&](const Meta& m, int slot) __attribute__((always_inline)) {
     if (split_mode) {
-      float* po = args.ws + (size_t)args.rows * args.nsplit * H * 2 +
-                  ((size_t)m.row * args.nsplit + m.split) * H * dv + (size_t)m.h0 * dv;
+      // unnormalised partial outputs in bf16 (their scale is the split's
+      // running max; the merge weighs them in fp32)
+      u16* po = reinterpret_cast<u16*>(args.ws + (size_t)args.rows * args.nsplit * H * 2) +
+                ((size_t)m.row * args.nsplit + m.split) * H * dv + (size_t)m.h0 * dv;
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb)
-          *reinterpret_cast<f32x4*>(po + (size_t)(16 * mb + c16) * dv + cbase + 16 * nb + 4 * g) =
-              acc[mb][nb];
+          *reinterpret_cast<uint2*>(po + (size_t)(16 * mb + c16) * dv + cbase + 16 * nb + 4 * g) =
+              make_uint2(pack2(acc[mb][nb][0], acc[mb][nb][1]),
+                         pack2(acc[mb][nb][2], acc[mb][nb][3]));
       return;
     }
     // The bf16 results go out through LDS as 16-byte stores: the buffer the
@@ -1104,8 +1107,8 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnParams p, const f
   const int half = p.rope_dim >> 1, rbase = p.D - p.rope_dim;
   const float2* cs = reinterpret_cast<const float2*>(p.cs);
   const float* ml = ws + (size_t)row * nsplit * H * 2;
-  const float* po =
-      ws + (size_t)((long)p.B * p.S) * nsplit * H * 2 + (size_t)row * nsplit * H * dv;
+  const u16* po = reinterpret_cast<const u16*>(ws + (size_t)((long)p.B * p.S) * nsplit * H * 2) +
+                  (size_t)row * nsplit * H * dv;
   float M = p.sink ? p.sink[h] * kLog2e : -INFINITY;
   bool nan = false;
   for (int s = 0; s < nsplit; ++s) {
@@ -1119,10 +1122,9 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnParams p, const f
   for (int s = 0; s < nsplit; ++s) {
     const float f = exp2f(ml[(s * H + h) * 2] - Mb);
     L += f * ml[(s * H + h) * 2 + 1];
-    const float4* os = reinterpret_cast<const float4*>(po + ((size_t)s * H + h) * dv + c);
-    const float4 a = os[0], bq = os[1];
-    o[0] += f * a.x; o[1] += f * a.y; o[2] += f * a.z; o[3] += f * a.w;
-    o[4] += f * bq.x; o[5] += f * bq.y; o[6] += f * bq.z; o[7] += f * bq.w;
+    const uint4 u = *reinterpret_cast<const uint4*>(po + ((size_t)s * H + h) * dv + c);
+    o[0] += f * bf_lo(u.x); o[1] += f * bf_hi(u.x); o[2] += f * bf_lo(u.y); o[3] += f * bf_hi(u.y);
+    o[4] += f * bf_lo(u.z); o[5] += f * bf_hi(u.z); o[6] += f * bf_lo(u.w); o[7] += f * bf_hi(u.w);
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
 #pragma unroll
@@ -1192,7 +1194,8 @@ AttnPlan plan_attention(int B, int S, int H, int D, int dv, int rope_dim, int wi
     if (ns > 1) {
       pl.nsplit = ns;
       pl.tiles_per_split = tps;
-      pl.ws_bytes = (size_t)B * S * ns * H * (dv + 2) * sizeof(float);
+      // fp32 (max, sum) per head, then bf16 partial outputs
+      pl.ws_bytes = (size_t)B * S * ns * H * (2 * sizeof(float) + dv * 2);
     }
   }
   return pl;

@@ -131,7 +131,7 @@ csa_status_t run_attn(const char* fn, const csa::AttnParams& p, int npool_max,
 // Host code never uses the array's name as an address: the device address of
 // each GPU's copy comes from hipGetSymbolAddress, once per device, with that
 // device current, and only that address is passed to kernels.
-constexpr size_t kScratchBytes = size_t(48) << 20;
+constexpr size_t kScratchBytes = size_t(24) << 20;
 static __device__ __align__(256) unsigned char scratch[kScratchBytes];
 
 constexpr int kMaxDevices = 64;
@@ -305,6 +305,51 @@ csa_status_t csa_topk(const float* scores, int32_t* idx, const int32_t* q_pos, i
   if ((long)B * S == 0) return CSA_OK;
   if (!idx || !q_pos || (T > 0 && !scores)) return fail(CSA_ERR_INVALID, "%s: NULL tensor", fn);
   return launched(csa::launch_topk(scores, idx, q_pos, B, S, T, k, m, as_stream(stream)), fn);
+}
+
+size_t csa_index_topk_workspace_size(int32_t B, int32_t S, int32_t T, int32_t n_heads,
+                                     int32_t head_dim, int32_t k, int32_t m, int32_t dtype) {
+  if (B < 0 || S < 0 || T < 0 || n_heads < 1 || head_dim < 1 || k < 1 || m < 1) return 0;
+  if (csa::index_topk_fused_shape(S, T, n_heads, head_dim, k, m, dtype == CSA_BF16)) return 0;
+  return (size_t)B * S * T * sizeof(float);
+}
+
+csa_status_t csa_index_topk(const void* q_idx, const float* w_idx, const void* k_pool,
+                            int32_t* idx, const int32_t* q_pos, int32_t B, int32_t S, int32_t T,
+                            int32_t n_heads, int32_t head_dim, int32_t k, int32_t m,
+                            void* workspace, size_t ws_bytes, int32_t dtype, void* stream) {
+  const char* fn = "csa_index_topk";
+  if (!dtype_ok(dtype)) return fail(CSA_ERR_INVALID, "%s: unknown dtype %d", fn, dtype);
+  if (B < 0 || S < 0 || T < 0 || n_heads < 1 || head_dim < 1 || m < 1 || k < 1)
+    return fail(CSA_ERR_INVALID,
+                "%s: bad sizes (B=%d S=%d T=%d heads=%d dim=%d k=%d m=%d)", fn, B, S, T,
+                n_heads, head_dim, k, m);
+  if (head_dim % 8 != 0)
+    return fail(CSA_ERR_INVALID, "%s: head_dim=%d must be a multiple of 8", fn, head_dim);
+  if ((long)n_heads * head_dim + n_heads > 16384)
+    return fail(CSA_ERR_UNSUPPORTED, "%s: n_heads*head_dim=%d too large", fn,
+                n_heads * head_dim);
+  if ((long)B * S == 0) return CSA_OK;
+  if (!idx || !q_pos || (T > 0 && (!q_idx || !w_idx || !k_pool)))
+    return fail(CSA_ERR_INVALID, "%s: NULL tensor", fn);
+  if (T > 0 && (!aligned16(q_idx) || !aligned16(k_pool)))
+    return fail(CSA_ERR_INVALID, "%s: q_idx and k_pool must be 16-byte aligned", fn);
+  const hipStream_t s = as_stream(stream);
+  if (csa::index_topk_fused_shape(S, T, n_heads, head_dim, k, m, dtype == CSA_BF16))
+    return launched(csa::launch_index_topk_fused(q_idx, w_idx, k_pool, idx, q_pos, B, S, T, m,
+                                                 k, s),
+                    fn);
+  // other shapes: the scores go through the caller's workspace
+  const size_t need = (size_t)B * S * T * sizeof(float);
+  if (!workspace || ws_bytes < need || !aligned16(workspace))
+    return fail(CSA_ERR_INVALID,
+                "%s: this shape needs a 16-byte aligned workspace of %zu bytes (got %zu)", fn,
+                need, ws_bytes);
+  float* sc = reinterpret_cast<float*>(workspace);
+  hipError_t e = csa::launch_index_scores(q_idx, w_idx, k_pool, sc, q_pos, B, S, T, n_heads,
+                                          head_dim, m, dtype == CSA_BF16, s);
+  if (e != hipSuccess) return launched(e, fn);
+  return launched(csa::launch_topk(sc, idx, q_pos, B, S, T, k, m, s), fn);
 }
 
 size_t csa_sparse_attn_workspace_size(int32_t B, int32_t S, int32_t H, int32_t D, int32_t dv,

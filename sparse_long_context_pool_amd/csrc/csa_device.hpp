@@ -157,6 +157,11 @@ hipError_t launch_index_scores(const void* q_idx, const float* w_idx, const void
                                int n_heads, int head_dim, int m, bool bf16,
                                hipStream_t s);
 
+bool index_topk_fused_shape(int S, int T, int n_heads, int head_dim, int k, int m, bool bf16);
+hipError_t launch_index_topk_fused(const void* q_idx, const float* w_idx, const void* k_pool,
+                                   int* idx, const int* q_pos, int B, int S, int T, int m,
+                                   int k, hipStream_t s);
+
 hipError_t launch_topk(const float* scores, int* idx, const int* q_pos, int B, int S,
                        int T, int k, int m, hipStream_t s);
 

@@ -102,9 +102,10 @@ __global__ __launch_bounds__(64 * QR) void index_scores_mfma(
       wreg[mb][q] = *reinterpret_cast<const float4*>(w_idx + row * NI + 32 * mb + 8 * q +
                                                      4 * (lane >> 5));
 
-  // pool rows lo .. hi-1 of this sequence; tiles past hi read zeros
+  // pool rows lo .. hi-1 of this sequence
   const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<u16*>(k_pool + ((long)b * T + lo) * CI), 0, (hi - lo) * CI * 2, 0x00020000);
+  const int klim = (hi - lo) * CI * 2 - 16;   // the range's last 16-byte chunk
   // this wave's slices of a tile: 1 KiB slice g = 4 wave + q (rows 4g .. 4g+3);
   // lane l fills LDS slot l of the slice with chunk (l % 16) ^ (row % 16) of
   // row 4g + l / 16 (row % 16 depends on q only)
@@ -118,8 +119,12 @@ __global__ __launch_bounds__(64 * QR) void index_scores_mfma(
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int g = 4 * wave + q;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)(buf + g * 1024), 16, loff[q],
-                                               tile * TB + g * 1024, 0, 0);
+      // (every lane's address is clamped into the key rows of the range: a
+      // slot past the range re-reads its last chunk, which no score uses, so
+      // no load ever touches memory past the tensor)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)(buf + g * 1024), 16,
+                                               min(loff[q] + tile * TB + g * 1024, klim), 0, 0,
+                                               0);
     }
   };
   // B-fragment read address: row 32nb + lane%32, chunk 2ks + lane/32
@@ -129,9 +134,13 @@ __global__ __launch_bounds__(64 * QR) void index_scores_mfma(
     roff[ks] = (lane & 31) * 256 + 16 * ((2 * ks + (lane >> 5)) ^ (lane & 15));
 
   // scores of this row within the chunk: a bounded buffer store drops lanes
-  // past the row's ready entries (and the upper half, which holds copies)
+  // past the row's ready entries (and the upper half, which holds copies).
+  // A row of the block can end before the chunk starts (rows of one block
+  // differ in readiness by up to three entries at m = 1): its range is then
+  // empty, never negative, which would wrap the descriptor's byte count and
+  // let every store through.
   const __amdgpu_buffer_rsrc_t out_rs = __builtin_amdgcn_make_buffer_rsrc(
-      scores + row * T + lo, 0, (hi_my - lo) * 4, 0x00020000);
+      scores + row * T + lo, 0, max(hi_my - lo, 0) * 4, 0x00020000);
 
   // tile j: the products of the 8 rows on buffer J, four 32-entry blocks per
   // wave; blocks past the row's entries are skipped, but every block issues
@@ -214,6 +223,258 @@ __global__ __launch_bounds__(64 * QR) void index_scores_mfma(
   wait_vmcnt<0>();  // no load into LDS outlives the workgroup
 }
 
+// ---------------------------------------------------------------- fused top-k
+// Order-preserving 32-bit key of a score (-0 folded onto +0): larger score,
+// larger key; every non-NaN score maps above 0.
+__device__ __forceinline__ uint32_t topk_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) == 0u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Top-k of one row by one wave: the row's R scores (R <= 64 KPL) sit in LDS
+// (`sc`); lane l takes entries 64 u + l.  Radix select (most significant digit
+// first, up to three digits of up to 11 bits over the key's offset above the
+// row's smallest key) with the wave's own 2048-bin histogram `h` in LDS, then
+// an ordered compaction by ballots: every key above the k-th largest K, and
+// the first copies of K in index order, written in ascending index order,
+// then -1 in the remaining slots.  (LDS operations of one wave complete in
+// order, so the wave needs no barrier between its own writes and reads.)
+template <int KPL>
+__device__ __forceinline__ void wave_topk(const float* sc, uint32_t* h, int R, int k, int* out,
+                                          int lane) {
+  if (R <= k) {
+    for (int j = lane; j < k; j += 64) out[j] = j < R ? j : -1;
+    return;
+  }
+  uint32_t key[KPL];
+  uint32_t lo = 0xffffffffu, hi = 0u;
+#pragma unroll
+  for (int u = 0; u < KPL; ++u) {
+    const int j = 64 * u + lane;
+    key[u] = j < R ? topk_key(sc[j]) : 0u;
+    if (key[u] != 0u) { lo = min(lo, key[u]); hi = max(hi, key[u]); }
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    lo = min(lo, (uint32_t)__shfl_xor((int)lo, off, 64));
+    hi = max(hi, (uint32_t)__shfl_xor((int)hi, off, 64));
+  }
+#pragma unroll
+  for (int u = 0; u < KPL; ++u) key[u] = key[u] != 0u ? key[u] - lo + 1u : 0u;
+  const int nbits = 32 - (int)__builtin_clz(hi - lo + 1u);
+  uint32_t prefix = 0u, pmask = 0u;
+  int kk = k;
+  for (int pass = 0; pass < 3; ++pass) {
+    const int top = nbits - 11 * pass;
+    if (top <= 0) break;
+    const int shift = max(top - 11, 0);
+    const uint32_t dmask = (1u << (top - shift)) - 1u;
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+      *reinterpret_cast<uint4*>(h + 256 * q + 4 * lane) = make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+    for (int u = 0; u < KPL; ++u)
+      if (key[u] != 0u && (key[u] & pmask) == prefix) atomicAdd(&h[(key[u] >> shift) & dmask], 1u);
+    // lane l owns bins 32 l .. 32 l + 31: suffix sums over the bins above
+    int cnt[32];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const uint4 v = *reinterpret_cast<const uint4*>(h + 32 * lane + 4 * q);
+      cnt[4 * q] = (int)v.x; cnt[4 * q + 1] = (int)v.y;
+      cnt[4 * q + 2] = (int)v.z; cnt[4 * q + 3] = (int)v.w;
+    }
+    int loc = 0;
+#pragma unroll
+    for (int u = 0; u < 32; ++u) loc += cnt[u];
+    int suf = loc;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int v = __shfl_down(suf, off, 64);
+      if (lane + off < 64) suf += v;
+    }
+    int above = suf - loc, dig = -1, abv = 0;
+#pragma unroll
+    for (int u = 31; u >= 0; --u) {
+      if (above < kk && above + cnt[u] >= kk) { dig = 32 * lane + u; abv = above; }
+      above += cnt[u];
+    }
+    const uint64_t own = __ballot(dig >= 0);
+    const int src = (int)__builtin_ctzll(own);
+    const uint32_t digit = (uint32_t)__builtin_amdgcn_readlane(dig, src);
+    kk -= __builtin_amdgcn_readlane(abv, src);
+    prefix |= digit << shift;
+    pmask |= dmask << shift;
+  }
+  const uint32_t K = prefix;
+  const uint64_t lt = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+  int sel = 0, eqs = 0;
+#pragma unroll
+  for (int u = 0; u < KPL; ++u) {
+    const bool gt = key[u] > K, eq = key[u] == K;
+    const uint64_t me = __ballot(eq);
+    const bool take = gt || (eq && eqs + __popcll(me & lt) < kk);
+    const uint64_t mt = __ballot(take);
+    if (take) out[sel + __popcll(mt & lt)] = 64 * u + lane;
+    sel += __popcll(mt);
+    eqs += __popcll(me);
+  }
+  for (int j = sel + lane; j < k; j += 64) out[j] = -1;
+}
+
+// Index scores and top-k in one kernel (rows of at most TMAX ready entries):
+// the scores of index_scores_mfma (the same products, epilogue and order, so
+// the same bits) go to LDS instead of HBM, one TMAX-entry array per row, and
+// when every tile is done each wave selects its own row's top-k from its
+// array (wave_topk), its histogram in the freed tile buffers.  Nothing but the
+// index rows is written.
+template <int NI, int CI, int QR, int NT, int TMAX>
+__global__ __launch_bounds__(64 * QR) void index_topk_fused(
+    const u16* __restrict__ q_idx, const float* __restrict__ w_idx,
+    const u16* __restrict__ k_pool, int* __restrict__ idx, const int* __restrict__ q_pos,
+    int S, int T, int m, int k) {
+  constexpr int MB = NI / 32;
+  constexpr int KS = CI / 16;
+  constexpr int TB = NT * CI * 2;
+  static_assert(TB == QR * 4096, "each wave fills four 1 KiB slices of a tile");
+  static_assert(CI == 128 && NI <= 64, "shape");
+  static_assert(QR * 8192 <= 3 * TB, "the histograms fit the tile buffers");
+  __shared__ __attribute__((aligned(16))) unsigned char kb0[TB];
+  __shared__ __attribute__((aligned(16))) unsigned char kb1[TB];
+  __shared__ __attribute__((aligned(16))) unsigned char kb2[TB];
+  __shared__ __attribute__((aligned(16))) float sc[QR][TMAX];
+
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int b = blockIdx.z;
+  const int rb = gridDim.x - 1 - blockIdx.x;  // heaviest (latest) rows first
+  const int i0 = rb * QR;
+  const long qp = q_pos[b];
+  int r_wg = 0;
+#pragma unroll
+  for (int r = 0; r < QR; ++r)
+    if (i0 + r < S) r_wg = max(r_wg, ready_count(qp + i0 + r, m, T));
+  const int my_i = i0 + wave;
+  const bool valid = my_i < S;
+  const int R_my = valid ? ready_count(qp + my_i, m, T) : 0;
+  const long row = (long)b * S + (valid ? my_i : 0);
+
+  bf16x8 a[MB][KS];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      a[mb][ks] = as_bf16x8(*reinterpret_cast<const uint4*>(
+          q_idx + (row * NI + 32 * mb + (lane & 31)) * CI + 16 * ks + 8 * (lane >> 5)));
+  float4 wreg[MB][4];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      wreg[mb][q] = *reinterpret_cast<const float4*>(w_idx + row * NI + 32 * mb + 8 * q +
+                                                     4 * (lane >> 5));
+  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<u16*>(k_pool + (long)b * T * CI), 0, r_wg * CI * 2, 0x00020000);
+  const int klim = r_wg * CI * 2 - 16;        // the range's last 16-byte chunk
+  int loff[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    loff[q] = (lane >> 4) * 256 + 16 * ((lane & 15) ^ ((4 * q + (lane >> 4)) & 15));
+  auto issue = [&](auto JC, int tile) __attribute__((always_inline)) {
+    constexpr int J = decltype(JC)::value;
+    unsigned char* buf = J == 0 ? kb0 : J == 1 ? kb1 : kb2;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int g = 4 * wave + q;
+      // (every lane's address is clamped into the key rows of the range: a
+      // slot past the range re-reads its last chunk, which no score uses, so
+      // no load ever touches memory past the tensor)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)(buf + g * 1024), 16,
+                                               min(loff[q] + tile * TB + g * 1024, klim), 0, 0,
+                                               0);
+    }
+  };
+  int roff[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks)
+    roff[ks] = (lane & 31) * 256 + 16 * ((2 * ks + (lane >> 5)) ^ (lane & 15));
+  float* my_sc = sc[wave];
+  auto compute = [&](auto JC, int tile) __attribute__((always_inline)) {
+    constexpr int J = decltype(JC)::value;
+    const unsigned char* buf = J == 0 ? kb0 : J == 1 ? kb1 : kb2;
+#pragma unroll
+    for (int nb = 0; nb < NT / 32; ++nb) {
+      const int e0 = tile * NT + 32 * nb;
+      if (e0 < R_my) {
+        f32x16 acc[MB];
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[mb][r] = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const uint4 bv = *reinterpret_cast<const uint4*>(buf + nb * 8192 + roff[ks]);
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb)
+            acc[mb] = mfma32x32x16(a[mb][ks], as_bf16x8(bv), acc[mb]);
+        }
+        float p4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const float4 w4 = wreg[mb][q];
+            p4[0] += w4.x * relu_bits(acc[mb][4 * q]);
+            p4[1] += w4.y * relu_bits(acc[mb][4 * q + 1]);
+            p4[2] += w4.z * relu_bits(acc[mb][4 * q + 2]);
+            p4[3] += w4.w * relu_bits(acc[mb][4 * q + 3]);
+          }
+        float part = (p4[0] + p4[1]) + (p4[2] + p4[3]);
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part),
+                                                         __float_as_uint(part), false, false);
+        part = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+        if (lane < 32 && e0 + lane < R_my) my_sc[e0 + lane] = (part == 0.f) ? 0.f : part;
+      }
+    }
+  };
+
+  // tile j: wait for this wave's slices of tile j (the loads of tile j + 1
+  // may stay in flight), barrier, refill the buffer of tile j - 1 with tile
+  // j + 2, products
+  const int ntiles = (r_wg + NT - 1) / NT;
+  if (ntiles > 0) {
+    issue(std::integral_constant<int, 0>{}, 0);
+    issue(std::integral_constant<int, 1>{}, 1);
+    wait_vmcnt<4>();
+    lds_barrier();
+    issue(std::integral_constant<int, 2>{}, 2);
+    compute(std::integral_constant<int, 0>{}, 0);
+    wait_vmcnt<4>();
+    lds_barrier();
+    issue(std::integral_constant<int, 0>{}, 3);
+    compute(std::integral_constant<int, 1>{}, 1);
+    for (int j = 2; j < ntiles; j += 3) {
+      wait_vmcnt<4>();
+      lds_barrier();
+      issue(std::integral_constant<int, 1>{}, j + 2);
+      compute(std::integral_constant<int, 2>{}, j);
+      wait_vmcnt<4>();
+      lds_barrier();
+      issue(std::integral_constant<int, 2>{}, j + 3);
+      compute(std::integral_constant<int, 0>{}, j + 1);
+      wait_vmcnt<4>();
+      lds_barrier();
+      issue(std::integral_constant<int, 0>{}, j + 4);
+      compute(std::integral_constant<int, 1>{}, j + 2);
+    }
+  }
+  wait_vmcnt<0>();
+  lds_barrier();  // every wave is done with the tile buffers
+  if (!valid) return;
+  unsigned char* hb = (wave >> 1) == 0 ? kb0 : (wave >> 1) == 1 ? kb1 : kb2;
+  wave_topk<TMAX / 64>(my_sc, reinterpret_cast<uint32_t*>(hb + (wave & 1) * 8192), R_my, k,
+                       idx + row * k, lane);
+}
+
 // Streaming kernel for few query rows.  Workgroup (x = query row, y = pool
 // chunk); wave w scores 32-entry blocks w, w + 4, w + 8, ... of the chunk.
 // A block (32 rows x 256 bytes, contiguous in HBM) comes in with eight
@@ -225,7 +486,8 @@ __global__ __launch_bounds__(64 * QR) void index_scores_mfma(
 // lands, and its buffer is refilled at once, so two blocks stay in flight per
 // wave.  Query fragments (the A operand) stay in registers.  A wave with no
 // block leaves at once; the chunk is covered in whole rounds of two blocks
-// (blocks past the end read zeros and their scores are dropped).
+// (blocks past the end re-read the chunk's last bytes; their scores are
+// dropped).
 template <int NI, int CI>
 __global__ __launch_bounds__(256, 2) void index_scores_stream(
     const u16* __restrict__ q_idx, const float* __restrict__ w_idx,
@@ -252,11 +514,12 @@ __global__ __launch_bounds__(256, 2) void index_scores_stream(
   int blk = wave;
   if (blk >= nblk) return;  // wave-uniform
 
-  // key rows lo .. hi-1 of this sequence; reads past hi return zeros
+  // key rows lo .. hi-1 of this sequence
   const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<u16*>(k_pool + ((long)b * T + lo) * CI), 0, (hi - lo) * CI * 2, 0x00020000);
-  // per-lane source offset of load i within its 1 KiB (rows 4i .. 4i+3; the
-  // scalar offset adds the 1 KiB steps); it depends on i % 4 only
+  const int klim = (hi - lo) * CI * 2 - 16;   // the chunk's last 16-byte chunk
+  // per-lane source offset of load i within its 1 KiB (rows 4i .. 4i+3); it
+  // depends on i % 4 only
   int loff[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
@@ -267,9 +530,12 @@ __global__ __launch_bounds__(256, 2) void index_scores_stream(
     unsigned char* buf = decltype(JC)::value ? kb1[wave] : kb0[wave];
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
-      const int soff = bk * BLK + q * 1024;
+      // (addresses clamped into the chunk's rows: a block past the chunk
+      // re-reads its last 16 bytes, whose scores are dropped, so no load
+      // touches memory past the tensor)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)(buf + q * 1024), 16,
-                                               loff[q & 3], soff, 0, 0);
+                                               min(loff[q & 3] + bk * BLK + q * 1024, klim), 0,
+                                               0, 0);
     }
   };
   // head weights to LDS (lane l: 4 bytes at +4l), A fragments to registers:
@@ -394,6 +660,27 @@ __global__ __launch_bounds__(256) void index_scores_generic(
 }
 
 }  // namespace
+
+// Shapes the fused kernel takes: bf16, 64 x 128 indexer heads, at least 16
+// query rows per sequence, rows of at most 2048 entries, compressed pools
+// (m >= 2: the CSA prefill shape; token-level rows take the workspace path).
+bool index_topk_fused_shape(int S, int T, int n_heads, int head_dim, int k, int m, bool bf16) {
+  return bf16 && n_heads == 64 && head_dim == 128 && S >= 16 && T <= 2048 && k >= 1 && m >= 2;
+}
+
+hipError_t launch_index_topk_fused(const void* q_idx, const float* w_idx, const void* k_pool,
+                                   int* idx, const int* q_pos, int B, int S, int T, int m,
+                                   int k, hipStream_t s) {
+  if (B == 0 || S == 0) return hipSuccess;
+  // 4 rows per workgroup, 64-entry tiles: 48 KiB of tiles + 32 KiB of scores,
+  // two workgroups per compute unit
+  constexpr int QR = 4, NT = 16 * QR;
+  dim3 grid((S + QR - 1) / QR, 1, B);
+  hipLaunchKernelGGL((index_topk_fused<64, 128, QR, NT, 2048>), grid, dim3(64 * QR), 0, s,
+                     reinterpret_cast<const u16*>(q_idx), w_idx,
+                     reinterpret_cast<const u16*>(k_pool), idx, q_pos, S, T, m, k);
+  return hipGetLastError();
+}
 
 hipError_t launch_index_scores(const void* q_idx, const float* w_idx, const void* k_pool,
                                float* scores, const int* q_pos, int B, int S, int T,

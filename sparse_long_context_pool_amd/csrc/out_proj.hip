@@ -13,16 +13,16 @@
 // activations [rows][K] and nn.Linear-style weights [out][K].
 //
 // Matrix-core kernel (bf16, fp32 accumulation): a 256 x 256 output tile per
-// workgroup of 8 waves, K in steps of 32 through a 4-deep ring of LDS tiles
-// filled by direct-to-LDS 16-byte buffer loads (each wave loads 4 KiB of each
-// tile).  The MFMA (v_mfma_f32_32x32x16_bf16) takes weight rows as its A
+// workgroup of 8 waves, K in steps of 32 through a 5-deep ring of LDS tiles
+// (160 KiB: four tiles in flight) filled by direct-to-LDS 16-byte buffer loads
+// (each wave loads 4 KiB of each tile, spread between its products).  The MFMA (v_mfma_f32_32x32x16_bf16) takes weight rows as its A
 // operand and token rows as its B operand, so the accumulator of a lane holds
 // four consecutive output features of one token: 8-byte bf16 stores.  Each
 // wave owns 128 features x 64 tokens (4 x 2 blocks of 32 x 32).  Tile rows are
 // 64 bytes (four 16-byte chunks); chunk c of row r sits at c ^ ((r / 4) % 4),
 // so the 16 lanes of one LDS read phase (16 consecutive rows, one chunk) hit
-// distinct banks.  Rows past M read as zeros (bounded descriptors) and their
-// stores are dropped.
+// distinct banks.  Token rows past M re-read row M - 1 and their stores are
+// dropped (bounded descriptor).
 // Generic kernel (fp32, other shapes): one thread per output element, the
 // sum taken in k order.
 #include "csa_device.hpp"
@@ -33,7 +33,7 @@ namespace {
 constexpr int kGM = 256;     // tokens per workgroup tile
 constexpr int kGN = 256;     // output features per workgroup tile
 constexpr int kGK = 32;      // reduction step
-constexpr int kGStages = 4;  // LDS ring depth
+constexpr int kGStages = 5;  // LDS ring depth (160 KiB)
 constexpr int kGTileBytes = kGM * kGK * 2;  // one operand tile (16 KiB)
 
 struct GemmArgs {
@@ -53,7 +53,7 @@ __global__ __launch_bounds__(512) void gemm_nt_mfma(GemmArgs a) {
   const int m0 = blockIdx.x * kGM, n0 = blockIdx.y * kGN;
   const int wn = wave & 1, wm = wave >> 1;      // 2 x 4 waves: 128 features x 64 tokens each
 
-  // bounded descriptors: token rows past M read as zeros, their stores drop
+  // bounded descriptors (the store of a token row past M is dropped)
   const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<u16*>(a.x), 0, a.M * a.ldx * 2, 0x00020000);
   const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
@@ -70,7 +70,9 @@ __global__ __launch_bounds__(512) void gemm_nt_mfma(GemmArgs a) {
     const int r = 16 * (2 * wave + u) + (lane >> 2);
     const int lc = (lane & 3) ^ gswz(r);
     woff[u] = (((g * a.N + n0 + r) * a.K) + 8 * lc) * 2;
-    xoff[u] = (((m0 + r) * a.ldx) + g * a.K + 8 * lc) * 2;
+    // (token rows past M re-read row M - 1, whose products are never stored:
+    // no load touches memory past the tensor)
+    xoff[u] = ((min(m0 + r, a.M - 1) * a.ldx) + g * a.K + 8 * lc) * 2;
   }
   auto issue = [&](int kt, int st) __attribute__((always_inline)) {
     const int kb = kt * kGK * 2;
@@ -108,7 +110,19 @@ __global__ __launch_bounds__(512) void gemm_nt_mfma(GemmArgs a) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[bn][bm][e] = 0.f;
 
-  auto compute = [&](int st) __attribute__((always_inline)) {
+  // The products of a tile with the four loads of a later tile spread between
+  // them (one after every four products), so that the loads do not stall the
+  // wave in one burst.
+  auto issue_one = [&](int kt, int st, int u) __attribute__((always_inline)) {
+    const int kb = kt * kGK * 2;
+    if (u < 2)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          wrs, (lds_void*)(&lds[st][0][1024 * (2 * wave + u)]), 16, woff[u], kb, 0, 0);
+    else
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          xrs, (lds_void*)(&lds[st][1][1024 * (2 * wave + u - 2)]), 16, xoff[u - 2], kb, 0, 0);
+  };
+  auto compute_loading = [&](int st, bool ld, int kn, int sn) __attribute__((always_inline)) {
     const unsigned char* wt = lds[st][0];
     const unsigned char* xt = lds[st][1];
 #pragma unroll
@@ -119,26 +133,34 @@ __global__ __launch_bounds__(512) void gemm_nt_mfma(GemmArgs a) {
 #pragma unroll
       for (int bm = 0; bm < 2; ++bm) xf[bm] = as_bf16x8(*reinterpret_cast<const uint4*>(xt + xrd[bm][s]));
 #pragma unroll
-      for (int bn = 0; bn < 4; ++bn)
+      for (int bn = 0; bn < 4; ++bn) {
 #pragma unroll
         for (int bm = 0; bm < 2; ++bm) acc[bn][bm] = mfma32x32x16(wf[bn], xf[bm], acc[bn][bm]);
+        if ((bn & 1) == 1) {
+          __builtin_amdgcn_sched_barrier(0);
+          if (ld) issue_one(kn, sn, 2 * s + (bn >> 1));
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
     }
   };
 
   // Iteration kt: wait for this wave's loads of tile kt, barrier (every wave's
   // loads of tile kt have landed, and every wave is done with tile kt - 1,
-  // whose buffer takes tile kt + 3), refill, products.
+  // whose buffer takes tile kt + 4), products of tile kt with the loads of
+  // tile kt + 4.  (A wave has 4 loads per tile, issued in tile order.)
   const int nk = a.K / kGK;
 #pragma unroll
   for (int s = 0; s < kGStages - 1; ++s)
     if (s < nk) issue(s, s);
   for (int kt = 0; kt < nk; ++kt) {
-    if (kt + 2 < nk) wait_vmcnt<8>();
+    if (kt + 3 < nk) wait_vmcnt<12>();
+    else if (kt + 2 < nk) wait_vmcnt<8>();
     else if (kt + 1 < nk) wait_vmcnt<4>();
     else wait_vmcnt<0>();
     lds_barrier();
-    if (kt + kGStages - 1 < nk) issue(kt + kGStages - 1, (kt + kGStages - 1) % kGStages);
-    compute(kt % kGStages);
+    compute_loading(kt % kGStages, kt + kGStages - 1 < nk, kt + kGStages - 1,
+                    (kt + kGStages - 1) % kGStages);
   }
 
   // Output: accumulator register e of block (bn, bm) holds feature

@@ -49,6 +49,9 @@ def _compare_rows(wl, g, inp, caches, b, rows_local):
     by a near tie is still checked element by element)."""
     tol = BF16_ATOL if wl.dtype == "bf16" else F32_ATOL
     gi = host(g["idx"][b]).astype(np.int32)[rows_local] if wl.n_idx_heads else None
+    if wl.n_idx_heads:
+        # the fused selection equals the two-kernel one on the same scores
+        assert torch.equal(g["idx"][b], g["idx_two"][b])
     rows = np.asarray(rows_local) + b * wl.S
     res = oracle_rows(wl, inp, rows, caches, idx_override=gi)
     if wl.n_idx_heads:

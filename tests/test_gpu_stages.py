@@ -124,6 +124,10 @@ def _score_bound(q, w, k):
     # few rows per sequence, many blocks per wave (several rounds, ragged ends)
     ("bf16", 16, 8, 64, 128, 3000, 4, [11990 + 13 * b - 4000 * (b % 3) for b in range(16)]),
     ("bf16", 1, 200, 64, 128, 200, 1, [0]),         # token level (m=1)
+    # token level at a position that is not a multiple of 4: rows of one 4-row
+    # block end on both sides of a chunk start (a row's range within a chunk
+    # can be empty)
+    ("bf16", 1, 20, 64, 128, 5000, 1, [4990]),
     ("f32", 2, 33, 2, 32, 64, 4, [0, 100]),         # generic kernel
     ("bf16", 1, 20, 4, 64, 50, 4, [150]),           # generic kernel, bf16
 ])

@@ -297,6 +297,29 @@ def test_topk_matches_full_sort(orc):
     assert np.array_equal(orc.topk(scores, t, k=k, m=4), _brute_topk(scores, t, k, 4))
 
 
+def test_index_topk_against_float64_selection(orc):
+    """The fused indexer step picks the entries a float64 evaluation of the
+    score ranks highest (inputs drawn so that no two ready scores of a row lie
+    closer than the fp32 evaluation's error), ascending, -1 padded."""
+    r = rng(41)
+    n, nI, cI, T, k = 12, 8, 16, 40, 7
+    q = r.standard_normal((n, nI, cI)).astype(np.float32)
+    w = r.standard_normal((n, nI)).astype(np.float32)
+    kk = r.standard_normal((T, cI)).astype(np.float32)
+    t = np.array([3, 7, 11, 15, 27, 40, 80, 100, 159, 160, 30, 2])
+    dots = np.einsum("njc,wc->njw", q.astype(np.float64), kk.astype(np.float64))
+    s64 = np.einsum("nj,njw->nw", w.astype(np.float64), np.maximum(dots, 0.0))
+    got = orc.index_topk(q, w, t, kk, k=k, m=4)
+    for i in range(n):
+        R = brute.ready(int(t[i]), 4, T)
+        sv = np.sort(s64[i, :R])[::-1]
+        if R > k:
+            assert sv[k - 1] - sv[k] > 1e-3     # no near tie at the boundary: a unique set
+        best = sorted(np.argsort(-s64[i, :R], kind="stable")[:min(k, R)].tolist())
+        assert got[i, :len(best)].tolist() == best
+        assert np.all(got[i, len(best):] == -1)
+
+
 def test_topk_worked_example_and_padding(orc):
     """16 tokens, m=4, k=2: no entry before t=3, one at t=3..6, two from t=7."""
     T, k, m = 4, 2, 4
