@@ -606,6 +606,8 @@ def summarize_pmc(csv_paths):
             vals.setdefault(k, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
     out = []
     for k, d in vals.items():
+        if k.startswith(("at::", "__amd")):     # the benchmark's own fills, copies, spins
+            continue
         mean = {c: sum(v) / len(v) for c, v in d.items()}
         line = f"- `{k}`:"
         gui = mean.get("GRBM_GUI_ACTIVE")
