@@ -127,6 +127,28 @@ csa_status_t csa_compress(const void *x, const void *gate, const float *slot_bia
                           int32_t n_pos, int32_t pos0, int32_t dtype, void *stream);
 
 /*
+ * csa_compress_many -- several csa_compress passes in as few launches as
+ * possible (a prefill step's window rows, K=V pool and index keys: one
+ * launch).  Each pass has exactly csa_compress's arguments, meaning and
+ * requirements and produces exactly its result; the passes must not write
+ * memory another pass reads.  Passes the batched kernel takes (m = 1 copies
+ * without gate or bias, and windows of (1+overlap)m = 4 or 8 tokens) share a
+ * launch, up to four per launch; the others run as csa_compress runs them.
+ * Every pass is checked before anything is enqueued.  n_passes <= 16.
+ */
+typedef struct {
+    const void *x, *gate;
+    const float *slot_bias;
+    void *pool;
+    int32_t B, S, D, m, overlap, rope_dim;
+    const float *cs;
+    int32_t n_pos, pos0;
+} csa_compress_pass_t;
+
+csa_status_t csa_compress_many(const csa_compress_pass_t *passes, int32_t n_passes,
+                               int32_t dtype, void *stream);
+
+/*
  * csa_cache_append -- the decode-time cache update: appends n tokens per
  * sequence to the compressor state, the pool and the sliding window.  Page
  * "DeepSeek-V4", "Cache layers" (a sliding window of K=V rows plus the

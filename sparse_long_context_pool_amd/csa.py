@@ -17,6 +17,15 @@ CSA_F32, CSA_BF16 = 0, 1
 _lib = None
 
 
+class CompressPass(ctypes.Structure):
+    """csa_compress_pass_t: one csa_compress call's arguments."""
+    _fields_ = [("x", ctypes.c_void_p), ("gate", ctypes.c_void_p),
+                ("slot_bias", ctypes.c_void_p), ("pool", ctypes.c_void_p),
+                ("B", ctypes.c_int32), ("S", ctypes.c_int32), ("D", ctypes.c_int32),
+                ("m", ctypes.c_int32), ("overlap", ctypes.c_int32), ("rope_dim", ctypes.c_int32),
+                ("cs", ctypes.c_void_p), ("n_pos", ctypes.c_int32), ("pos0", ctypes.c_int32)]
+
+
 def lib():
     """The loaded libcsa.so (raises if it has not been built)."""
     global _lib
@@ -34,6 +43,7 @@ def lib():
             "csa_rope_table_yarn": ([vp, i32, i32, f64, f64, i32, f64, f64, vp], ctypes.c_int),
             "csa_compress": ([vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp, i32, i32,
                               i32, vp], ctypes.c_int),
+            "csa_compress_many": ([ctypes.POINTER(CompressPass), i32, i32, vp], ctypes.c_int),
             "csa_cache_append": ([vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
                                   i32, i32, i32, vp, i32, i32, vp], ctypes.c_int),
             "csa_index_scores": ([vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
@@ -64,7 +74,7 @@ def lib():
 
 
 EXPORTS = ("csa_last_error", "csa_version", "csa_rope_table", "csa_rope_table_yarn",
-           "csa_compress",
+           "csa_compress", "csa_compress_many",
            "csa_cache_append",
            "csa_index_scores", "csa_topk", "csa_index_topk", "csa_index_topk_workspace_size",
            "csa_sparse_attn", "csa_sparse_attn_noalloc",
@@ -141,6 +151,40 @@ def csa_compress(x, gate=None, slot_bias=None, *, m: int, overlap: int, rope_dim
                               overlap, rope_dim, _ptr(cs), n_pos, pos0, _dtype(x), _stream()),
            "csa_compress")
     return out
+
+
+def csa_compress_many(passes) -> list:
+    """Several csa_compress passes in one call.  ``passes`` is a sequence of
+    dicts with csa_compress's arguments (keys x, gate, slot_bias, m, overlap,
+    rope_dim, cs, pos0, out); all x share one dtype.  Returns the pools."""
+    passes = list(passes)
+    arr = (CompressPass * max(len(passes), 1))()
+    outs = []
+    dtype = _dtype(passes[0]["x"]) if passes else CSA_BF16
+    for q, p in enumerate(passes):
+        x, gate, sb = p["x"], p.get("gate"), p.get("slot_bias")
+        m, overlap = p["m"], p.get("overlap", 0)
+        B, S, D = x.shape
+        if _dtype(x) != dtype:
+            raise TypeError("csa_compress_many: all passes must share one dtype")
+        if gate is not None:
+            assert gate.shape == x.shape and gate.dtype == x.dtype
+        if sb is not None:
+            assert sb.dtype == torch.float32 and sb.shape == ((1 + overlap) * m, D)
+        out = p.get("out")
+        if out is None:
+            out = torch.empty((B, S // m, D), dtype=x.dtype, device=x.device)
+        cs = p.get("cs")
+        c = arr[q]
+        c.x, c.gate, c.slot_bias, c.pool, c.cs = (
+            None if t is None else _ptr(t).value for t in (x, gate, sb, out, cs))
+        c.B, c.S, c.D, c.m, c.overlap = B, S, D, m, overlap
+        c.rope_dim = p.get("rope_dim", 0)
+        c.n_pos = 0 if cs is None else cs.shape[0]
+        c.pos0 = p.get("pos0", 0)
+        outs.append(out)
+    _check(lib().csa_compress_many(arr, len(passes), dtype, _stream()), "csa_compress_many")
+    return outs
 
 
 def csa_cache_append(x, gate, slot_bias, count, ring_x, ring_g, pool, win=None, *, m: int,

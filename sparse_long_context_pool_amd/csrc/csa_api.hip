@@ -33,6 +33,13 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 bool dtype_ok(int32_t dt) { return dt == CSA_F32 || dt == CSA_BF16; }
 
+// the argument checks of one compressor pass (CSA_OK: valid; nothing to do
+// when B * (S / m) == 0)
+csa_status_t check_compress(const char* fn, const void* x, const void* gate,
+                            const float* slot_bias, void* pool, int32_t B, int32_t S, int32_t D,
+                            int32_t m, int32_t overlap, int32_t rope_dim, const float* cs,
+                            int32_t n_pos, int32_t pos0);
+
 hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
 // Shared checks of csa_sparse_attn / hca_attn.
@@ -207,6 +214,44 @@ csa_status_t csa_compress(const void* x, const void* gate, const float* slot_bia
                           int32_t n_pos, int32_t pos0, int32_t dtype, void* stream) {
   const char* fn = "csa_compress";
   if (!dtype_ok(dtype)) return fail(CSA_ERR_INVALID, "%s: unknown dtype %d", fn, dtype);
+  csa_status_t st = check_compress(fn, x, gate, slot_bias, pool, B, S, D, m, overlap, rope_dim,
+                                   cs, n_pos, pos0);
+  if (st != CSA_OK || (long)B * (S / m) == 0) return st;
+  return launched(csa::launch_compress(x, gate, slot_bias, pool, B, S, D, m, overlap,
+                                       rope_dim, cs, pos0, dtype == CSA_BF16,
+                                       as_stream(stream)),
+                  fn);
+}
+
+csa_status_t csa_compress_many(const csa_compress_pass_t* passes, int32_t n_passes,
+                               int32_t dtype, void* stream) {
+  const char* fn = "csa_compress_many";
+  if (!dtype_ok(dtype)) return fail(CSA_ERR_INVALID, "%s: unknown dtype %d", fn, dtype);
+  if (n_passes < 0 || n_passes > 16 || (n_passes > 0 && !passes))
+    return fail(CSA_ERR_INVALID, "%s: need 0 <= n_passes <= 16 and a pass array", fn);
+  csa::CompressPass cp[16];
+  int n = 0;
+  for (int q = 0; q < n_passes; ++q) {
+    const csa_compress_pass_t& c = passes[q];
+    char name[48];
+    snprintf(name, sizeof(name), "%s: pass %d", fn, q);
+    csa_status_t st = check_compress(name, c.x, c.gate, c.slot_bias, c.pool, c.B, c.S, c.D, c.m,
+                                     c.overlap, c.rope_dim, c.cs, c.n_pos, c.pos0);
+    if (st != CSA_OK) return st;
+    if ((long)c.B * (c.S / c.m) == 0) continue;
+    cp[n++] = csa::CompressPass{c.x, c.gate, c.slot_bias, c.pool, c.B, c.S, c.D, c.m, c.overlap,
+                                c.rope_dim, c.rope_dim > 0 ? c.cs : nullptr, c.pos0};
+  }
+  return launched(csa::launch_compress_many(cp, n, dtype == CSA_BF16, as_stream(stream)), fn);
+}
+
+}  // extern "C"
+
+namespace {
+csa_status_t check_compress(const char* fn, const void* x, const void* gate,
+                            const float* slot_bias, void* pool, int32_t B, int32_t S, int32_t D,
+                            int32_t m, int32_t overlap, int32_t rope_dim, const float* cs,
+                            int32_t n_pos, int32_t pos0) {
   if (B < 0 || S < 0 || D < 8 || m < 1 || (overlap != 0 && overlap != 1))
     return fail(CSA_ERR_INVALID, "%s: bad sizes (B=%d S=%d D=%d m=%d overlap=%d)", fn, B, S,
                 D, m, overlap);
@@ -227,11 +272,11 @@ csa_status_t csa_compress(const void* x, const void* gate, const float* slot_bia
                   "%s: entry positions pos0=%d .. %ld exceed the RoPE table (n_pos=%d)", fn,
                   pos0, (long)pos0 + (long)(T - 1) * m, n_pos);
   }
-  return launched(csa::launch_compress(x, gate, slot_bias, pool, B, S, D, m, overlap,
-                                       rope_dim, cs, pos0, dtype == CSA_BF16,
-                                       as_stream(stream)),
-                  fn);
+  return CSA_OK;
 }
+}  // namespace
+
+extern "C" {
 
 csa_status_t csa_cache_append(const void* x, const void* gate, const float* slot_bias,
                               void* ring_x, void* ring_g, void* pool, void* win,

@@ -146,6 +146,18 @@ hipError_t launch_compress(const void* x, const void* gate, const float* slot_bi
                            int rope_dim, const float* cs, int pos0, bool bf16,
                            hipStream_t s);
 
+// one pass of launch_compress_many (the arguments of launch_compress)
+struct CompressPass {
+  const void* x;
+  const void* gate;
+  const float* slot_bias;
+  void* pool;
+  int B, S, D, m, overlap, rope_dim;
+  const float* cs;
+  int pos0;
+};
+hipError_t launch_compress_many(const CompressPass* p, int n, bool bf16, hipStream_t s);
+
 hipError_t launch_cache_append(const void* x, const void* gate, const float* slot_bias,
                                void* ring_x, void* ring_g, void* pool, void* win,
                                const int* count, int B, int n, int D, int m, int overlap,

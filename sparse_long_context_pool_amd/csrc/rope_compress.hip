@@ -298,14 +298,13 @@ __device__ __forceinline__ void rope8_apply(float v[8], const float2 rr[4], int 
 // contiguous per load).
 constexpr int kCopyUnroll = 4;
 template <bool BF16>
-__global__ __launch_bounds__(256) void rope_copy_kernel(
+__device__ __forceinline__ void rope_copy_body(
     const void* __restrict__ x, void* __restrict__ pool, long rows, int S, int D,
-    int rope_dim, const float2* __restrict__ cs, int pos0) {
+    int rope_dim, const float2* __restrict__ cs, int pos0, unsigned i0) {
   // (index arithmetic in 32 bits: the launcher keeps rows x D/8 < 2^31)
   const unsigned nchunk = (unsigned)D >> 3;
   const unsigned n = (unsigned)rows * nchunk;
   const unsigned q = (n + kCopyUnroll - 1) / kCopyUnroll;
-  const unsigned i0 = blockIdx.x * blockDim.x + threadIdx.x;
   if (i0 >= q) return;
   const int rope_base = D - rope_dim;
   float v[kCopyUnroll][8];
@@ -334,6 +333,14 @@ __global__ __launch_bounds__(256) void rope_copy_kernel(
   }
 }
 
+template <bool BF16>
+__global__ __launch_bounds__(256) void rope_copy_kernel(
+    const void* __restrict__ x, void* __restrict__ pool, long rows, int S, int D,
+    int rope_dim, const float2* __restrict__ cs, int pos0) {
+  rope_copy_body<BF16>(x, pool, rows, S, D, rope_dim, cs, pos0,
+                       blockIdx.x * blockDim.x + threadIdx.x);
+}
+
 // Windows of exactly NR = m (1 + overlap) rows (the token-window sizes in
 // use): one thread per (entry, 8-channel chunk), so small widths (an index key
 // of 128 channels is 16 chunks) still fill whole waves.  The window's rows are
@@ -341,14 +348,13 @@ __global__ __launch_bounds__(256) void rope_copy_kernel(
 // the gate logits, the softmax weights and the weighted sum.  Rows before
 // token 0 (the first entry's overlap half) take no part.
 template <bool BF16, int NR>
-__global__ __launch_bounds__(256) void compress_rows_kernel(
+__device__ __forceinline__ void compress_rows_body(
     const void* __restrict__ x, const void* __restrict__ gate,
     const float* __restrict__ slot_bias, void* __restrict__ pool, int B, int S, int D, int m,
-    int overlap, int rope_dim, const float2* __restrict__ cs, int pos0) {
+    int overlap, int rope_dim, const float2* __restrict__ cs, int pos0, unsigned i) {
   // (index arithmetic in 32 bits: the launcher keeps B x T x D/8 < 2^31)
   const unsigned nchunk = (unsigned)D >> 3;
   const unsigned T = (unsigned)(S / m);
-  const unsigned i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= (unsigned)B * T * nchunk) return;
   const unsigned e = i / nchunk;
   const int ch = (int)(i - e * nchunk);
@@ -399,6 +405,55 @@ __global__ __launch_bounds__(256) void compress_rows_kernel(
   }
   if (rot) rope8_apply(val, rr, ch, rope_base);
   store8<BF16>(pool, ((long)b * T + w) * D + ch * 8, val);
+}
+
+template <bool BF16, int NR>
+__global__ __launch_bounds__(256) void compress_rows_kernel(
+    const void* __restrict__ x, const void* __restrict__ gate,
+    const float* __restrict__ slot_bias, void* __restrict__ pool, int B, int S, int D, int m,
+    int overlap, int rope_dim, const float2* __restrict__ cs, int pos0) {
+  compress_rows_body<BF16, NR>(x, gate, slot_bias, pool, B, S, D, m, overlap, rope_dim, cs, pos0,
+                               blockIdx.x * blockDim.x + threadIdx.x);
+}
+
+// Several compressor passes in one launch (a prefill step's window rows, K=V
+// pool and index keys): each pass takes a contiguous range of the grid's
+// workgroups and runs the per-thread body of its single-pass kernel (the
+// streaming copy, or the 8- or 4-row window), so the passes share one launch
+// and fill the chip together instead of one after another.
+constexpr int kMaxJobs = 4;
+struct CompressJob {
+  const void* x;
+  const void* gate;
+  const float* slot_bias;
+  void* pool;
+  const float2* cs;
+  int B, S, D, m, overlap, rope_dim, pos0;
+  int kind;        // 0: streaming copy (m = 1), 1: 8-row windows, 2: 4-row windows
+  int block0;      // first workgroup of the pass
+};
+struct CompressBatch {
+  CompressJob job[kMaxJobs];
+  int n;
+};
+
+template <bool BF16>
+__global__ __launch_bounds__(256) void compress_batch_kernel(CompressBatch bt) {
+  int j = 0;
+#pragma unroll
+  for (int q = 1; q < kMaxJobs; ++q)
+    if (q < bt.n && (int)blockIdx.x >= bt.job[q].block0) j = q;
+  const CompressJob& jb = bt.job[j];
+  const unsigned i = ((unsigned)blockIdx.x - (unsigned)jb.block0) * blockDim.x + threadIdx.x;
+  if (jb.kind == 0)
+    rope_copy_body<BF16>(jb.x, jb.pool, (long)jb.B * jb.S, jb.S, jb.D, jb.rope_dim, jb.cs,
+                         jb.pos0, i);
+  else if (jb.kind == 1)
+    compress_rows_body<BF16, 8>(jb.x, jb.gate, jb.slot_bias, jb.pool, jb.B, jb.S, jb.D, jb.m,
+                                jb.overlap, jb.rope_dim, jb.cs, jb.pos0, i);
+  else
+    compress_rows_body<BF16, 4>(jb.x, jb.gate, jb.slot_bias, jb.pool, jb.B, jb.S, jb.D, jb.m,
+                                jb.overlap, jb.rope_dim, jb.cs, jb.pos0, i);
 }
 
 // Cache update (page "DeepSeek-V4", section "Cache layers": the compressor's
@@ -584,6 +639,84 @@ hipError_t launch_rope_table(float* cs, int n_pos, int rope_dim, double theta, d
   hipLaunchKernelGGL(rope_table_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
                      reinterpret_cast<float2*>(cs), n_pos, rope_dim, theta, sc);
   return hipGetLastError();
+}
+
+namespace {
+// The batched kernel's kind for a pass (-1: it needs its own kernel), and its
+// workgroup count.
+int batch_kind(const void* gate, const float* slot_bias, int B, int S, int D, int m,
+               int overlap, long* blocks) {
+  const int T = S / m;
+  if (m == 1 && overlap == 0 && gate == nullptr && slot_bias == nullptr && D % 8 == 0 &&
+      (long)B * S * (D / 8) < (1L << 31)) {
+    *blocks = (((long)B * S * (D / 8) + kCopyUnroll - 1) / kCopyUnroll + 255) / 256;
+    return 0;
+  }
+  if ((m * (1 + overlap) == 8 || m * (1 + overlap) == 4) && D % 8 == 0 &&
+      (long)B * T * (D / 8) < (1L << 31)) {
+    *blocks = ((long)B * T * (D / 8) + 255) / 256;
+    return m * (1 + overlap) == 8 ? 1 : 2;
+  }
+  return -1;
+}
+}  // namespace
+
+hipError_t launch_compress_many(const CompressPass* p, int n, bool bf16, hipStream_t s) {
+  // passes the batched kernel takes go into launches of up to kMaxJobs passes;
+  // the others run on their own
+  CompressBatch bt;
+  bt.n = 0;
+  long blocks = 0;
+  int lone = 0;      // the pass of bt.job[0]
+  auto flush = [&]() -> hipError_t {
+    if (bt.n == 0) return hipSuccess;
+    if (bt.n == 1) {
+      // a lone pass runs on its own kernel, whose occupancy is set by its body
+      // alone (the batched kernel's register count is that of its largest body)
+      const CompressPass& c = p[lone];
+      bt.n = 0;
+      blocks = 0;
+      return launch_compress(c.x, c.gate, c.slot_bias, c.pool, c.B, c.S, c.D, c.m, c.overlap,
+                             c.rope_dim, c.cs, c.pos0, bf16, s);
+    }
+    if (bf16)
+      hipLaunchKernelGGL(compress_batch_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, s, bt);
+    else
+      hipLaunchKernelGGL(compress_batch_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, s, bt);
+    bt.n = 0;
+    blocks = 0;
+    return hipGetLastError();
+  };
+  for (int q = 0; q < n; ++q) {
+    const CompressPass& c = p[q];
+    if (c.S / c.m == 0 || c.B == 0) continue;
+    long nb = 0;
+    const int kind = batch_kind(c.gate, c.slot_bias, c.B, c.S, c.D, c.m, c.overlap, &nb);
+    if (kind < 0) {
+      hipError_t e = launch_compress(c.x, c.gate, c.slot_bias, c.pool, c.B, c.S, c.D, c.m,
+                                     c.overlap, c.rope_dim, c.cs, c.pos0, bf16, s);
+      if (e != hipSuccess) return e;
+      continue;
+    }
+    // one pass takes at most 2^23 workgroups; a launch keeps its grid under
+    // 2^31 work-items (the 32-bit thread index of the bodies)
+    if (blocks + nb > (1L << 23)) {
+      hipError_t e = flush();
+      if (e != hipSuccess) return e;
+    }
+    if (bt.n == 0) lone = q;
+    CompressJob& jb = bt.job[bt.n++];
+    jb.x = c.x; jb.gate = c.gate; jb.slot_bias = c.slot_bias; jb.pool = c.pool;
+    jb.cs = reinterpret_cast<const float2*>(c.cs);
+    jb.B = c.B; jb.S = c.S; jb.D = c.D; jb.m = c.m; jb.overlap = c.overlap;
+    jb.rope_dim = c.rope_dim; jb.pos0 = c.pos0; jb.kind = kind; jb.block0 = (int)blocks;
+    blocks += nb;
+    if (bt.n == kMaxJobs) {
+      hipError_t e = flush();
+      if (e != hipSuccess) return e;
+    }
+  }
+  return flush();
 }
 
 hipError_t launch_compress(const void* x, const void* gate, const float* slot_bias,

@@ -92,6 +92,26 @@ def test_invalid_arguments_are_rejected_on_the_host(L):
     assert L.csa_compress(nul, nul, nul, nul, 1, 3, 16, 4, 1, 0, nul, 0, 0, 1, nul) == 0
 
 
+def test_compress_many_checks_every_pass_before_enqueueing(L):
+    from sparse_long_context_pool_amd.csa import CompressPass
+    arr = (CompressPass * 17)()
+    for c in arr:
+        c.x = c.pool = 0x10000
+        c.B, c.S, c.D, c.m, c.overlap = 1, 64, 16, 4, 1
+    arr[1].D = 12                   # pass 1 invalid: nothing may be enqueued for pass 0
+    assert L.csa_compress_many(arr, 2, 1, None) == 1
+    assert b"pass 1" in L.csa_last_error()
+    arr[1].D = 16
+    arr[1].rope_dim, arr[1].cs, arr[1].n_pos = 8, 0x10000, 10   # table too short
+    assert L.csa_compress_many(arr, 2, 1, None) == 1
+    assert b"RoPE table" in L.csa_last_error()
+    assert L.csa_compress_many(arr, 17, 1, None) == 1           # too many passes
+    assert L.csa_compress_many(arr, 1, 7, None) == 1            # unknown dtype
+    assert L.csa_compress_many(None, 0, 1, None) == 0           # nothing to do
+    arr[0].S = 3                                                # no whole window: no work
+    assert L.csa_compress_many(arr, 1, 1, None) == 0
+
+
 def test_cache_append_rejects_bad_arguments_on_the_host(L):
     nul = None
     fake = ctypes.c_void_p(0x10000)

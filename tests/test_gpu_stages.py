@@ -109,6 +109,65 @@ def test_compress(ops, bf16, m, ov, D, rope, gate, bias):
         np.testing.assert_allclose(out[b], ref, rtol=rel, atol=1e-5)
 
 
+@pytest.mark.parametrize("bf16", [False, True])
+@pytest.mark.parametrize("mix", ["prefill", "dsa", "hca", "five"])
+def test_compress_many(ops, bf16, mix):
+    """csa_compress_many gives exactly what separate csa_compress calls give
+    (the passes batched into one launch, the rest on their own kernels), and
+    the prefill trio matches the oracle."""
+    dt = torch.bfloat16 if bf16 else torch.float32
+    theta = 160000.0
+    B, S, D, Di, rope = 2, 4 * 37 + 3, 512, 128, 64
+    x = rnd((B, S, D), 11, bf16)
+    g = rnd((B, S, D), 12, bf16)
+    xi = rnd((B, S, Di), 13, bf16)
+    gi = rnd((B, S, Di), 14, bf16)
+    cs = ops.csa_rope_table(S + 40, rope, theta)
+    X, G, XI, GI = (dev(a, dt) for a in (x, g, xi, gi))
+    win = dict(x=X, m=1, overlap=0, rope_dim=rope, cs=cs, pos0=5)
+    kv = dict(x=X, gate=G, m=4, overlap=1, rope_dim=rope, cs=cs, pos0=5)
+    ki = dict(x=XI, gate=GI, m=4, overlap=1)
+    if mix == "prefill":
+        passes = [win, kv, ki]
+    elif mix == "dsa":
+        passes = [win, dict(x=XI, m=1, overlap=0)]
+    elif mix == "hca":        # m = 128: not batchable, runs on its own kernel between batched ones
+        passes = [win, dict(x=X, gate=G, m=128, overlap=0, rope_dim=rope, cs=cs, pos0=5), ki]
+    else:                     # more passes than one launch takes, with a slot bias and m = 8
+        sb = dev(rnd((8, Di), 15, False), torch.float32)
+        passes = [win, kv, ki, dict(x=XI, gate=GI, slot_bias=sb, m=8, overlap=0),
+                  dict(x=XI, gate=GI, m=2, overlap=1)]
+    many = [host(o) for o in ops.csa_compress_many(passes)]
+    torch.cuda.synchronize()
+    for q, p in enumerate(passes):
+        one = host(ops.csa_compress(p["x"], p.get("gate"), p.get("slot_bias"), m=p["m"],
+                                    overlap=p["overlap"], rope_dim=p.get("rope_dim", 0),
+                                    cs=p.get("cs"), pos0=p.get("pos0", 0)))
+        assert np.array_equal(many[q].view(np.uint8), one.view(np.uint8)), (mix, q)
+    if mix == "prefill":
+        rel = 2.0 ** -7 if bf16 else 1e-5
+        for b in range(B):
+            refs = [oracle.compress(x[b], None, None, m=1, overlap=0, rope_dim=rope,
+                                    theta=theta, pos0=5, round_bf16=bf16),
+                    oracle.compress(x[b], g[b], None, m=4, overlap=1, rope_dim=rope,
+                                    theta=theta, pos0=5, round_bf16=bf16),
+                    oracle.compress(xi[b], gi[b], None, m=4, overlap=1, round_bf16=bf16)]
+            for q in range(3):
+                np.testing.assert_allclose(many[q][b], refs[q], rtol=rel, atol=1e-5)
+
+
+def test_compress_many_empty_and_degenerate_passes(ops):
+    """No passes, and passes with no whole window, enqueue nothing; a valid
+    pass beside them is still computed."""
+    assert ops.csa_compress_many([]) == []
+    x = dev(rnd((1, 3, 64), 16, True), torch.bfloat16)
+    y = dev(rnd((2, 16, 64), 17, True), torch.bfloat16)
+    a, b = ops.csa_compress_many([dict(x=x, m=4, overlap=1), dict(x=y, m=4, overlap=1)])
+    assert a.shape == (1, 0, 64)
+    ref = host(ops.csa_compress(y, m=4, overlap=1))
+    assert np.array_equal(host(b).view(np.uint8), ref.view(np.uint8))
+
+
 # ------------------------------------------------------------------ index scores
 def _score_bound(q, w, k):
     tot = np.einsum("nj,njw->nw", np.abs(w).astype(np.float64),
