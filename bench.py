@@ -11,7 +11,7 @@ inputs already resident in HBM (the RoPE table is model set-up: built once,
 timed on its own and reported beside the step).  Each stage is timed with HIP events on the
 stream its kernels run on; ``roofline`` reports the dominant kernel's
 algorithmic FLOP/s or bytes/s against the MI355X peak.  CSA decode (64 x 1
-token after 131072 cached tokens) is reported in us/step, and the HCA and DSA
+token at position 131071, closing a pool entry) is reported in us/step, and the HCA and DSA
 workloads in tokens/s.  ``cpu_baseline`` times the CPU oracle on a stratified
 sample of the prefill rows.
 
@@ -72,8 +72,14 @@ def work_counts(wl):
         w["compress"] = ("hbm", c)
     if wl.decode:
         # the new token into both caches: x and gate read, written to the
-        # compressor buffers, and (K=V) rotated into the window
-        w["cache_append"] = ("hbm", B * wl.S * (wl.D * e * 5 + wl.idx_dim * e * 4))
+        # compressor buffers, and (K=V) rotated into the window; a token that
+        # closes an entry also reads the other (1+overlap)m - 1 rows of x and
+        # gate from the buffers and writes the pooled entry
+        L = (1 + wl.overlap) * wl.m
+        closes = (wl.q_pos0 + 1) % wl.m == 0
+        rows_kv = 5 + (2 * (L - 1) + 1 if closes else 0)
+        rows_idx = 4 + (2 * (L - 1) + 1 if closes else 0)
+        w["cache_append"] = ("hbm", B * wl.S * (wl.D * rows_kv + wl.idx_dim * rows_idx) * e)
     if wl.n_idx_heads:
         pairs = int(R.sum()) * B
         if wl.decode:   # streams the index-key pool once: HBM-bound

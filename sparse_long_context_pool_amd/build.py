@@ -2,6 +2,9 @@
 
 Each csrc/*.hip file is compiled on its own with hipcc for gfx950 only, then
 the objects are linked into sparse_long_context_pool_amd/libcsa.so in-tree.
+The same objects, with the C ABI compiled with CSA_DEBUG, also make
+libcsa_debug.so: it checks device-side inputs (attention index rows) before
+each launch, synchronizing the caller's stream.
 Usage: python -m sparse_long_context_pool_amd.build [--resource-usage]
 """
 from __future__ import annotations
@@ -28,8 +31,12 @@ HIP_FLAGS = [
 ]
 
 
-def _compile(src: str, extra: list[str]) -> str:
-    obj = os.path.join(BUILD, os.path.basename(src).replace(".hip", ".o"))
+DEBUG_LIB = os.path.join(PKG, "libcsa_debug.so")
+API_SRC = os.path.join(CSRC, "csa_api.hip")
+
+
+def _compile(src: str, extra: list[str], suffix: str = "") -> str:
+    obj = os.path.join(BUILD, os.path.basename(src).replace(".hip", suffix + ".o"))
     cmd = [HIPCC, *HIP_FLAGS, *extra, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     out = (r.stdout + r.stderr)
@@ -47,13 +54,18 @@ def build(resource_usage: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
     extra = ["-Rpass-analysis=kernel-resource-usage"] if resource_usage else []
-    with ThreadPoolExecutor(min(8, len(srcs))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, extra), srcs))
-    tmp = LIB + ".tmp"
-    subprocess.run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs],
-                   check=True)
-    _check_stubs(tmp)
-    os.replace(tmp, LIB)
+    jobs = [(s, extra, "") for s in srcs] + [(API_SRC, extra + ["-DCSA_DEBUG"], "_debug")]
+    with ThreadPoolExecutor(min(8, len(jobs))) as ex:
+        objs = list(ex.map(lambda j: _compile(*j), jobs))
+    api_debug = objs.pop()
+    for lib, members in ((LIB, objs),
+                         (DEBUG_LIB, [api_debug if os.path.basename(o) == "csa_api.o" else o
+                                      for o in objs])):
+        tmp = lib + ".tmp"
+        subprocess.run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp,
+                        *members], check=True)
+        _check_stubs(tmp)
+        os.replace(tmp, lib)
     return LIB
 
 

@@ -13,6 +13,8 @@ import os
 import torch
 
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libcsa.so")
+# the same library built with device-side input checks (synchronizes each checked call)
+DEBUG_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libcsa_debug.so")
 CSA_F32, CSA_BF16 = 0, 1
 _lib = None
 
@@ -30,47 +32,62 @@ def lib():
     """The loaded libcsa.so (raises if it has not been built)."""
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB_PATH):
-            raise RuntimeError(f"{_LIB_PATH} is missing: build it with "
-                               "`python -m sparse_long_context_pool_amd.build`")
-        L = ctypes.CDLL(_LIB_PATH)
-        vp, i32, f32, f64, sz = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_float,
-                                 ctypes.c_double, ctypes.c_size_t)
-        sig = {
-            "csa_last_error": ([], ctypes.c_char_p),
-            "csa_version": ([], ctypes.c_char_p),
-            "csa_rope_table": ([vp, i32, i32, f64, vp], ctypes.c_int),
-            "csa_rope_table_yarn": ([vp, i32, i32, f64, f64, i32, f64, f64, vp], ctypes.c_int),
-            "csa_compress": ([vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp, i32, i32,
-                              i32, vp], ctypes.c_int),
-            "csa_compress_many": ([ctypes.POINTER(CompressPass), i32, i32, vp], ctypes.c_int),
-            "csa_cache_append": ([vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
-                                  i32, i32, i32, vp, i32, i32, vp], ctypes.c_int),
-            "csa_index_scores": ([vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
-                                  vp], ctypes.c_int),
-            "csa_topk": ([vp, vp, vp, i32, i32, i32, i32, i32, vp], ctypes.c_int),
-            "csa_index_topk": ([vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, vp, sz,
-                                i32, vp], ctypes.c_int),
-            "csa_index_topk_workspace_size": ([i32] * 8, sz),
-            "csa_sparse_attn": ([vp, vp, vp, i32, vp, i32, vp, i32, vp, vp, vp, i32, i32,
-                                 i32, i32, i32, i32, vp, i32, i32, f32, vp, sz, i32, vp],
-                                ctypes.c_int),
-            "csa_sparse_attn_noalloc": ([vp, vp, vp, i32, vp, i32, vp, i32, vp, vp, vp, i32,
-                                         i32, i32, i32, i32, i32, vp, i32, i32, f32, i32, vp],
-                                        ctypes.c_int),
-            "csa_sparse_attn_workspace_size": ([i32] * 9, sz),
-            "hca_attn": ([vp, vp, vp, i32, vp, i32, i32, vp, vp, vp, i32, i32, i32, i32,
-                          i32, i32, vp, i32, i32, f32, vp, sz, i32, vp], ctypes.c_int),
-            "hca_attn_workspace_size": ([i32] * 9, sz),
-            "csa_grouped_out_proj": ([vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp],
-                                     ctypes.c_int),
-        }
-        for name, (args, res) in sig.items():
-            fn = getattr(L, name)
-            fn.argtypes = args
-            fn.restype = res
-        _lib = L
+        _lib = load(_LIB_PATH)
     return _lib
+
+
+def use_library(which):
+    """Make the bindings call another build: a path (e.g. DEBUG_LIB_PATH) or a
+    handle that load() or use_library() returned.  Returns the handle they
+    called before (None if none was loaded yet)."""
+    global _lib
+    prev = _lib
+    _lib = load(which) if isinstance(which, str) else which
+    return prev
+
+
+def load(path: str):
+    """A libcsa build at `path` with every entry point's signature set."""
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with "
+                           "`python -m sparse_long_context_pool_amd.build`")
+    L = ctypes.CDLL(path)
+    vp, i32, f32, f64, sz = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_float,
+                             ctypes.c_double, ctypes.c_size_t)
+    sig = {
+        "csa_last_error": ([], ctypes.c_char_p),
+        "csa_version": ([], ctypes.c_char_p),
+        "csa_rope_table": ([vp, i32, i32, f64, vp], ctypes.c_int),
+        "csa_rope_table_yarn": ([vp, i32, i32, f64, f64, i32, f64, f64, vp], ctypes.c_int),
+        "csa_compress": ([vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp, i32, i32,
+                          i32, vp], ctypes.c_int),
+        "csa_compress_many": ([ctypes.POINTER(CompressPass), i32, i32, vp], ctypes.c_int),
+        "csa_cache_append": ([vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
+                              i32, i32, i32, vp, i32, i32, vp], ctypes.c_int),
+        "csa_index_scores": ([vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
+                              vp], ctypes.c_int),
+        "csa_topk": ([vp, vp, vp, i32, i32, i32, i32, i32, vp], ctypes.c_int),
+        "csa_index_topk": ([vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, vp, sz,
+                            i32, vp], ctypes.c_int),
+        "csa_index_topk_workspace_size": ([i32] * 8, sz),
+        "csa_sparse_attn": ([vp, vp, vp, i32, vp, i32, vp, i32, vp, vp, vp, i32, i32,
+                             i32, i32, i32, i32, vp, i32, i32, f32, vp, sz, i32, vp],
+                            ctypes.c_int),
+        "csa_sparse_attn_noalloc": ([vp, vp, vp, i32, vp, i32, vp, i32, vp, vp, vp, i32,
+                                     i32, i32, i32, i32, i32, vp, i32, i32, f32, i32, vp],
+                                    ctypes.c_int),
+        "csa_sparse_attn_workspace_size": ([i32] * 9, sz),
+        "hca_attn": ([vp, vp, vp, i32, vp, i32, i32, vp, vp, vp, i32, i32, i32, i32,
+                      i32, i32, vp, i32, i32, f32, vp, sz, i32, vp], ctypes.c_int),
+        "hca_attn_workspace_size": ([i32] * 9, sz),
+        "csa_grouped_out_proj": ([vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp],
+                                 ctypes.c_int),
+    }
+    for name, (args, res) in sig.items():
+        fn = getattr(L, name)
+        fn.argtypes = args
+        fn.restype = res
+    return L
 
 
 EXPORTS = ("csa_last_error", "csa_version", "csa_rope_table", "csa_rope_table_yarn",

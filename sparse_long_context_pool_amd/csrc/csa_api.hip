@@ -166,13 +166,58 @@ csa_status_t scratch_on_current_device(const char* fn, void** ptr) {
   return CSA_OK;
 }
 
+#ifdef CSA_DEBUG
+// ---- debug build: the index rows are checked on the device before attention
+// runs (the stream is synchronized, so a debug build is not for graph
+// capture).  The two result words live in a device array of the library,
+// addressed like the scratch array above.
+static __device__ __align__(16) int dbg_res[4];
+std::mutex g_dbg_mu;
+void* g_dbg_ptr[kMaxDevices] = {};
+
+csa_status_t debug_check_idx(const char* fn, const int32_t* idx, long n, int32_t T,
+                             hipStream_t s) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0 || dev >= kMaxDevices)
+    return fail(CSA_ERR_LAUNCH, "%s: debug check: no usable device", fn);
+  std::lock_guard<std::mutex> lock(g_dbg_mu);
+  if (!g_dbg_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(dbg_res));
+    if (e != hipSuccess || p == nullptr)
+      return fail(CSA_ERR_LAUNCH, "%s: debug check: hipGetSymbolAddress failed: %s", fn,
+                  hipGetErrorString(e));
+    g_dbg_ptr[dev] = p;
+  }
+  int* res = static_cast<int*>(g_dbg_ptr[dev]);
+  const int init[2] = {0, 0x7fffffff};
+  int got[2] = {0, 0};
+  e = hipMemcpyAsync(res, init, sizeof(init), hipMemcpyHostToDevice, s);
+  if (e == hipSuccess) e = csa::launch_check_idx(idx, n, T, res, s);
+  if (e == hipSuccess) e = hipMemcpyAsync(got, res, sizeof(got), hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess)
+    return fail(CSA_ERR_LAUNCH, "%s: debug check of idx failed: %s", fn, hipGetErrorString(e));
+  if (got[0] != 0)
+    return fail(CSA_ERR_INVALID,
+                "%s: idx holds %d entries outside [-1, T=%d); the first at element %d", fn,
+                got[0], T, got[1]);
+  return CSA_OK;
+}
+#endif
+
 }  // namespace
 
 extern "C" {
 
 const char* csa_last_error(void) { return g_err; }
 
+#ifdef CSA_DEBUG
+const char* csa_version(void) { return "csa-mi355x 0.1 (gfx950, debug checks)"; }
+#else
 const char* csa_version(void) { return "csa-mi355x 0.1 (gfx950)"; }
+#endif
 
 csa_status_t csa_rope_table(float* cs, int32_t n_pos, int32_t rope_dim, double theta,
                             void* stream) {
@@ -434,6 +479,12 @@ csa_status_t csa_sparse_attn(const void* q, const void* kv_win, const int32_t* w
     p.k = 0;
     p.dense = 0;
   }
+#ifdef CSA_DEBUG
+  if (p.k > 0) {
+    st = debug_check_idx(fn, idx, (long)B * S * k, T, as_stream(stream));
+    if (st != CSA_OK) return st;
+  }
+#endif
   return run_attn(fn, p, p.k, workspace, ws_bytes, as_stream(stream));
 }
 
@@ -460,6 +511,12 @@ csa_status_t csa_sparse_attn_noalloc(const void* q, const void* kv_win,
     p.k = 0;
     p.dense = 0;
   }
+#ifdef CSA_DEBUG
+  if (p.k > 0) {
+    st = debug_check_idx(fn, idx, (long)B * S * k, T, as_stream(stream));
+    if (st != CSA_OK) return st;
+  }
+#endif
   // the same plan as csa_sparse_attn with a large enough workspace
   const csa::AttnPlan plan =
       csa::plan_attention(p.B, p.S, p.H, p.D, p.dv, p.rope_dim, p.window, p.k, p.bf16,

@@ -223,4 +223,8 @@ AttnPlan plan_attention(int B, int S, int H, int D, int dv, int rope_dim, int wi
 hipError_t launch_attention(const AttnParams& p, const AttnPlan& plan, void* ws,
                             hipStream_t s);
 
+// debug builds: counts the entries of idx[0 .. n) outside [-1, T) into res[0]
+// and the first such element index into res[1] (res preset to {0, INT_MAX})
+hipError_t launch_check_idx(const int* idx, long n, int T, int* res, hipStream_t s);
+
 }  // namespace csa

@@ -469,6 +469,7 @@ __global__ __launch_bounds__(256) void compress_batch_kernel(CompressBatch bt) {
 // it (j >= count), else from the ring.  Pooled as the compressor pools them:
 // per channel the max of the logits, the weights, the weighted sum.
 // entry w of sequence b, channels [8ch, 8ch + 8)
+constexpr int kEntryRows = 8;
 template <bool BF16>
 __device__ __forceinline__ void cache_entry(
     const void* __restrict__ x, const void* __restrict__ gate,
@@ -479,14 +480,15 @@ __device__ __forceinline__ void cache_entry(
   const int L = (1 + overlap) * m;
   const long first = (w - overlap) * m;             // token held by slot 0
   const long j0 = first < 0 ? 0 : first, j1 = (w + 1) * m;
+  // (j >= 0 and counts below 2^31: the ring slot is a 32-bit remainder)
   auto row_x = [&](long j, float v[8]) {
     if (j >= c0) load8<BF16>(x, ((long)b * n + (j - c0)) * D + ch * 8, v);
-    else load8<BF16>(ring_x, ((long)b * L + j % L) * D + ch * 8, v);
+    else load8<BF16>(ring_x, ((long)b * L + (unsigned)j % (unsigned)L) * D + ch * 8, v);
   };
   auto row_a = [&](long j, float a[8]) {
     if (gate) {
       if (j >= c0) load8<BF16>(gate, ((long)b * n + (j - c0)) * D + ch * 8, a);
-      else load8<BF16>(ring_g, ((long)b * L + j % L) * D + ch * 8, a);
+      else load8<BF16>(ring_g, ((long)b * L + (unsigned)j % (unsigned)L) * D + ch * 8, a);
     } else {
 #pragma unroll
       for (int v = 0; v < 8; ++v) a[v] = 0.f;
@@ -498,29 +500,60 @@ __device__ __forceinline__ void cache_entry(
       a[4] += s1.x; a[5] += s1.y; a[6] += s1.z; a[7] += s1.w;
     }
   };
-  float mx[8], sm[8], ac[8];
+  float val[8];
+  if (L <= kEntryRows) {
+    // windows of up to 8 rows: every row's loads in flight together, then the
+    // max, the weights and the weighted sum in row order (the compressor
+    // kernels' arithmetic, so an entry pooled here equals theirs bit for bit)
+    float xv[kEntryRows][8], a[kEntryRows][8];
 #pragma unroll
-  for (int v = 0; v < 8; ++v) { mx[v] = -INFINITY; sm[v] = 0.f; ac[v] = 0.f; }
-  for (long j = j0; j < j1; ++j) {
-    float a[8];
-    row_a(j, a);
-#pragma unroll
-    for (int v = 0; v < 8; ++v) mx[v] = fmaxf(mx[v], a[v]);
-  }
-  for (long j = j0; j < j1; ++j) {
-    float a[8], xv[8];
-    row_a(j, a);
-    row_x(j, xv);
+    for (int r = 0; r < kEntryRows; ++r) {
+      const long j = first + r;
+      if (r < L && j >= 0) {
+        row_a(j, a[r]);
+        row_x(j, xv[r]);
+      }
+    }
 #pragma unroll
     for (int v = 0; v < 8; ++v) {
-      const float ev = __expf(a[v] - mx[v]);
-      sm[v] += ev;
-      ac[v] += ev * xv[v];
-    }
-  }
-  float val[8];
+      float mx = -INFINITY;
 #pragma unroll
-  for (int v = 0; v < 8; ++v) val[v] = ac[v] / sm[v];
+      for (int r = 0; r < kEntryRows; ++r)
+        if (r < L && first + r >= 0) mx = fmaxf(mx, a[r][v]);
+      float sm = 0.f, ac = 0.f;
+#pragma unroll
+      for (int r = 0; r < kEntryRows; ++r)
+        if (r < L && first + r >= 0) {
+          const float ev = __expf(a[r][v] - mx);
+          sm += ev;
+          ac += ev * xv[r][v];
+        }
+      val[v] = ac / sm;
+    }
+  } else {
+    float mx[8], sm[8], ac[8];
+#pragma unroll
+    for (int v = 0; v < 8; ++v) { mx[v] = -INFINITY; sm[v] = 0.f; ac[v] = 0.f; }
+    for (long j = j0; j < j1; ++j) {
+      float a[8];
+      row_a(j, a);
+#pragma unroll
+      for (int v = 0; v < 8; ++v) mx[v] = fmaxf(mx[v], a[v]);
+    }
+    for (long j = j0; j < j1; ++j) {
+      float a[8], xv[8];
+      row_a(j, a);
+      row_x(j, xv);
+#pragma unroll
+      for (int v = 0; v < 8; ++v) {
+        const float ev = __expf(a[v] - mx[v]);
+        sm[v] += ev;
+        ac[v] += ev * xv[v];
+      }
+    }
+#pragma unroll
+    for (int v = 0; v < 8; ++v) val[v] = ac[v] / sm[v];
+  }
   const long pos = w * m;
   if (rope_dim > 0) {
     if (pos < n_pos) {

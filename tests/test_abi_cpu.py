@@ -45,6 +45,18 @@ def test_library_exports_every_declared_symbol(L):
     assert b"gfx950" in L.csa_version()
 
 
+def test_debug_build_loads_and_exports_the_same_entry_points():
+    from sparse_long_context_pool_amd import csa
+    D = csa.load(csa.DEBUG_LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(D, name), name
+    assert b"debug" in D.csa_version()
+    assert b"debug" not in csa.lib().csa_version()
+    # host-side checks are the same in both builds
+    nul = None
+    assert D.csa_compress(nul, nul, nul, nul, 1, 8, 12, 4, 1, 0, nul, 0, 0, 1, nul) == 1
+
+
 def test_invalid_arguments_are_rejected_on_the_host(L):
     nul = None
     # YaRN table: factor below 1, beta_fast not above beta_slow
