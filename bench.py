@@ -105,11 +105,13 @@ def work_counts(wl):
 class Runner:
     def __init__(self, wl, csa, torch):
         self.wl, self.csa, self.torch = wl, csa, torch
-        self.stages = []          # (name, launch fn)
+        self.stages = []          # (name, launch fn, launch fn in the step graph)
         self.extra = []           # (name, launch fn) timed beside the step
 
-    def add(self, name, fn):
-        self.stages.append((name, fn))
+    def add(self, name, fn, step_fn=None):
+        """A stage: `fn` launches it on its own (the per-stage times), `step_fn`
+        (default `fn`) as the whole-step graph runs it."""
+        self.stages.append((name, fn, step_fn or fn))
 
     def beside(self, name, fn):
         """A launch timed on its own, after the step (not part of it)."""
@@ -145,10 +147,10 @@ class Runner:
         outside the events."""
         torch = self.torch
         for _ in range(warmup):
-            for _, fn in self.stages:
+            for _, fn, _ in self.stages:
                 fn()
         torch.cuda.synchronize()
-        whole = self._capture([fn for _, fn in self.stages])
+        whole = self._capture([sfn for _, _, sfn in self.stages])
         for _ in range(warmup):
             whole.replay()
         torch.cuda.synchronize()
@@ -174,13 +176,13 @@ class Runner:
             torch.cuda.synchronize()
             total_ms = sum(a.elapsed_time(b) for a, b in pairs)
         del whole
-        ev = {n: [] for n, _ in self.stages}
+        ev = {n: [] for n, _, _ in self.stages}
         if flush is None:
             torch.cuda._sleep(1 << 22)   # a few ms of spinning: the host runs ahead
         for _ in range(steps):
             if flush is not None:
                 flush()
-            for name, fn in self.stages:
+            for name, fn, _ in self.stages:
                 a = torch.cuda.Event(enable_timing=True)
                 b = torch.cuda.Event(enable_timing=True)
                 a.record()
@@ -251,11 +253,31 @@ def setup(wl, csa, torch, synth):
         xi_new = gen("xi_new", B, (1, wl.idx_dim)).view(B, 1, wl.idx_dim)
         gi_new = gen("gi_new", B, (1, wl.idx_dim)).view(B, 1, wl.idx_dim)
         count = torch.full((B,), wl.q_pos0, dtype=torch.int32, device=dev)
-        r.add("cache_append", lambda: (
+
+        def append_kv():
             csa.csa_cache_append(x_new, g_new, None, count, ring_x, ring_g, pool, kv_win,
-                                 m=wl.m, overlap=wl.overlap, rope_dim=wl.rope_dim, cs=cs),
+                                 m=wl.m, overlap=wl.overlap, rope_dim=wl.rope_dim, cs=cs)
+
+        def append_keys():
             csa.csa_cache_append(xi_new, gi_new, None, count, ring_xi, ring_gi, k_idx, None,
-                                 m=wl.m, overlap=wl.overlap)))
+                                 m=wl.m, overlap=wl.overlap)
+
+        # In the step graph the two cache updates, which touch different caches,
+        # do not wait for each other: the index-key update runs on the step's
+        # stream (the index scores read it next), the K=V update on a second
+        # stream beside the index scores and top-k, and the attention waits for
+        # it.  The per-stage times launch both updates back to back.
+        side = torch.cuda.Stream()
+        fork, kv_done = torch.cuda.Event(), torch.cuda.Event()
+
+        def append_step():
+            fork.record(torch.cuda.current_stream())
+            side.wait_event(fork)
+            with torch.cuda.stream(side):
+                append_kv()
+                kv_done.record(side)
+            append_keys()
+        r.add("cache_append", lambda: (append_kv(), append_keys()), append_step)
     else:
         # the sequence's compression in one call: window rows (m = 1, rotated
         # in place of the K=V rows), the K=V pool, the index keys
@@ -297,10 +319,16 @@ def setup(wl, csa, torch, synth):
         need = csa.lib().csa_sparse_attn_workspace_size(B, S, wl.H, wl.D, wl.dv, wl.rope_dim,
                                                         wl.topk, wl.window, 1)
         ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
-        r.add("attention", lambda: csa.csa_sparse_attn(q, kvw, win_pos0, pool, idx, sink, q_pos,
-                                                       rope_dim=wl.rope_dim, cs=cs,
-                                                       window=wl.window, scale=wl.scale,
-                                                       dv=wl.dv, out=out, workspace=ws))
+        def attention():
+            csa.csa_sparse_attn(q, kvw, win_pos0, pool, idx, sink, q_pos, rope_dim=wl.rope_dim,
+                                cs=cs, window=wl.window, scale=wl.scale, dv=wl.dv, out=out,
+                                workspace=ws)
+
+        def attention_step():
+            if wl.decode:
+                torch.cuda.current_stream().wait_event(kv_done)
+            attention()
+        r.add("attention", attention, attention_step)
     else:
         need = csa.lib().hca_attn_workspace_size(B, S, wl.H, wl.D, wl.dv, wl.rope_dim, wl.T,
                                                  wl.window, 1)

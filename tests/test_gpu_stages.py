@@ -215,7 +215,9 @@ def test_index_scores(ops, case):
 
 # ------------------------------------------------------------------ top-k
 @pytest.mark.parametrize("T,k,m,qp,S", [
+    # T <= 2048: one wave per row (8, 16 or 32 keys per lane)
     (64, 16, 4, [0, 120], 37), (2048, 512, 4, [0, 6000], 70), (2048, 512, 1, [1000, 1500], 20),
+    (1000, 128, 1, [900, 10], 33), (1536, 700, 4, [5000, 2100], 11),
     (32768, 2048, 4, [131071, 90000], 3), (40000, 2048, 1, [39990, 20000], 4),
     (300, 300, 1, [0, 100], 9), (12000, 1024, 1, [11000, 6000], 130),
     # 2048 < T <= 8192: the 512-thread register kernel with 16 keys per thread
