@@ -11,7 +11,7 @@ inputs already resident in HBM (the RoPE table is model set-up: built once,
 timed on its own and reported beside the step).  Each stage is timed with HIP events on the
 stream its kernels run on; ``roofline`` reports the dominant kernel's
 algorithmic FLOP/s or bytes/s against the MI355X peak.  CSA decode (64 x 1
-token at position 131071, closing a pool entry) is reported in us/step, and the HCA and DSA
+token after 131072 cached tokens) is reported in us/step, and the HCA and DSA
 workloads in tokens/s.  ``cpu_baseline`` times the CPU oracle on a stratified
 sample of the prefill rows.
 
@@ -76,10 +76,15 @@ def work_counts(wl):
         # closes an entry also reads the other (1+overlap)m - 1 rows of x and
         # gate from the buffers and writes the pooled entry
         L = (1 + wl.overlap) * wl.m
-        closes = (wl.q_pos0 + 1) % wl.m == 0
-        rows_kv = 5 + (2 * (L - 1) + 1 if closes else 0)
-        rows_idx = 4 + (2 * (L - 1) + 1 if closes else 0)
-        w["cache_append"] = ("hbm", B * wl.S * (wl.D * rows_kv + wl.idx_dim * rows_idx) * e)
+
+        def append_bytes(closes):
+            rows_kv = 5 + (2 * (L - 1) + 1 if closes else 0)
+            rows_idx = 4 + (2 * (L - 1) + 1 if closes else 0)
+            return B * wl.S * (wl.D * rows_kv + wl.idx_dim * rows_idx) * e
+        w["cache_append"] = ("hbm", append_bytes((wl.q_pos0 + 1) % wl.m == 0))
+        # beside the step: the update of the token one position earlier, which
+        # closes a pool entry when q_pos0 is one past a window's end
+        w["cache_append_closing"] = ("hbm", append_bytes(wl.q_pos0 % wl.m == 0))
     if wl.n_idx_heads:
         pairs = int(R.sum()) * B
         if wl.decode:   # streams the index-key pool once: HBM-bound
@@ -105,17 +110,17 @@ def work_counts(wl):
 class Runner:
     def __init__(self, wl, csa, torch):
         self.wl, self.csa, self.torch = wl, csa, torch
-        self.stages = []          # (name, launch fn, launch fn in the step graph)
-        self.extra = []           # (name, launch fn) timed beside the step
+        self.stages = []          # (name, launch fn)
+        self.extra = []           # (name, launch fn, flushed) timed beside the step
 
-    def add(self, name, fn, step_fn=None):
-        """A stage: `fn` launches it on its own (the per-stage times), `step_fn`
-        (default `fn`) as the whole-step graph runs it."""
-        self.stages.append((name, fn, step_fn or fn))
+    def add(self, name, fn):
+        self.stages.append((name, fn))
 
-    def beside(self, name, fn):
-        """A launch timed on its own, after the step (not part of it)."""
-        self.extra.append((name, fn))
+    def beside(self, name, fn, flushed=False):
+        """A launch timed on its own, after the step (not part of it): back to
+        back, or (flushed) one launch after each cache flush, as the step's
+        stages are."""
+        self.extra.append((name, fn, flushed))
 
     def _capture(self, fns):
         """A HIP graph of the launches of `fns` (launched once on the capture
@@ -147,10 +152,10 @@ class Runner:
         outside the events."""
         torch = self.torch
         for _ in range(warmup):
-            for _, fn, _ in self.stages:
+            for _, fn in self.stages:
                 fn()
         torch.cuda.synchronize()
-        whole = self._capture([sfn for _, _, sfn in self.stages])
+        whole = self._capture([fn for _, fn in self.stages])
         for _ in range(warmup):
             whole.replay()
         torch.cuda.synchronize()
@@ -176,13 +181,13 @@ class Runner:
             torch.cuda.synchronize()
             total_ms = sum(a.elapsed_time(b) for a, b in pairs)
         del whole
-        ev = {n: [] for n, _, _ in self.stages}
+        ev = {n: [] for n, _ in self.stages}
         if flush is None:
             torch.cuda._sleep(1 << 22)   # a few ms of spinning: the host runs ahead
         for _ in range(steps):
             if flush is not None:
                 flush()
-            for name, fn, _ in self.stages:
+            for name, fn in self.stages:
                 a = torch.cuda.Event(enable_timing=True)
                 b = torch.cuda.Event(enable_timing=True)
                 a.record()
@@ -192,10 +197,23 @@ class Runner:
         torch.cuda.synchronize()
         avg = {n: float(np.mean([a.elapsed_time(b) for a, b in v])) for n, v in ev.items()}
         beside = {}
-        for name, fn in self.extra:
+        for name, fn, flushed in self.extra:
             for _ in range(warmup):
                 fn()
             torch.cuda.synchronize()
+            if flushed and flush is not None:
+                pairs = []
+                for _ in range(steps):
+                    flush()
+                    a = torch.cuda.Event(enable_timing=True)
+                    b = torch.cuda.Event(enable_timing=True)
+                    a.record()
+                    fn()
+                    b.record()
+                    pairs.append((a, b))
+                torch.cuda.synchronize()
+                beside[name] = float(np.mean([a.elapsed_time(b) for a, b in pairs]))
+                continue
             torch.cuda._sleep(1 << 22)
             a = torch.cuda.Event(enable_timing=True)
             b = torch.cuda.Event(enable_timing=True)
@@ -254,30 +272,18 @@ def setup(wl, csa, torch, synth):
         gi_new = gen("gi_new", B, (1, wl.idx_dim)).view(B, 1, wl.idx_dim)
         count = torch.full((B,), wl.q_pos0, dtype=torch.int32, device=dev)
 
-        def append_kv():
-            csa.csa_cache_append(x_new, g_new, None, count, ring_x, ring_g, pool, kv_win,
+        def append(cnt):
+            csa.csa_cache_append(x_new, g_new, None, cnt, ring_x, ring_g, pool, kv_win,
                                  m=wl.m, overlap=wl.overlap, rope_dim=wl.rope_dim, cs=cs)
-
-        def append_keys():
-            csa.csa_cache_append(xi_new, gi_new, None, count, ring_xi, ring_gi, k_idx, None,
+            csa.csa_cache_append(xi_new, gi_new, None, cnt, ring_xi, ring_gi, k_idx, None,
                                  m=wl.m, overlap=wl.overlap)
 
-        # In the step graph the two cache updates, which touch different caches,
-        # do not wait for each other: the index-key update runs on the step's
-        # stream (the index scores read it next), the K=V update on a second
-        # stream beside the index scores and top-k, and the attention waits for
-        # it.  The per-stage times launch both updates back to back.
-        side = torch.cuda.Stream()
-        fork, kv_done = torch.cuda.Event(), torch.cuda.Event()
-
-        def append_step():
-            fork.record(torch.cuda.current_stream())
-            side.wait_event(fork)
-            with torch.cuda.stream(side):
-                append_kv()
-                kv_done.record(side)
-            append_keys()
-        r.add("cache_append", lambda: (append_kv(), append_keys()), append_step)
+        r.add("cache_append", lambda: append(count))
+        # the update of the previous token (position q_pos0 - 1), which closes
+        # pool entry q_pos0 / m - 1 when q_pos0 is a multiple of m: timed beside
+        # the step, after a cache flush like the step's stages
+        count_prev = torch.full((B,), wl.q_pos0 - 1, dtype=torch.int32, device=dev)
+        r.beside("cache_append_closing", lambda: append(count_prev), flushed=True)
     else:
         # the sequence's compression in one call: window rows (m = 1, rotated
         # in place of the K=V rows), the K=V pool, the index keys
@@ -324,11 +330,7 @@ def setup(wl, csa, torch, synth):
                                 cs=cs, window=wl.window, scale=wl.scale, dv=wl.dv, out=out,
                                 workspace=ws)
 
-        def attention_step():
-            if wl.decode:
-                torch.cuda.current_stream().wait_event(kv_done)
-            attention()
-        r.add("attention", attention, attention_step)
+        r.add("attention", attention)
     else:
         need = csa.lib().hca_attn_workspace_size(B, S, wl.H, wl.D, wl.dv, wl.rope_dim, wl.T,
                                                  wl.window, 1)

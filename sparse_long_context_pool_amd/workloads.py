@@ -80,14 +80,12 @@ WORKLOADS = {
                          rope_dim=64, m=128, overlap=0, ctx=65536, n_idx_heads=0,
                          idx_dim=0, topk=0, window=128, theta=160000.0, act_scale=1.0,
                          sink=True),
-    # CSA decode, bf16, 64 sequences x 1 new token after 131071 cached tokens:
-    # the 131072nd token (position 131071), whose arrival closes pool entry
-    # 32767, so the step's cache update writes an entry as well as the window
-    # and buffer rows; 32768 entries at m=4, top-2048, window 128; caches N(0,1).
+    # CSA decode, bf16, 64 sequences x 1 new token after 131072 cached tokens
+    # (32768 entries at m=4); top-2048, window 128; caches N(0,1).
     "csa_decode_bf16": Workload("csa_decode_bf16", "csa", "bf16", B=64, S=1, H=64, D=512,
                                 dv=512, rope_dim=64, m=4, overlap=1, ctx=131072,
                                 n_idx_heads=64, idx_dim=128, topk=2048, window=128,
-                                theta=160000.0, act_scale=1.0, sink=True, q_pos0=131071,
+                                theta=160000.0, act_scale=1.0, sink=True, q_pos0=131072,
                                 decode=True),
     # DSA token-level indexer (m=1), bf16, S=32768, indexer 64 x 128, top-2048
     # tokens; sparse MQA with 128 heads, head_dim 576 (rope 64), latent 512 as
