@@ -57,15 +57,22 @@ def _pipeline(ops, S, ctx, q_pos0):
         ops.csa_sparse_attn(q, kv_win, win_pos0, pool, idx, sink, q_pos, rope_dim=R, cs=cs,
                             window=win, scale=D ** -0.5, out=out, workspace=ws)
 
-    return step, (kv_win, pool, k_idx, scores, idx, out)
+    def separate():
+        return (ops.csa_compress(x, m=1, overlap=0, rope_dim=R, cs=cs, pos0=0),
+                ops.csa_compress(x, gate, m=m, overlap=1, rope_dim=R, cs=cs, pos0=0),
+                ops.csa_compress(xi, gi, m=m, overlap=1))
+
+    return step, (kv_win, pool, k_idx, scores, idx, out), separate
 
 
 @pytest.mark.parametrize("S,ctx,q_pos0", [(1024, 4096, 3072), (4, 8192, 8188)])
 def test_step_graph_replays(ops, S, ctx, q_pos0):
-    step, outs = _pipeline(ops, S, ctx, q_pos0)
+    step, outs, separate = _pipeline(ops, S, ctx, q_pos0)
     step()
     torch.cuda.synchronize()
     ref = [t.clone() for t in outs]
+    for name, a, b in zip(("kv_win", "pool", "k_idx"), separate(), ref[:3]):
+        assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), name
     cap = torch.cuda.Stream()
     cap.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(cap):
