@@ -273,10 +273,12 @@ def setup(wl, csa, torch, synth):
         count = torch.full((B,), wl.q_pos0, dtype=torch.int32, device=dev)
 
         def append(cnt):
-            csa.csa_cache_append(x_new, g_new, None, cnt, ring_x, ring_g, pool, kv_win,
-                                 m=wl.m, overlap=wl.overlap, rope_dim=wl.rope_dim, cs=cs)
-            csa.csa_cache_append(xi_new, gi_new, None, cnt, ring_xi, ring_gi, k_idx, None,
-                                 m=wl.m, overlap=wl.overlap)
+            # both caches (K=V with its window, index keys) in one launch
+            csa.csa_cache_append_many([
+                dict(x=x_new, gate=g_new, count=cnt, ring_x=ring_x, ring_g=ring_g, pool=pool,
+                     win=kv_win, m=wl.m, overlap=wl.overlap, rope_dim=wl.rope_dim, cs=cs),
+                dict(x=xi_new, gate=gi_new, count=cnt, ring_x=ring_xi, ring_g=ring_gi,
+                     pool=k_idx, m=wl.m, overlap=wl.overlap)])
 
         r.add("cache_append", lambda: append(count))
         # the update of the previous token (position q_pos0 - 1), which closes

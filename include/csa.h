@@ -184,6 +184,29 @@ csa_status_t csa_cache_append(const void *x, const void *gate, const float *slot
                               int32_t dtype, void *stream);
 
 /*
+ * csa_cache_append_many -- several csa_cache_append updates in as few launches
+ * as possible (a decode step's K=V cache and index-key cache: one launch).
+ * Each pass has exactly csa_cache_append's arguments, meaning and requirements
+ * and leaves its cache exactly as csa_cache_append leaves it; the passes must
+ * update different caches (no buffer written by one pass is read or written
+ * by another).  Passes of one token per sequence (n = 1) share launches, up to
+ * four caches per launch; others run as csa_cache_append runs them.  Every
+ * pass is checked before anything is enqueued.  n_passes <= 16.
+ */
+typedef struct {
+    const void *x, *gate;
+    const float *slot_bias;
+    void *ring_x, *ring_g, *pool, *win;
+    const int32_t *count;
+    int32_t B, n, D, m, overlap, T_cap, W, rope_dim;
+    const float *cs;
+    int32_t n_pos;
+} csa_cache_pass_t;
+
+csa_status_t csa_cache_append_many(const csa_cache_pass_t *passes, int32_t n_passes,
+                                   int32_t dtype, void *stream);
+
+/*
  * csa_index_scores -- Lightning-Indexer index scores.  Page "DeepSeek-V4",
  * "Hybrid attention" (indexer scoring queries against the pool, eqs. 13-17)
  * and DeepseekV4Config (index_n_heads = n_h^I of eq. 14, index_head_dim);

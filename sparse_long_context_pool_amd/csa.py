@@ -28,6 +28,17 @@ class CompressPass(ctypes.Structure):
                 ("cs", ctypes.c_void_p), ("n_pos", ctypes.c_int32), ("pos0", ctypes.c_int32)]
 
 
+class CachePass(ctypes.Structure):
+    """csa_cache_pass_t: one csa_cache_append call's arguments."""
+    _fields_ = [("x", ctypes.c_void_p), ("gate", ctypes.c_void_p),
+                ("slot_bias", ctypes.c_void_p), ("ring_x", ctypes.c_void_p),
+                ("ring_g", ctypes.c_void_p), ("pool", ctypes.c_void_p), ("win", ctypes.c_void_p),
+                ("count", ctypes.c_void_p), ("B", ctypes.c_int32), ("n", ctypes.c_int32),
+                ("D", ctypes.c_int32), ("m", ctypes.c_int32), ("overlap", ctypes.c_int32),
+                ("T_cap", ctypes.c_int32), ("W", ctypes.c_int32), ("rope_dim", ctypes.c_int32),
+                ("cs", ctypes.c_void_p), ("n_pos", ctypes.c_int32)]
+
+
 def lib():
     """The loaded libcsa.so (raises if it has not been built)."""
     global _lib
@@ -62,6 +73,7 @@ def load(path: str):
         "csa_compress": ([vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp, i32, i32,
                           i32, vp], ctypes.c_int),
         "csa_compress_many": ([ctypes.POINTER(CompressPass), i32, i32, vp], ctypes.c_int),
+        "csa_cache_append_many": ([ctypes.POINTER(CachePass), i32, i32, vp], ctypes.c_int),
         "csa_cache_append": ([vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
                               i32, i32, i32, vp, i32, i32, vp], ctypes.c_int),
         "csa_index_scores": ([vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
@@ -92,7 +104,7 @@ def load(path: str):
 
 EXPORTS = ("csa_last_error", "csa_version", "csa_rope_table", "csa_rope_table_yarn",
            "csa_compress", "csa_compress_many",
-           "csa_cache_append",
+           "csa_cache_append", "csa_cache_append_many",
            "csa_index_scores", "csa_topk", "csa_index_topk", "csa_index_topk_workspace_size",
            "csa_sparse_attn", "csa_sparse_attn_noalloc",
            "csa_sparse_attn_workspace_size", "hca_attn", "hca_attn_workspace_size",
@@ -222,6 +234,36 @@ def csa_cache_append(x, gate, slot_bias, count, ring_x, ring_g, pool, win=None, 
                                   overlap, T_cap, W, rope_dim, _ptr(cs), n_pos, _dtype(x),
                                   _stream()),
            "csa_cache_append")
+
+
+def csa_cache_append_many(passes) -> None:
+    """Several csa_cache_append updates in one call.  ``passes`` is a sequence
+    of dicts with csa_cache_append's arguments (keys x, gate, slot_bias, count,
+    ring_x, ring_g, pool, win, m, overlap, rope_dim, cs); all x share one dtype
+    and every pass updates its own cache."""
+    passes = list(passes)
+    arr = (CachePass * max(len(passes), 1))()
+    dtype = _dtype(passes[0]["x"]) if passes else CSA_BF16
+    for q, p in enumerate(passes):
+        x, gate, count = p["x"], p.get("gate"), p["count"]
+        B, n, D = x.shape
+        if _dtype(x) != dtype:
+            raise TypeError("csa_cache_append_many: all passes must share one dtype")
+        if gate is not None:
+            assert gate.shape == x.shape and gate.dtype == x.dtype
+        assert count.dtype == torch.int32 and count.numel() == B
+        pool, win, cs = p["pool"], p.get("win"), p.get("cs")
+        c = arr[q]
+        c.x, c.gate, c.slot_bias, c.ring_x, c.ring_g, c.pool, c.win, c.count, c.cs = (
+            None if t is None else _ptr(t).value
+            for t in (x, gate, p.get("slot_bias"), p["ring_x"], p.get("ring_g"), pool, win,
+                      count, cs))
+        c.B, c.n, c.D, c.m, c.overlap = B, n, D, p["m"], p.get("overlap", 0)
+        c.T_cap, c.W = pool.shape[1], 0 if win is None else win.shape[1]
+        c.rope_dim = p.get("rope_dim", 0)
+        c.n_pos = 0 if cs is None else cs.shape[0]
+    _check(lib().csa_cache_append_many(arr, len(passes), dtype, _stream()),
+           "csa_cache_append_many")
 
 
 def csa_index_scores(q_idx, w_idx, k_pool, q_pos, *, m: int, out=None) -> torch.Tensor:

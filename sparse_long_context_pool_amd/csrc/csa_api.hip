@@ -33,6 +33,14 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 bool dtype_ok(int32_t dt) { return dt == CSA_F32 || dt == CSA_BF16; }
 
+// the argument checks of one cache update (CSA_OK: valid; nothing to do when
+// B * n == 0)
+csa_status_t check_cache_append(const char* fn, const void* x, const void* gate,
+                                const float* slot_bias, void* ring_x, void* ring_g, void* pool,
+                                void* win, const int32_t* count, int32_t B, int32_t n,
+                                int32_t D, int32_t m, int32_t overlap, int32_t T_cap, int32_t W,
+                                int32_t rope_dim, const float* cs, int32_t n_pos);
+
 // the argument checks of one compressor pass (CSA_OK: valid; nothing to do
 // when B * (S / m) == 0)
 csa_status_t check_compress(const char* fn, const void* x, const void* gate,
@@ -330,6 +338,48 @@ csa_status_t csa_cache_append(const void* x, const void* gate, const float* slot
                               const float* cs, int32_t n_pos, int32_t dtype, void* stream) {
   const char* fn = "csa_cache_append";
   if (!dtype_ok(dtype)) return fail(CSA_ERR_INVALID, "%s: unknown dtype %d", fn, dtype);
+  csa_status_t st = check_cache_append(fn, x, gate, slot_bias, ring_x, ring_g, pool, win, count,
+                                       B, n, D, m, overlap, T_cap, W, rope_dim, cs, n_pos);
+  if (st != CSA_OK || (long)B * n == 0) return st;
+  return launched(csa::launch_cache_append(x, gate, slot_bias, ring_x, ring_g, pool, win,
+                                           count, B, n, D, m, overlap, T_cap, W, rope_dim, cs,
+                                           n_pos, dtype == CSA_BF16, as_stream(stream)),
+                  fn);
+}
+
+csa_status_t csa_cache_append_many(const csa_cache_pass_t* passes, int32_t n_passes,
+                                   int32_t dtype, void* stream) {
+  const char* fn = "csa_cache_append_many";
+  if (!dtype_ok(dtype)) return fail(CSA_ERR_INVALID, "%s: unknown dtype %d", fn, dtype);
+  if (n_passes < 0 || n_passes > 16 || (n_passes > 0 && !passes))
+    return fail(CSA_ERR_INVALID, "%s: need 0 <= n_passes <= 16 and a pass array", fn);
+  csa::CachePass cp[16];
+  int n = 0;
+  for (int q = 0; q < n_passes; ++q) {
+    const csa_cache_pass_t& c = passes[q];
+    char name[48];
+    snprintf(name, sizeof(name), "%s: pass %d", fn, q);
+    csa_status_t st = check_cache_append(name, c.x, c.gate, c.slot_bias, c.ring_x, c.ring_g,
+                                         c.pool, c.win, c.count, c.B, c.n, c.D, c.m, c.overlap,
+                                         c.T_cap, c.W, c.rope_dim, c.cs, c.n_pos);
+    if (st != CSA_OK) return st;
+    if ((long)c.B * c.n == 0) continue;
+    cp[n++] = csa::CachePass{c.x, c.gate, c.slot_bias, c.ring_x, c.ring_g, c.pool, c.win,
+                             c.count, c.B, c.n, c.D, c.m, c.overlap, c.T_cap, c.W, c.rope_dim,
+                             c.cs, c.n_pos};
+  }
+  return launched(csa::launch_cache_append_many(cp, n, dtype == CSA_BF16, as_stream(stream)),
+                  fn);
+}
+
+}  // extern "C"
+
+namespace {
+csa_status_t check_cache_append(const char* fn, const void* x, const void* gate,
+                                const float* slot_bias, void* ring_x, void* ring_g, void* pool,
+                                void* win, const int32_t* count, int32_t B, int32_t n,
+                                int32_t D, int32_t m, int32_t overlap, int32_t T_cap, int32_t W,
+                                int32_t rope_dim, const float* cs, int32_t n_pos) {
   if (B < 0 || n < 0 || D < 8 || m < 1 || (overlap != 0 && overlap != 1) || T_cap < 0 ||
       W < 0)
     return fail(CSA_ERR_INVALID, "%s: bad sizes (B=%d n=%d D=%d m=%d overlap=%d T_cap=%d W=%d)",
@@ -355,11 +405,11 @@ csa_status_t csa_cache_append(const void* x, const void* gate, const float* slot
     return fail(CSA_ERR_INVALID, "%s: tensors must be 16-byte aligned", fn);
   if (rope_dim > 0 && (!cs || n_pos < 1))
     return fail(CSA_ERR_INVALID, "%s: the RoPE table is required", fn);
-  return launched(csa::launch_cache_append(x, gate, slot_bias, ring_x, ring_g, pool, win,
-                                           count, B, n, D, m, overlap, T_cap, W, rope_dim, cs,
-                                           n_pos, dtype == CSA_BF16, as_stream(stream)),
-                  fn);
+  return CSA_OK;
 }
+}  // namespace
+
+extern "C" {
 
 csa_status_t csa_index_scores(const void* q_idx, const float* w_idx, const void* k_pool,
                               float* scores, const int32_t* q_pos, int32_t B, int32_t S,

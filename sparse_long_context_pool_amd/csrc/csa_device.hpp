@@ -164,6 +164,23 @@ hipError_t launch_cache_append(const void* x, const void* gate, const float* slo
                                int T_cap, int W, int rope_dim, const float* cs, int n_pos,
                                bool bf16, hipStream_t s);
 
+// one csa_cache_append pass; launch_cache_append_many runs the single-token
+// passes of a list in shared launches and the others on their own
+struct CachePass {
+  const void* x;
+  const void* gate;
+  const float* slot_bias;
+  void* ring_x;
+  void* ring_g;
+  void* pool;
+  void* win;
+  const int* count;
+  int B, n, D, m, overlap, T_cap, W, rope_dim;
+  const float* cs;
+  int n_pos;
+};
+hipError_t launch_cache_append_many(const CachePass* p, int n, bool bf16, hipStream_t s);
+
 hipError_t launch_index_scores(const void* q_idx, const float* w_idx, const void* k_pool,
                                float* scores, const int* q_pos, int B, int S, int T,
                                int n_heads, int head_dim, int m, bool bf16,

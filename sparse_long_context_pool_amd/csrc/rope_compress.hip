@@ -643,14 +643,12 @@ __global__ __launch_bounds__(256) void cache_tokens_kernel(
 // a chunk pools its entry (if the token closes one) before it overwrites the
 // ring row of the token L positions back, which that entry does not read.
 template <bool BF16>
-__global__ __launch_bounds__(256) void cache_one_kernel(
+__device__ __forceinline__ void cache_one_body(
     const void* __restrict__ x, const void* __restrict__ gate,
     const float* __restrict__ slot_bias, void* __restrict__ ring_x, void* __restrict__ ring_g,
     void* __restrict__ pool, void* __restrict__ win, const int* __restrict__ count, int D,
     int m, int overlap, int T_cap, int W, int rope_dim, const float2* __restrict__ cs,
-    int n_pos) {
-  const int ch = blockIdx.x * blockDim.x + threadIdx.x;
-  const int b = blockIdx.y;
+    int n_pos, int b, int ch) {
   if (ch >= (D >> 3)) return;
   const long c0 = count[b];
   if (c0 < 0) return;
@@ -659,6 +657,54 @@ __global__ __launch_bounds__(256) void cache_one_kernel(
                       D, m, overlap, T_cap, rope_dim, cs, n_pos);
   cache_token<BF16>(x, gate, ring_x, ring_g, win, b, c0, 0, ch, 1, D, (1 + overlap) * m, W,
                     rope_dim, cs, n_pos);
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(256) void cache_one_kernel(
+    const void* __restrict__ x, const void* __restrict__ gate,
+    const float* __restrict__ slot_bias, void* __restrict__ ring_x, void* __restrict__ ring_g,
+    void* __restrict__ pool, void* __restrict__ win, const int* __restrict__ count, int D,
+    int m, int overlap, int T_cap, int W, int rope_dim, const float2* __restrict__ cs,
+    int n_pos) {
+  cache_one_body<BF16>(x, gate, slot_bias, ring_x, ring_g, pool, win, count, D, m, overlap,
+                       T_cap, W, rope_dim, cs, n_pos, blockIdx.y,
+                       blockIdx.x * blockDim.x + threadIdx.x);
+}
+
+// One token per sequence for several caches in one launch (a decode step's
+// K=V cache and index-key cache): each cache owns a contiguous range of the
+// grid's workgroups, one workgroup of 128 threads per sequence (a thread per
+// 8-channel chunk, D <= 1024), and runs the single-cache kernel's body, so the
+// caches come out exactly as separate updates leave them.
+constexpr int kMaxCacheJobs = 4;
+struct CacheJob {
+  const void* x;
+  const void* gate;
+  const float* slot_bias;
+  void* ring_x;
+  void* ring_g;
+  void* pool;
+  void* win;
+  const int* count;
+  const float2* cs;
+  int D, m, overlap, T_cap, W, rope_dim, n_pos;
+  int block0;  // first workgroup of the cache
+};
+struct CacheBatch {
+  CacheJob job[kMaxCacheJobs];
+  int n;
+};
+
+template <bool BF16>
+__global__ __launch_bounds__(128) void cache_one_batch_kernel(CacheBatch bt) {
+  int j = 0;
+#pragma unroll
+  for (int q = 1; q < kMaxCacheJobs; ++q)
+    if (q < bt.n && (int)blockIdx.x >= bt.job[q].block0) j = q;
+  const CacheJob& c = bt.job[j];
+  cache_one_body<BF16>(c.x, c.gate, c.slot_bias, c.ring_x, c.ring_g, c.pool, c.win, c.count,
+                       c.D, c.m, c.overlap, c.T_cap, c.W, c.rope_dim, c.cs, c.n_pos,
+                       (int)blockIdx.x - c.block0, threadIdx.x);
 }
 
 }  // namespace
@@ -852,6 +898,53 @@ hipError_t launch_cache_append(const void* x, const void* gate, const float* slo
     hipLaunchKernelGGL(cache_tokens_kernel<false>, g2, dim3(256), 0, s, x, gate, ring_x, ring_g,
                        win, count, n, D, L, W, rope_dim, cs2, n_pos);
   return hipGetLastError();
+}
+
+hipError_t launch_cache_append_many(const CachePass* p, int n, bool bf16, hipStream_t s) {
+  // single-token updates share launches of up to kMaxCacheJobs caches; the
+  // others run as launch_cache_append runs them
+  CacheBatch bt;
+  bt.n = 0;
+  long blocks = 0;
+  auto flush = [&]() -> hipError_t {
+    if (bt.n == 0) return hipSuccess;
+    if (bf16)
+      hipLaunchKernelGGL(cache_one_batch_kernel<true>, dim3((unsigned)blocks), dim3(128), 0, s,
+                         bt);
+    else
+      hipLaunchKernelGGL(cache_one_batch_kernel<false>, dim3((unsigned)blocks), dim3(128), 0, s,
+                         bt);
+    bt.n = 0;
+    blocks = 0;
+    return hipGetLastError();
+  };
+  for (int q = 0; q < n; ++q) {
+    const CachePass& c = p[q];
+    if (c.B == 0 || c.n == 0) continue;
+    if (c.n != 1 || c.D > 1024) {
+      hipError_t e = launch_cache_append(c.x, c.gate, c.slot_bias, c.ring_x, c.ring_g, c.pool,
+                                         c.win, c.count, c.B, c.n, c.D, c.m, c.overlap, c.T_cap,
+                                         c.W, c.rope_dim, c.cs, c.n_pos, bf16, s);
+      if (e != hipSuccess) return e;
+      continue;
+    }
+    if (blocks + c.B >= (1L << 31)) {
+      hipError_t e = flush();
+      if (e != hipSuccess) return e;
+    }
+    CacheJob& jb = bt.job[bt.n++];
+    jb.x = c.x; jb.gate = c.gate; jb.slot_bias = c.slot_bias; jb.ring_x = c.ring_x;
+    jb.ring_g = c.ring_g; jb.pool = c.pool; jb.win = c.win; jb.count = c.count;
+    jb.cs = reinterpret_cast<const float2*>(c.cs);
+    jb.D = c.D; jb.m = c.m; jb.overlap = c.overlap; jb.T_cap = c.T_cap; jb.W = c.W;
+    jb.rope_dim = c.rope_dim; jb.n_pos = c.n_pos; jb.block0 = (int)blocks;
+    blocks += c.B;
+    if (bt.n == kMaxCacheJobs) {
+      hipError_t e = flush();
+      if (e != hipSuccess) return e;
+    }
+  }
+  return flush();
 }
 
 }  // namespace csa

@@ -124,6 +124,25 @@ def test_compress_many_checks_every_pass_before_enqueueing(L):
     assert L.csa_compress_many(arr, 1, 1, None) == 0
 
 
+def test_cache_append_many_checks_every_pass_before_enqueueing(L):
+    from sparse_long_context_pool_amd.csa import CachePass
+    arr = (CachePass * 17)()
+    for c in arr:
+        c.x = c.ring_x = c.pool = c.count = 0x10000
+        c.B, c.n, c.D, c.m, c.overlap, c.T_cap = 2, 1, 64, 4, 1, 8
+    arr[1].win = 0x10000                 # pass 1: a window buffer but W = 0
+    assert L.csa_cache_append_many(arr, 2, 1, None) == 1
+    assert b"pass 1" in L.csa_last_error()
+    arr[1].win = None
+    arr[1].D = 2048                      # beyond the supported width
+    assert L.csa_cache_append_many(arr, 2, 1, None) == 2
+    assert L.csa_cache_append_many(arr, 17, 1, None) == 1      # too many passes
+    assert L.csa_cache_append_many(arr, 1, 9, None) == 1       # unknown dtype
+    assert L.csa_cache_append_many(None, 0, 1, None) == 0      # nothing to do
+    arr[0].n = 0                                               # no token: no work
+    assert L.csa_cache_append_many(arr, 1, 1, None) == 0
+
+
 def test_cache_append_rejects_bad_arguments_on_the_host(L):
     nul = None
     fake = ctypes.c_void_p(0x10000)

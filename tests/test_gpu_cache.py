@@ -96,6 +96,60 @@ def test_cache_append(ops, name):
                                            err_msg=f"{name} window b={b}")
 
 
+def test_cache_append_many_matches_separate_calls(ops):
+    """csa_cache_append_many leaves every cache exactly as separate
+    csa_cache_append calls do: a decode step's K=V cache (window, RoPE) and
+    index-key cache, an HCA cache (m' = 128) and a 3-token update (its own
+    kernels) in one call; counts that close an entry, that do not, and a
+    negative count (no update)."""
+    dt = torch.bfloat16
+    B = 6
+    counts = [3, 7, 12, 130, 0, -1]       # 3, 7: close entries at m = 4; 127 + ... at m'
+    cs = ops.csa_rope_table(1024, 64, 160000.0)
+
+    def cache(seed, D, m, ov, W, T_cap, n, rope, gate=True, bias=False):
+        L = (1 + ov) * m
+        st = dict(x=dev(rnd((B, n, D), seed, True), dt),
+                  gate=dev(rnd((B, n, D), seed + 1, True), dt) if gate else None,
+                  ring_x=dev(rnd((B, L, D), seed + 2, True), dt),
+                  ring_g=dev(rnd((B, L, D), seed + 3, True), dt) if gate else None,
+                  pool=dev(rnd((B, T_cap, D), seed + 4, True), dt),
+                  win=dev(rnd((B, W, D), seed + 5, True), dt) if W else None,
+                  slot_bias=dev(rnd((L, D), seed + 6, False), torch.float32) if bias else None,
+                  m=m, overlap=ov, rope_dim=rope, cs=cs if rope else None)
+        return st
+
+    passes = [cache(10, 512, 4, 1, 128, 64, 1, 64),              # K=V cache with window
+              cache(20, 128, 4, 1, 0, 64, 1, 0),                 # index keys
+              cache(30, 512, 128, 0, 16, 4, 1, 64, bias=True),   # HCA m' = 128
+              cache(40, 64, 4, 1, 8, 64, 3, 16)]                 # 3 tokens: own kernels
+    count = torch.tensor(counts, dtype=torch.int32, device="cuda")
+    keys = ("ring_x", "ring_g", "pool", "win")
+
+    def clone(p):
+        q = dict(p)
+        for k in keys:
+            if q[k] is not None:
+                q[k] = q[k].clone()
+        q["count"] = count
+        return q
+
+    many = [clone(p) for p in passes]
+    one = [clone(p) for p in passes]
+    ops.csa_cache_append_many(many)
+    for p in one:
+        ops.csa_cache_append(p["x"], p["gate"], p["slot_bias"], p["count"], p["ring_x"],
+                             p["ring_g"], p["pool"], p["win"], m=p["m"], overlap=p["overlap"],
+                             rope_dim=p["rope_dim"], cs=p["cs"])
+    torch.cuda.synchronize()
+    for i, (a, b) in enumerate(zip(many, one)):
+        for k in keys:
+            if a[k] is not None:
+                assert torch.equal(a[k].view(torch.int16), b[k].view(torch.int16)), (i, k)
+    # the updates did something: the closing K=V entry of sequence 0 (count 3 -> entry 0)
+    assert not torch.equal(many[0]["pool"][0, 0], passes[0]["pool"][0, 0])
+
+
 def test_cache_append_matches_compress(ops):
     """Token by token, the cache's pool is the compressor's pool over the whole
     sequence, bit for bit (the two kernels pool a window the same way)."""
