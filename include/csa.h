@@ -12,9 +12,10 @@
  * Conventions shared by every entry point
  * ---------------------------------------
  *  - Every tensor pointer is a DEVICE pointer owned by the caller.  The
- *    library never allocates or frees device memory and keeps no state besides
- *    a thread-local error string.  Scratch space, where a call can use it,
- *    comes in through a caller-owned workspace argument.
+ *    library never allocates or frees device memory.  Its state is a
+ *    thread-local error string and, for csa_sparse_attn_noalloc only, a static
+ *    device array per GPU (see there).  Scratch space otherwise comes in
+ *    through a caller-owned workspace argument.
  *  - Tensors are dense, row-major, innermost dimension contiguous, and 16-byte
  *    aligned.  Element type: `dtype` (CSA_F32 = fp32, CSA_BF16 = bfloat16)
  *    unless an argument says fp32 or int32 explicitly.
@@ -30,7 +31,11 @@
  *    Kernels read cos/sin from a table built by csa_rope_table.
  *  - `stream` is a hipStream_t (NULL = the default stream).  Calls only
  *    enqueue work and return; they never synchronize.  Device faults surface at
- *    the caller's next synchronization.
+ *    the caller's next synchronization.  (The debug build of the library,
+ *    libcsa_debug.so, is the exception: before each attention launch it
+ *    checks the index rows on the device, synchronizes the stream and returns
+ *    CSA_ERR_INVALID for an entry outside [-1, T); it is not for graph
+ *    capture.)
  *  - Every call returns a csa_status_t.  On a non-OK status nothing was
  *    enqueued and csa_last_error() describes the problem.  Calls never abort
  *    or throw.
