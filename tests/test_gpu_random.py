@@ -150,3 +150,49 @@ def test_random_attention(ops, seed):
                                rope_dim=rope, theta=theta, scale=scale, dv=dv)
         err = float(np.abs(out[b] - ref).max())
         assert err <= tol, (dict(H=H, D=D, dv=dv, m=m, T=T, S=S, k=k, window=window), b, err)
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_random_hca_attention(ops, seed):
+    """Dense attention over every ready entry (HCA), including layers with no
+    pool (sliding window only), on the matrix-core and generic kernels."""
+    r = np.random.default_rng(4000 + seed)
+    mfma = seed % 2 == 0
+    if mfma:
+        H, D, rope, dv, bf16 = 64, 512, 64, 512, True
+    else:
+        H = int(r.choice([1, 2, 4, 8]))
+        D = int(r.choice([32, 64, 96]))
+        rope = int(r.choice([8, 16]))
+        dv = int(r.choice([D, D - rope]))
+        bf16 = bool(r.integers(0, 2))
+    m = int(r.choice([4, 8, 16, 128]))
+    T = 0 if seed % 5 == 4 else int(r.integers(1, 40))
+    B = int(r.integers(1, 3))
+    S = int(r.choice([1, 2, int(r.integers(3, 60))]))
+    window = int(r.choice([8, 32, 128])) if T == 0 else int(r.choice([0, 5, 32, 128]))
+    sink = bool(r.integers(0, 2))
+    qp = [int(r.integers(0, max(T, 1) * m + 30)) for _ in range(B)]
+    theta = 160000.0
+    q = _data(r, (B, S, H, D), bf16)
+    L = max(qp) + S if window else 0
+    kv = _data(r, (B, L, D), bf16) if window else None
+    pool = _data(r, (B, T, D), bf16)
+    z = _data(r, (H,), False) if sink else None
+    dt = torch.bfloat16 if bf16 else torch.float32
+    cs = ops.csa_rope_table(max(qp) + S + 1, rope, theta)
+    q_pos = torch.tensor(qp, dtype=torch.int32, device="cuda")
+    win_pos0 = torch.zeros(B, dtype=torch.int32, device="cuda")
+    scale = 1.0 / math.sqrt(D)
+    out = host(ops.hca_attn(dev(q, dt), None if kv is None else dev(kv, dt), win_pos0,
+                            dev(pool, dt) if T else None,
+                            None if z is None else dev(z, torch.float32), q_pos, m=m,
+                            rope_dim=rope, cs=cs, window=window, scale=scale, dv=dv))
+    tol = BF16_ATOL if bf16 else F32_ATOL
+    for b in range(B):
+        t = qp[b] + np.arange(S)
+        ref = oracle.attention(q[b], t, kv_win=None if kv is None else kv[b], win_pos0=0,
+                               window=window, pool=pool[b], idx=None, m=m, sink=z,
+                               rope_dim=rope, theta=theta, scale=scale, dv=dv)
+        err = float(np.abs(out[b] - ref).max())
+        assert err <= tol, (dict(H=H, D=D, dv=dv, m=m, T=T, S=S, window=window), b, err)
