@@ -239,6 +239,29 @@ def test_topk_bit_exact(ops, T, k, m, qp, S):
         assert np.array_equal(idx[b], ref), b
 
 
+@pytest.mark.parametrize("T,k,crowd", [
+    # the k-th largest key lies in a crowded bin of the first 11-bit radix
+    # digit (hundreds to thousands of distinct values and ties), so the second
+    # and third digits decide the selection
+    (32768, 2048, 5000), (32768, 2048, 1500), (12000, 1024, 3000), (6000, 512, 2500),
+    (2048, 512, 900)])
+def test_topk_crowded_top_digit(ops, T, k, crowd):
+    B, S, m = 1, 6, 1
+    r = rng(T + crowd)
+    sc = np.minimum(r.standard_normal((B, S, T)), 1.99).astype(np.float32)
+    for i in range(S):
+        sel = r.choice(T, crowd, replace=False)
+        # [2, 2.5): one bin of the first digit (sign, exponent, two mantissa bits)
+        sc[0, i, sel] = (2.0 + 0.5 * r.random(crowd)).astype(np.float32)
+        sc[0, i, sel[: crowd // 4]] = 2.25  # and ties inside it
+    qp = [T - S]
+    q_pos = torch.tensor(qp, dtype=torch.int32, device="cuda")
+    idx = host(ops.csa_topk(dev(sc, torch.float32), q_pos, k=k, m=m)).astype(np.int32)
+    t = qp[0] + np.arange(S)
+    ref = oracle.topk(sc[0], t, k=k, m=m)
+    assert np.array_equal(idx[0], ref)
+
+
 # ------------------------------------------------------------------ attention
 def _attn_case(seed, B, S, H, D, dv, rope, T, k, window, m, qp, sink, bf16, dense):
     r = rng(seed)
