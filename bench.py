@@ -13,7 +13,10 @@ stream its kernels run on; ``roofline`` reports the dominant kernel's
 algorithmic FLOP/s or bytes/s against the MI355X peak.  CSA decode (64 x 1
 token after 131072 cached tokens) is reported in us/step, and the HCA and DSA
 workloads in tokens/s.  ``cpu_baseline`` times the CPU oracle on a stratified
-sample of the prefill rows.
+sample of the prefill rows.  ``achievable_peaks`` gives what the device
+sustains for the two bounding resources (a bf16 matrix-core loop and a
+streaming read, libcsa_probe.so), and every stage and roofline carries
+``frac_achievable`` against it beside ``frac`` against the published peak.
 
 HBM traffic of the dominant kernels (``roofline.traffic``) comes from two
 rocprofv3 counter runs (FETCH_SIZE, then WRITE_SIZE) of one workload each,
@@ -467,12 +470,66 @@ def run_out_proj(steps, warmup, csa, torch, synth, S=8192, H=64, dv=512, groups=
     return rep
 
 
-def roofline_of(wl_name, res):
+def achievable_key(st):
+    """Which achievable peak a stage is read against: the matrix-core loop of
+    about its length (1 ms or 20 ms) for matrix-core stages, the read else."""
+    if st["bound"] == "mfma":
+        return "mfma_bf16_long" if st["ms"] >= 5.0 else "mfma_bf16_short"
+    return "hbm_read"
+
+
+def add_achievable(stages, ach):
+    for st in stages.values():
+        st["frac_achievable"] = round(st["achieved"] / ach[achievable_key(st)]["value"], 4)
+    return stages
+
+
+def roofline_of(wl_name, res, ach=None):
     dom = res["dominant"]
     st = res["stages"][dom]
-    return {"kernel": dom, "bound": st["bound"], "achieved": st["achieved"], "peak": st["peak"],
-            "unit": st["unit"], "frac": st["frac"],
-            "traffic": measured_traffic(wl_name, dom)}
+    r = {"kernel": dom, "bound": st["bound"], "achieved": st["achieved"], "peak": st["peak"],
+         "unit": st["unit"], "frac": st["frac"],
+         "traffic": measured_traffic(wl_name, dom)}
+    if ach:
+        # the same kernel against what the device sustains (achievable_peaks)
+        key = achievable_key(st)
+        r["achievable_peak"] = ach[key]["value"]
+        r["frac_achievable"] = round(st["achieved"] / ach[key]["value"], 4)
+    return r
+
+
+# ------------------------------------------------------------------ achievable peaks
+def achievable_peaks(torch):
+    """What the device sustains for the two bounding resources (libcsa_probe.so):
+    a bf16 matrix-core loop (two four-wave workgroups per compute unit, eight
+    independent chains per wave, no memory traffic) run for about 1 ms and about
+    20 ms -- the sustained clock depends on the length of a matrix-core-heavy
+    run -- a streaming read of 2 GiB (8x the last-level cache), and the LDS read
+    rate of 16-byte reads and of the transposing 8-byte operand reads."""
+    from sparse_long_context_pool_amd import probe
+    props = torch.cuda.get_device_properties(0)
+    cus = props.multi_processor_count
+    out = {}
+    # (the long run first: it also brings the clock up from idle)
+    for key, iters, reps in (("mfma_bf16_long", 50000, 3), ("mfma_bf16_short", 2500, 9)):
+        tf, _ = probe.mfma_bf16(2 * cus, iters, reps=reps)
+        ms = probe.lib().csa_probe_mfma_flops(2 * cus, iters) / (tf * 1e12) * 1e3
+        out[key] = {"value": round(tf, 1), "unit": "TFLOP/s", "ms": round(ms, 3)}
+    buf = torch.empty(1 << 31, dtype=torch.uint8, device="cuda")
+    gbs, _ = probe.hbm_read(buf, 8 * cus, reps=5)
+    del buf
+    torch.cuda.empty_cache()
+    out["hbm_read"] = {"value": round(gbs, 1), "unit": "GB/s", "bytes": 1 << 31}
+    # LDS read rates of the two operand widths (one 8-wave workgroup per CU, as
+    # the attention kernel runs)
+    for key, mode in (("lds_read_b128", 0), ("lds_read_tr_b64", 1)):
+        tbs, per_clk, _ = probe.lds_read(mode, cus, 4096, reps=5)
+        out[key] = {"value": round(tbs, 2), "unit": "TB/s",
+                    "bytes_per_clock_per_cu": round(per_clk, 1)}
+    print("[bench] achievable: " + ", ".join(f"{k} {v['value']} {v['unit']}"
+                                             for k, v in out.items()),
+          file=sys.stderr, flush=True)
+    return out
 
 
 # ------------------------------------------------------------------ CPU baseline
@@ -708,6 +765,7 @@ def main():
     from sparse_long_context_pool_amd.workloads import WORKLOADS
     csa.lib()
     torch.cuda.set_device(0)
+    ach = achievable_peaks(torch)
 
     names = [n for n in args.workloads.split(",") if n]
     results = {}
@@ -726,15 +784,16 @@ def main():
                    "rope_dim": wl.rope_dim, "m": wl.m, "T": wl.T, "index_heads": wl.n_idx_heads,
                    "index_dim": wl.idx_dim, "index_topk": wl.topk, "window": wl.window,
                    "parallelism": "single GPU"},
-        "roofline": roofline_of(main_name, res),
-        "stages": res["stages"], "setup_ms": res["setup_ms"],
+        "roofline": roofline_of(main_name, res, ach),
+        "stages": add_achievable(res["stages"], ach), "setup_ms": res["setup_ms"],
+        "achievable_peaks": ach,
     }
     for n, (w2, r2) in results.items():
         if n == main_name:
             continue
         key = {"csa_decode_bf16": "decode", "hca_bf16": "hca", "dsa_bf16": "dsa"}.get(n, n)
         entry = {"workload": n, "ms_per_step": r2["ms_per_step"], "setup_ms": r2["setup_ms"],
-                 "roofline": roofline_of(n, r2), "stages": r2["stages"]}
+                 "roofline": roofline_of(n, r2, ach), "stages": add_achievable(r2["stages"], ach)}
         if w2.decode:
             entry["us_per_step"] = r2["us_per_step"]
         else:
@@ -742,9 +801,9 @@ def main():
         line[key] = entry
     if "csa_prefill_bf16" in names and not args.no_next:
         # the rows after the hot path, each measured on its own
-        line["next_rows"] = {"out_proj": run_out_proj(args.steps, args.warmup, csa, torch,
-                                                      synth)}
-        for n, v in res.get("beside_step", {}).items():
+        line["next_rows"] = add_achievable(
+            {"out_proj": run_out_proj(args.steps, args.warmup, csa, torch, synth)}, ach)
+        for n, v in add_achievable(dict(res.get("beside_step", {})), ach).items():
             line["next_rows"][n] = dict(v, workload=f"{main_name}: scores and top-k in one "
                                                     f"call (replaces index_scores + topk)")
     if args.calib_copy:

@@ -4,7 +4,8 @@ Each csrc/*.hip file is compiled on its own with hipcc for gfx950 only, then
 the objects are linked into sparse_long_context_pool_amd/libcsa.so in-tree.
 The same objects, with the C ABI compiled with CSA_DEBUG, also make
 libcsa_debug.so: it checks device-side inputs (attention index rows) before
-each launch, synchronizing the caller's stream.
+each launch, synchronizing the caller's stream.  The achievable-peak probes
+(probes/peaks.hip, include/csa_probe.h) go into libcsa_probe.so.
 Usage: python -m sparse_long_context_pool_amd.build [--resource-usage]
 """
 from __future__ import annotations
@@ -33,6 +34,9 @@ HIP_FLAGS = [
 
 DEBUG_LIB = os.path.join(PKG, "libcsa_debug.so")
 API_SRC = os.path.join(CSRC, "csa_api.hip")
+# the achievable-peak probes (include/csa_probe.h): a library of their own
+PROBE_SRC = os.path.join(PKG, "probes", "peaks.hip")
+PROBE_LIB = os.path.join(PKG, "libcsa_probe.so")
 
 
 def _compile(src: str, extra: list[str], suffix: str = "") -> str:
@@ -54,9 +58,11 @@ def build(resource_usage: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
     extra = ["-Rpass-analysis=kernel-resource-usage"] if resource_usage else []
-    jobs = [(s, extra, "") for s in srcs] + [(API_SRC, extra + ["-DCSA_DEBUG"], "_debug")]
+    jobs = [(s, extra, "") for s in srcs] + [(API_SRC, extra + ["-DCSA_DEBUG"], "_debug"),
+                                             (PROBE_SRC, extra, "")]
     with ThreadPoolExecutor(min(8, len(jobs))) as ex:
         objs = list(ex.map(lambda j: _compile(*j), jobs))
+    probe_obj = objs.pop()
     api_debug = objs.pop()
     for lib, members in ((LIB, objs),
                          (DEBUG_LIB, [api_debug if os.path.basename(o) == "csa_api.o" else o
@@ -66,6 +72,11 @@ def build(resource_usage: bool = False) -> str:
                         *members], check=True)
         _check_stubs(tmp)
         os.replace(tmp, lib)
+    tmp = PROBE_LIB + ".tmp"
+    subprocess.run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, probe_obj],
+                   check=True)
+    _check_stubs(tmp)
+    os.replace(tmp, PROBE_LIB)
     return LIB
 
 

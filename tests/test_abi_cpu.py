@@ -182,3 +182,35 @@ def test_workspace_plans(L):
     # fp32 never splits
     assert L.csa_sparse_attn_workspace_size(1, 4, 4, 64, 64, 16, 16, 32, 0) == 0
     assert L.hca_attn_workspace_size(1, 2, 64, 512, 512, 64, 512, 128, 1) > 0
+
+
+# ------------------------------------------------------------------ probe library
+PROBE_HEADER = os.path.join(ROOT, "include", "csa_probe.h")
+
+
+def probe_declared_functions():
+    text = open(PROBE_HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(?:int|double)\s+(\w+)\s*\(", text)))
+
+
+def test_probe_library_exports_its_header():
+    from sparse_long_context_pool_amd import probe
+    P = probe.lib()
+    names = probe_declared_functions()
+    assert names == sorted(probe.EXPORTS)
+    for n in names:
+        assert hasattr(P, n), n
+    ctypes.CDLL(probe._LIB_PATH, mode=os.RTLD_NOW | os.RTLD_LOCAL)
+
+
+def test_probe_arguments_are_checked_on_the_host():
+    from sparse_long_context_pool_amd import probe
+    P = probe.lib()
+    assert P.csa_probe_mfma_bf16(None, 4, 10, None) != 0
+    assert P.csa_probe_mfma_bf16(ctypes.c_void_p(16), 0, 10, None) != 0
+    assert P.csa_probe_read(None, 1024, ctypes.c_void_p(16), 4, None) != 0
+    assert P.csa_probe_read(ctypes.c_void_p(16), 1000, ctypes.c_void_p(16), 4, None) != 0
+    assert P.csa_probe_read(ctypes.c_void_p(8), 1024, ctypes.c_void_p(16), 4, None) != 0
+    # 4 waves x 8 chains x 32768 flop per round
+    assert P.csa_probe_mfma_flops(3, 7) == 3 * 4 * 8 * 32768 * 7
