@@ -695,7 +695,8 @@ def summarize_pmc(csv_paths):
     """Markdown table of rocprofv3 counter runs (`--pmc ... -f csv`): per kernel
     the mean over its dispatches of MFMA busy (SQ_VALU_MFMA_BUSY_CYCLES over
     GRBM_GUI_ACTIVE of one XCD times the 1024 SIMDs), LDS busy and bank-conflict
-    share, and the raw means of every counter taken."""
+    share, texture-addresser busy (TA_TA_BUSY over one XCD's active cycles times
+    the 256 compute units), and the raw means of every counter taken."""
     import csv
     vals = {}
     for path in csv_paths:
@@ -717,6 +718,9 @@ def summarize_pmc(csv_paths):
             if "SQ_LDS_BANK_CONFLICT" in mean:
                 line += (f" bank-conflict cycles / LDS busy "
                          f"{mean['SQ_LDS_BANK_CONFLICT'] / max(mean['SQ_LDS_IDX_ACTIVE'], 1):.3f};")
+        if gui and "TA_TA_BUSY" in mean:
+            # one texture addresser per compute unit (the counter sums them)
+            line += f" TA busy {mean['TA_TA_BUSY'] / (gui / 8 * 256):.3f};"
         line += " raw means: " + ", ".join(f"{c} {v:.4g}" for c, v in sorted(mean.items()))
         out.append(line)
     return "\n".join(out)
