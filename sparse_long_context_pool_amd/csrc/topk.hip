@@ -158,8 +158,10 @@ __global__ __launch_bounds__(NT) void topk_reg(
   static_assert(BPT == 2 || BPT == 4 || BPT == 8, "bins per thread");
   __shared__ uint32_t hist[2][2048];
   __shared__ int wtot[NW];
-  __shared__ int meta[2];
+  __shared__ int meta[3];  // digit, keys above its bin, bin taken whole
   __shared__ int gtot[KPT * NW], etot[KPT * NW];  // per (slice, wave) counts, then prefixes
+  __shared__ int wsg[NW], wse[NW];                // wave totals of the prefix scan
+  static_assert(KPT <= 64, "one (slice, wave) entry per thread");
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const long row = blockIdx.x;
@@ -189,12 +191,20 @@ __global__ __launch_bounds__(NT) void topk_reg(
   int kk = k;
   int buf = 0;
   for (int j = tid; j < 2048; j += NT) hist[0][j] = 0u;
+  __syncthreads();  // the first histogram is clear
+  // Pass p: atomics into h, barrier, bin counts and wave suffix sums, barrier,
+  // the digit, barrier.  A pass needs no barrier before its atomics: its
+  // histogram was cleared during the previous pass, and the previous pass's
+  // reads of wtot, meta and the other histogram all precede its last barrier.
+  // The passes stop early once the bin holding the kk-th largest key is taken
+  // whole (its count is exactly kk): every key matching the prefix so far is
+  // kept, and K = the prefix with zero low bits keeps exactly them (keys above
+  // it, and the copies of K itself, all of which kk admits).
 #pragma unroll
   for (int pass = 0; pass < 3; ++pass) {
     const int shift = pass == 0 ? 21 : pass == 1 ? 10 : 0;
     const uint32_t dmask = pass == 2 ? 1023u : 2047u;
     uint32_t* h = hist[buf];
-    __syncthreads();  // h cleared, meta of the last pass read
     // (entries past R, key 0, are skipped: they would all hit one bin of the
     // first pass and serialise its atomics)
 #pragma unroll
@@ -235,6 +245,7 @@ __global__ __launch_bounds__(NT) void topk_reg(
       if (above < kk && above + cnt[u] >= kk) {
         meta[0] = BPT * tid + u;
         meta[1] = above;
+        meta[2] = above + cnt[u] == kk ? 1 : 0;
       }
       above += cnt[u];
     }
@@ -244,6 +255,7 @@ __global__ __launch_bounds__(NT) void topk_reg(
     prefix |= digit << shift;
     pmask |= dmask << shift;
     buf ^= 1;
+    if (meta[2] != 0) break;  // uniform: the bin is taken whole
   }
 
   // prefix is the k-th largest key K: keep every key > K and the first kk
@@ -271,28 +283,33 @@ __global__ __launch_bounds__(NT) void topk_reg(
     __builtin_amdgcn_sched_barrier(0);
   }
   __syncthreads();
-  // exclusive prefix over (slice, wave) in index order, by wave 0
-  if (wave == 0) {
-    int rg = 0, re = 0;
-    for (int base = 0; base < KPT * NW; base += 64) {
-      const int s = base + lane;
-      int g = s < KPT * NW ? gtot[s] : 0, e = s < KPT * NW ? etot[s] : 0;
-      int ig = g, ie = e;  // inclusive scans over the 64 lanes
+  // exclusive prefix over the KPT x NW (slice, wave) counts in index order:
+  // thread s takes entry s (KPT NW <= NT), inclusive scans within each wave,
+  // then each wave adds the totals of the waves before it
+  {
+    constexpr int E = KPT * NW;
+    const int g = tid < E ? gtot[tid] : 0, e = tid < E ? etot[tid] : 0;
+    int ig = g, ie = e;
 #pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const int vg = __shfl_up(ig, off, 64), ve = __shfl_up(ie, off, 64);
-        if (lane >= off) { ig += vg; ie += ve; }
-      }
-      if (s < KPT * NW) { gtot[s] = rg + ig - g; etot[s] = re + ie - e; }
-      rg += __shfl(ig, 63, 64);
-      re += __shfl(ie, 63, 64);
+    for (int off = 1; off < 64; off <<= 1) {
+      const int vg = __shfl_up(ig, off, 64), ve = __shfl_up(ie, off, 64);
+      if (lane >= off) { ig += vg; ie += ve; }
     }
+    if (lane == 63) { wsg[wave] = ig; wse[wave] = ie; }
+    __syncthreads();
+    int bg = 0, be = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w)
+      if (w < wave) { bg += wsg[w]; be += wse[w]; }
+    if (tid < E) { gtot[tid] = bg + ig - g; etot[tid] = be + ie - e; }
   }
   __syncthreads();
   // the ballots are recomputed rather than kept: opaque keys stop the
   // compiler from reusing the first ones
 #pragma unroll
   for (int j = 0; j < KPT; ++j) asm volatile("" : "+v"(key[j]));
+  // (the row's k slots through a bounded descriptor: 32-bit offsets)
+  const __amdgpu_buffer_rsrc_t ors = __builtin_amdgcn_make_buffer_rsrc(out, 0, k * 4, 0x00020000);
 #pragma unroll
   for (int j0 = 0; j0 < KPT; j0 += GS) {
     int gb0[GS], eb0[GS];
@@ -306,9 +323,19 @@ __global__ __launch_bounds__(NT) void topk_reg(
       const int j = j0 + u;
       const bool gt = key[j] > K, eq = key[j] == K;
       const uint64_t mg = __ballot(gt), me = __ballot(eq);
-      const int gb = gb0[u] + __popcll(mg & lt);
-      const int eb = eb0[u] + __popcll(me & lt);
-      if (gt || (eq && eb < kk)) out[gb + min(eb, kk)] = j * NT + tid;
+      int pos;
+      bool take;
+      if (me == 0ull) {
+        // no copy of K among this wave's keys of the slice (nearly every
+        // slice): the copies before it are all counted in eb0
+        pos = gb0[u] + __popcll(mg & lt) + min(eb0[u], kk);
+        take = gt;
+      } else {
+        const int eb = eb0[u] + __popcll(me & lt);
+        pos = gb0[u] + __popcll(mg & lt) + min(eb, kk);
+        take = gt || (eq && eb < kk);
+      }
+      if (take) __builtin_amdgcn_raw_buffer_store_b32(j * NT + tid, ors, 4 * pos, 0, 0);
     }
     __builtin_amdgcn_sched_barrier(0);
   }
