@@ -156,7 +156,15 @@ __global__ __launch_bounds__(NT) void topk_reg(
   constexpr int NW = NT / 64;
   constexpr int BPT = 2048 / NT;
   static_assert(BPT == 2 || BPT == 4 || BPT == 8, "bins per thread");
-  __shared__ uint32_t hist[2][2048];
+  // the first pass spreads its counts over HC copies of the histogram (lane
+  // l counts into copy l % HC; copies one word apart in bank order), so that
+  // lanes of one atomic instruction whose keys share a bin mostly hit
+  // different words; the rows of up to 2048 entries (eight workgroups per
+  // compute unit) keep one copy for their LDS budget
+  constexpr int HC = NT >= 512 ? 4 : 1;
+  constexpr int HS = HC > 1 ? 2049 : 2048;  // words between copies
+  __shared__ __attribute__((aligned(16))) uint32_t hist0[HC * HS];
+  __shared__ __attribute__((aligned(16))) uint32_t hist1[2048];
   __shared__ int wtot[NW];
   __shared__ int meta[3];  // digit, keys above its bin, bin taken whole
   __shared__ int gtot[KPT * NW], etot[KPT * NW];  // per (slice, wave) counts, then prefixes
@@ -190,7 +198,7 @@ __global__ __launch_bounds__(NT) void topk_reg(
   uint32_t prefix = 0u, pmask = 0u;
   int kk = k;
   int buf = 0;
-  for (int j = tid; j < 2048; j += NT) hist[0][j] = 0u;
+  for (int j = tid; j < HC * HS; j += NT) hist0[j] = 0u;
   __syncthreads();  // the first histogram is clear
   // Pass p: atomics into h, barrier, bin counts and wave suffix sums, barrier,
   // the digit, barrier.  A pass needs no barrier before its atomics: its
@@ -204,18 +212,29 @@ __global__ __launch_bounds__(NT) void topk_reg(
   for (int pass = 0; pass < 3; ++pass) {
     const int shift = pass == 0 ? 21 : pass == 1 ? 10 : 0;
     const uint32_t dmask = pass == 2 ? 1023u : 2047u;
-    uint32_t* h = hist[buf];
+    // pass 0: hist0 (HC copies); pass 1: hist1; pass 2: hist0's first copy
+    uint32_t* h = buf == 0 ? hist0 : hist1;
+    uint32_t* hc = pass == 0 ? hist0 + (lane % HC) * HS : h;
     // (entries past R, key 0, are skipped: they would all hit one bin of the
     // first pass and serialise its atomics)
 #pragma unroll
     for (int j = 0; j < KPT; ++j)
-      if (key[j] != 0u && (key[j] & pmask) == prefix) atomicAdd(&h[(key[j] >> shift) & dmask], 1u);
-    // clear the other copy for the next pass meanwhile
-    for (int j = tid; j < 2048; j += NT) hist[buf ^ 1][j] = 0u;
+      if (key[j] != 0u && (key[j] & pmask) == prefix) atomicAdd(&hc[(key[j] >> shift) & dmask], 1u);
+    // clear the other histogram for the next pass meanwhile (its first 2048
+    // words: a later pass uses one copy)
+    for (int j = tid; j < 2048; j += NT) (buf == 0 ? hist1 : hist0)[j] = 0u;
     __syncthreads();
     // thread t owns bins BPT t .. BPT t + BPT-1; suffix sums over the bins above
     int cnt[BPT];
-    if constexpr (BPT == 2) {
+    if (HC > 1 && pass == 0) {
+#pragma unroll
+      for (int u = 0; u < BPT; ++u) {
+        int c = 0;
+#pragma unroll
+        for (int q = 0; q < HC; ++q) c += (int)hist0[q * HS + BPT * tid + u];
+        cnt[u] = c;
+      }
+    } else if constexpr (BPT == 2) {
       const uint2 hb = *reinterpret_cast<const uint2*>(&h[2 * tid]);
       cnt[0] = (int)hb.x; cnt[1] = (int)hb.y;
     } else {
