@@ -186,22 +186,33 @@ __global__ __launch_bounds__(NT) void topk_reg(
   // any score that is not NaN (-inf maps to 0x007fffff), so they fall in the
   // lowest bin of the first pass, never match a later prefix and are never
   // kept: no separate validity test is needed.
+  // The first histogram is cleared before the loads are issued, so that the
+  // first pass's atomics run as the keys arrive (each key is counted as soon
+  // as its load has landed) instead of after all of them.
   // (the loads are unconditional, clamped into the row, so that all of them
   // are in flight together)
+  for (int j = tid; j < HC * HS; j += NT) hist0[j] = 0u;
+  __syncthreads();  // the first histogram is clear
   float sv[KPT];
 #pragma unroll
   for (int j = 0; j < KPT; ++j) sv[j] = src[min(j * NT + tid, R - 1)];
   uint32_t key[KPT];
+  {
+    // first pass's atomics (digit = the top 11 bits; entries past R, key 0,
+    // are skipped: they would all hit one bin and serialise the atomics)
+    uint32_t* hc0 = hist0 + (lane % HC) * HS;
 #pragma unroll
-  for (int j = 0; j < KPT; ++j) key[j] = j * NT + tid < R ? score_key(sv[j]) : 0u;
+    for (int j = 0; j < KPT; ++j) {
+      key[j] = j * NT + tid < R ? score_key(sv[j]) : 0u;
+      if (key[j] != 0u) atomicAdd(&hc0[key[j] >> 21], 1u);
+    }
+  }
 
   uint32_t prefix = 0u, pmask = 0u;
   int kk = k;
   int buf = 0;
-  for (int j = tid; j < HC * HS; j += NT) hist0[j] = 0u;
-  __syncthreads();  // the first histogram is clear
-  // Pass p: atomics into h, barrier, bin counts and wave suffix sums, barrier,
-  // the digit, barrier.  A pass needs no barrier before its atomics: its
+  // Pass p: atomics into h (pass 0's were issued with the loads), barrier, bin
+  // counts and wave suffix sums, barrier, the digit, barrier.  A pass needs no barrier before its atomics: its
   // histogram was cleared during the previous pass, and the previous pass's
   // reads of wtot, meta and the other histogram all precede its last barrier.
   // The passes stop early once the bin holding the kk-th largest key is taken
@@ -214,12 +225,12 @@ __global__ __launch_bounds__(NT) void topk_reg(
     const uint32_t dmask = pass == 2 ? 1023u : 2047u;
     // pass 0: hist0 (HC copies); pass 1: hist1; pass 2: hist0's first copy
     uint32_t* h = buf == 0 ? hist0 : hist1;
-    uint32_t* hc = pass == 0 ? hist0 + (lane % HC) * HS : h;
-    // (entries past R, key 0, are skipped: they would all hit one bin of the
-    // first pass and serialise its atomics)
+    // (the first pass counted its keys as they were loaded)
+    if (pass > 0) {
 #pragma unroll
-    for (int j = 0; j < KPT; ++j)
-      if (key[j] != 0u && (key[j] & pmask) == prefix) atomicAdd(&hc[(key[j] >> shift) & dmask], 1u);
+      for (int j = 0; j < KPT; ++j)
+        if (key[j] != 0u && (key[j] & pmask) == prefix) atomicAdd(&h[(key[j] >> shift) & dmask], 1u);
+    }
     // clear the other histogram for the next pass meanwhile (its first 2048
     // words: a later pass uses one copy)
     for (int j = tid; j < 2048; j += NT) (buf == 0 ? hist1 : hist0)[j] = 0u;
