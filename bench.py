@@ -504,7 +504,8 @@ def achievable_peaks(torch):
     a bf16 matrix-core loop (two four-wave workgroups per compute unit, eight
     independent chains per wave, no memory traffic) run for about 1 ms and about
     20 ms -- the sustained clock depends on the length of a matrix-core-heavy
-    run -- a streaming read of 2 GiB (8x the last-level cache), and the LDS read
+    run -- a streaming read of 4 GiB (16x the last-level cache; non-temporal
+    loads, 32 workgroups per compute unit), and the LDS read
     rate of 16-byte reads and of the transposing 8-byte operand reads."""
     from sparse_long_context_pool_amd import probe
     props = torch.cuda.get_device_properties(0)
@@ -515,11 +516,11 @@ def achievable_peaks(torch):
         tf, _ = probe.mfma_bf16(2 * cus, iters, reps=reps)
         ms = probe.lib().csa_probe_mfma_flops(2 * cus, iters) / (tf * 1e12) * 1e3
         out[key] = {"value": round(tf, 1), "unit": "TFLOP/s", "ms": round(ms, 3)}
-    buf = torch.empty(1 << 31, dtype=torch.uint8, device="cuda")
-    gbs, _ = probe.hbm_read(buf, 8 * cus, reps=5)
+    buf = torch.empty(1 << 32, dtype=torch.uint8, device="cuda")
+    gbs, _ = probe.hbm_read(buf, 32 * cus, reps=5)
     del buf
     torch.cuda.empty_cache()
-    out["hbm_read"] = {"value": round(gbs, 1), "unit": "GB/s", "bytes": 1 << 31}
+    out["hbm_read"] = {"value": round(gbs, 1), "unit": "GB/s", "bytes": 1 << 32}
     # LDS read rates of the two operand widths (one 8-wave workgroup per CU, as
     # the attention kernel runs)
     for key, mode in (("lds_read_b128", 0), ("lds_read_tr_b64", 1)):

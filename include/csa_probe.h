@@ -34,8 +34,8 @@ int csa_probe_mfma_bf16(float *sink, int32_t n_wg, int32_t iters, hipStream_t st
 double csa_probe_mfma_flops(int32_t n_wg, int32_t iters);
 
 /* Streaming read: n_wg workgroups of 256 threads read `bytes` bytes at `buf`
- * once, 16 bytes per lane per load with four loads in flight per thread
- * (grid-stride order, so each load instruction of a wave covers 1 KiB
+ * once, 16 bytes per lane per non-temporal load with eight loads in flight per
+ * thread (grid-stride order, so each load instruction of a wave covers 1 KiB
  * contiguous), and thread i writes the xor of the words it read to sink[i]
  * (sink: n_wg * 256 uint32).  bytes is a multiple of 16 and buf 16-byte
  * aligned. */

@@ -193,9 +193,16 @@ __global__ __launch_bounds__(NT) void topk_reg(
   // are in flight together)
   for (int j = tid; j < HC * HS; j += NT) hist0[j] = 0u;
   __syncthreads();  // the first histogram is clear
+  // (rows of more than 8192 entries -- decode, token-level rows -- load
+  // their scores non-temporally: each is read once, and this measured ~1 us
+  // faster on the decode rows; the short prefill rows, still in the caches
+  // from the index kernel, measured ~1 us slower with it)
   float sv[KPT];
 #pragma unroll
-  for (int j = 0; j < KPT; ++j) sv[j] = src[min(j * NT + tid, R - 1)];
+  for (int j = 0; j < KPT; ++j) {
+    const float* a = src + min(j * NT + tid, R - 1);
+    sv[j] = NT >= 1024 ? __builtin_nontemporal_load(a) : *a;
+  }
   uint32_t key[KPT];
   {
     // first pass's atomics (digit = the top 11 bits; entries past R, key 0,

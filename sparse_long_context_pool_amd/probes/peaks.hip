@@ -57,20 +57,29 @@ __global__ __launch_bounds__(256, 2) void mfma_loop(float* __restrict__ sink, in
   sink[gid] = s;
 }
 
-// Grid-stride 16-byte loads, four in flight per thread per iteration.
+// Grid-stride 16-byte loads, eight in flight per thread per iteration, marked
+// non-temporal (streamed once).  Swept on one box (4 GiB, best of five): plain
+// loads 5.4-6.0 TB/s over 4-64 workgroups per compute unit and 4-16 loads in
+// flight; non-temporal loads 5.7-6.5 TB/s, the most with 8 in flight and 32
+// workgroups per compute unit -- the shape the bench runs.
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
 __global__ __launch_bounds__(256) void read_loop(const uint4* __restrict__ buf, size_t n16,
                                                  uint32_t* __restrict__ sink) {
+  constexpr int U = 8;
   const size_t stride = (size_t)gridDim.x * 256u;
   size_t i = (size_t)blockIdx.x * 256u + threadIdx.x;
+  const u32x4* b = reinterpret_cast<const u32x4*>(buf);
   uint32_t x = 0u;
-  for (; i + 3 * stride < n16; i += 4 * stride) {
-    const uint4 v0 = buf[i], v1 = buf[i + stride], v2 = buf[i + 2 * stride],
-                v3 = buf[i + 3 * stride];
-    x ^= (v0.x ^ v0.y ^ v0.z ^ v0.w) ^ (v1.x ^ v1.y ^ v1.z ^ v1.w) ^
-         (v2.x ^ v2.y ^ v2.z ^ v2.w) ^ (v3.x ^ v3.y ^ v3.z ^ v3.w);
+  for (; i + (U - 1) * stride < n16; i += U * stride) {
+    u32x4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = __builtin_nontemporal_load(b + i + u * stride);
+#pragma unroll
+    for (int u = 0; u < U; ++u) x ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
   }
   for (; i < n16; i += stride) {
-    const uint4 v = buf[i];
+    const u32x4 v = __builtin_nontemporal_load(b + i);
     x ^= v.x ^ v.y ^ v.z ^ v.w;
   }
   sink[(size_t)blockIdx.x * 256u + threadIdx.x] = x;
