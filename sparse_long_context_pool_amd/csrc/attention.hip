@@ -33,13 +33,16 @@ namespace {
 constexpr int kNK = 32;     // keys per tile
 constexpr int kPS = kNK + 8;  // P row stride (u16): 80 bytes keeps P reads conflict-free
 constexpr int kMaxK = 2048;   // index slots per query the matrix-core kernel keeps in LDS
-// Cache-policy operand of buffer loads and stores: the non-temporal hint.  The
-// queries (each read once) and the outputs (each written once, and together
-// far larger than the 256 MB last-level cache: 512 MB for an 8192-token
-// prefill) carry it, so that streaming them does not evict what the caches
-// hold for the stages around the attention (measured: the next step's
-// compression 21.5 -> 19.5 us and index scores 130 -> 126 us on CSA prefill,
-// HCA compression 80 -> 62 us; the attention itself unchanged).
+// Cache-policy operand of buffer loads and stores: the non-temporal hint.  On
+// the 512-wide rows (CSA, HCA) the queries (each read once) and the outputs
+// (each written once, and together far larger than the 256 MB last-level
+// cache: 512 MB for an 8192-token prefill) carry it, so that streaming them
+// does not evict what the caches hold for the stages around the attention
+// (measured: the next step's compression 21.5 -> 19.5 us and index scores
+// 130 -> 126 us on CSA prefill, HCA compression 80 -> 62 us; the attention
+// itself unchanged).  The 576-wide DSA rows keep plain queries and outputs:
+// with the hint their attention fetched 53 GB instead of 40 GB and ran 1%
+// slower.
 constexpr int kNT = 2;
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
@@ -280,6 +283,7 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(MfmaArgs args) {
   constexpr int KS = D / 32;
   constexpr int R = 64, half = R / 2, rbase = D - R;
   constexpr float kRescale = 64.f;
+  constexpr int QO = D == 512 ? kNT : 0;             // cache policy of queries and outputs
   constexpr int NS = 4;                              // S waves (and PV waves)
   constexpr int RPW = kNK / NS;                      // gathered rows per PV wave per tile
   constexpr int NSCAN = kMaxK / (NS * 64);           // index-row loads per S lane
@@ -479,8 +483,9 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(MfmaArgs args) {
       const u16* qrow = reinterpret_cast<const u16*>(p.q) + (row * H + it.h0 + hq) * D;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
-        qf[ks] = __builtin_bit_cast(
-            bf16x8, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(qrow + 32 * ks + 8 * g)));
+        qf[ks] = QO != 0 ? __builtin_bit_cast(bf16x8, __builtin_nontemporal_load(
+                                                   reinterpret_cast<const u32x4*>(qrow + 32 * ks + 8 * g)))
+                         : as_bf16x8(*reinterpret_cast<const uint4*>(qrow + 32 * ks + 8 * g));
 #pragma unroll
       for (int kr = 0; kr < KR; ++kr) {
         const float4* c4 = reinterpret_cast<const float4*>(cs + (long)t * half + 16 * kr + 4 * g);
@@ -511,7 +516,7 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(MfmaArgs args) {
       const int qoff = (hq * D + 8 * g) * 2;
       auto qld = [&](int ks) __attribute__((always_inline)) -> bf16x8 {
         return __builtin_bit_cast(bf16x8,
-                                  __builtin_amdgcn_raw_buffer_load_b128(qrs, qoff, 64 * ks, kNT));
+                                  __builtin_amdgcn_raw_buffer_load_b128(qrs, qoff, 64 * ks, QO));
       };
       if constexpr (part == 0) {
 #pragma unroll
@@ -1015,7 +1020,7 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(MfmaArgs args) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
           __builtin_amdgcn_raw_buffer_store_b128(d[i], ors, olane,
-                                                 (32 * pass + 4 * (i0 + i)) * dv * 2, kNT);
+                                                 (32 * pass + 4 * (i0 + i)) * dv * 2, QO);
       }
     }
   };
