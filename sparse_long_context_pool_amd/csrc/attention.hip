@@ -1113,7 +1113,12 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(MfmaArgs args) {
 
 // Merge split partials: M = max(z, m_s), L = e^(z-M) + sum e^(m_s-M) l_s,
 // O = sum e^(m_s-M) O_s / L, then the output rope slice is rotated at -t.
-// Thread = 8 consecutive columns of one head; 4 heads per workgroup.
+// Thread = 8 consecutive columns of one head; 4 heads per workgroup.  With at
+// most NSM splits (NSM > 0: the decode shapes) every load of a thread --
+// sink, (m, l) pairs, partial outputs, RoPE factors -- is issued before any
+// arithmetic, one memory round trip instead of a chain of them; NSM = 0
+// loops over any number of splits.
+template <int NSM>
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnParams p, const float* ws,
                                                            int nsplit) {
   const long row = blockIdx.x;
@@ -1129,32 +1134,70 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnParams p, const f
   const float* ml = ws + (size_t)row * nsplit * H * 2;
   const u16* po = reinterpret_cast<const u16*>(ws + (size_t)((long)p.B * p.S) * nsplit * H * 2) +
                   (size_t)row * nsplit * H * dv;
-  float M = p.sink ? p.sink[h] * kLog2e : -INFINITY;
+  const bool tin = t >= 0 && t < p.n_pos;
+  const bool rot = p.dv == p.D && p.rope_dim > 0 && tin;
+  float zs = p.sink ? p.sink[h] * kLog2e : -INFINITY;
+  float M = zs;
   bool nan = false;
-  for (int s = 0; s < nsplit; ++s) {
-    const float ms = ml[(s * H + h) * 2];
-    if (ms != ms) nan = true;
-    M = fmaxf(M, ms);
-  }
-  const float Mb = (M == -INFINITY) ? 0.f : M;
-  float L = p.sink ? exp2f(p.sink[h] * kLog2e - Mb) : 0.f;
   float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int s = 0; s < nsplit; ++s) {
-    const float f = exp2f(ml[(s * H + h) * 2] - Mb);
-    L += f * ml[(s * H + h) * 2 + 1];
-    const uint4 u = *reinterpret_cast<const uint4*>(po + ((size_t)s * H + h) * dv + c);
+  float L;
+  // the output's rope pairs: RoPE factors at t (loaded with the rest)
+  float2 r4[4];
+#pragma unroll
+  for (int e = 0; e < 8; e += 2)
+    r4[e >> 1] = (rot && c + e >= rbase) ? cs[t * half + ((c + e - rbase) >> 1)]
+                                         : make_float2(1.f, 0.f);
+  auto acc8 = [&](float f, const uint4 u) __attribute__((always_inline)) {
     o[0] += f * bf_lo(u.x); o[1] += f * bf_hi(u.x); o[2] += f * bf_lo(u.y); o[3] += f * bf_hi(u.y);
     o[4] += f * bf_lo(u.z); o[5] += f * bf_hi(u.z); o[6] += f * bf_lo(u.w); o[7] += f * bf_hi(u.w);
+  };
+  if constexpr (NSM > 0) {
+    float2 msl[NSM];
+    uint4 u[NSM];
+#pragma unroll
+    for (int s = 0; s < NSM; ++s) {
+      if (s < nsplit) {
+        msl[s] = *reinterpret_cast<const float2*>(ml + (s * H + h) * 2);
+        u[s] = *reinterpret_cast<const uint4*>(po + ((size_t)s * H + h) * dv + c);
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < NSM; ++s)
+      if (s < nsplit) {
+        if (msl[s].x != msl[s].x) nan = true;
+        M = fmaxf(M, msl[s].x);
+      }
+    const float Mb = (M == -INFINITY) ? 0.f : M;
+    L = p.sink ? exp2f(zs - Mb) : 0.f;
+#pragma unroll
+    for (int s = 0; s < NSM; ++s)
+      if (s < nsplit) {
+        const float f = exp2f(msl[s].x - Mb);
+        L += f * msl[s].y;
+        acc8(f, u[s]);
+      }
+  } else {
+    for (int s = 0; s < nsplit; ++s) {
+      const float ms = ml[(s * H + h) * 2];
+      if (ms != ms) nan = true;
+      M = fmaxf(M, ms);
+    }
+    const float Mb = (M == -INFINITY) ? 0.f : M;
+    L = p.sink ? exp2f(zs - Mb) : 0.f;
+    for (int s = 0; s < nsplit; ++s) {
+      const float f = exp2f(ml[(s * H + h) * 2] - Mb);
+      L += f * ml[(s * H + h) * 2 + 1];
+      acc8(f, *reinterpret_cast<const uint4*>(po + ((size_t)s * H + h) * dv + c));
+    }
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
 #pragma unroll
   for (int e = 0; e < 8; ++e) o[e] *= inv;
-  const bool tin = t >= 0 && t < p.n_pos;
-  if (p.dv == p.D && p.rope_dim > 0 && tin) {
+  if (rot) {
 #pragma unroll
     for (int e = 0; e < 8; e += 2) {
       if (c + e >= rbase) {
-        const float2 r = cs[t * half + ((c + e - rbase) >> 1)];
+        const float2 r = r4[e >> 1];
         const float a = o[e], bb = o[e + 1];
         o[e] = a * r.x + bb * r.y;
         o[e + 1] = -a * r.y + bb * r.x;
@@ -1266,8 +1309,13 @@ hipError_t launch_attention(const AttnParams& p, const AttnPlan& plan, void* ws,
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || !split) return err;
   const int per_wg = 256 / (p.dv / 8);
-  hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)rows, (p.H + per_wg - 1) / per_wg),
-                     dim3(256), 0, s, p, reinterpret_cast<const float*>(ws), a.nsplit);
+  const dim3 cgrid((unsigned)rows, (p.H + per_wg - 1) / per_wg);
+  if (a.nsplit <= 8)
+    hipLaunchKernelGGL((attn_combine_kernel<8>), cgrid, dim3(256), 0, s, p,
+                       reinterpret_cast<const float*>(ws), a.nsplit);
+  else
+    hipLaunchKernelGGL((attn_combine_kernel<0>), cgrid, dim3(256), 0, s, p,
+                       reinterpret_cast<const float*>(ws), a.nsplit);
   return hipGetLastError();
 }
 
