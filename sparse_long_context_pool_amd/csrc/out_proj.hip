@@ -14,8 +14,9 @@
 //
 // Matrix-core kernel (bf16, fp32 accumulation): a 256 x 256 output tile per
 // workgroup of 8 waves, K in steps of 32 through a 5-deep ring of LDS tiles
-// (160 KiB: four tiles in flight) filled by direct-to-LDS 16-byte buffer loads
-// (each wave loads 4 KiB of each tile, spread between its products).  The MFMA (v_mfma_f32_32x32x16_bf16) takes weight rows as its A
+// (160 KiB: four tiles in flight, one static array per stage) filled by
+// direct-to-LDS 16-byte buffer loads (each wave loads 4 KiB of each tile,
+// spread between its products).  The MFMA (v_mfma_f32_32x32x16_bf16) takes weight rows as its A
 // operand and token rows as its B operand, so the accumulator of a lane holds
 // four consecutive output features of one token: 8-byte bf16 stores.  Each
 // wave owns 128 features x 64 tokens (4 x 2 blocks of 32 x 32).  Tile rows are
@@ -25,6 +26,8 @@
 // dropped (bounded descriptor).
 // Generic kernel (fp32, other shapes): one thread per output element, the
 // sum taken in k order.
+#include <type_traits>
+
 #include "csa_device.hpp"
 
 namespace csa {
@@ -46,7 +49,25 @@ struct GemmArgs {
 __device__ __forceinline__ int gswz(int r) { return (r >> 2) & 3; }
 
 __global__ __launch_bounds__(512) void gemm_nt_mfma(GemmArgs a) {
-  __shared__ __attribute__((aligned(16))) unsigned char lds[kGStages][2][kGTileBytes];
+  // One static array per ring stage (weight tile, then token tile): with
+  // distinct objects the compiler sees that the loads in flight into the
+  // later stages do not alias the reads of the current one, and waits only
+  // for the loads of the stage it reads (one array for the whole ring made it
+  // wait for every load in flight before each LDS read).
+  __shared__ __attribute__((aligned(16))) unsigned char st0[2 * kGTileBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char st1[2 * kGTileBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char st2[2 * kGTileBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char st3[2 * kGTileBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char st4[2 * kGTileBytes];
+  static_assert(kGStages == 5, "one array per stage");
+  auto stage = [&](auto JC) __attribute__((always_inline)) -> unsigned char* {
+    constexpr int J = decltype(JC)::value % kGStages;
+    if constexpr (J == 0) return st0;
+    else if constexpr (J == 1) return st1;
+    else if constexpr (J == 2) return st2;
+    else if constexpr (J == 3) return st3;
+    else return st4;
+  };
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = blockIdx.z;
@@ -74,15 +95,17 @@ __global__ __launch_bounds__(512) void gemm_nt_mfma(GemmArgs a) {
     // no load touches memory past the tensor)
     xoff[u] = ((min(m0 + r, a.M - 1) * a.ldx) + g * a.K + 8 * lc) * 2;
   }
-  auto issue = [&](int kt, int st) __attribute__((always_inline)) {
+  // load u (0, 1: weight blocks; 2, 3: token blocks) of tile kt into stage J
+  auto issue_one = [&](auto JC, int kt, int u) __attribute__((always_inline)) {
+    unsigned char* sb = stage(JC);
     const int kb = kt * kGK * 2;
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
+    if (u < 2)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          wrs, (lds_void*)(&lds[st][0][1024 * (2 * wave + u)]), 16, woff[u], kb, 0, 0);
+          wrs, (lds_void*)(sb + 1024 * (2 * wave + u)), 16, woff[u], kb, 0, 0);
+    else
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          xrs, (lds_void*)(&lds[st][1][1024 * (2 * wave + u)]), 16, xoff[u], kb, 0, 0);
-    }
+          xrs, (lds_void*)(sb + kGTileBytes + 1024 * (2 * wave + u - 2)), 16, xoff[u - 2], kb,
+          0, 0);
   };
 
   // Fragment reads: block of 32 rows from row rb, k-step s: lane l reads row
@@ -98,7 +121,7 @@ __global__ __launch_bounds__(512) void gemm_nt_mfma(GemmArgs a) {
 #pragma unroll
     for (int bm = 0; bm < 2; ++bm) {
       const int r = 64 * wm + 32 * bm + (lane & 31);
-      xrd[bm][s] = r * 64 + 16 * ((2 * s + (lane >> 5)) ^ gswz(r));
+      xrd[bm][s] = kGTileBytes + r * 64 + 16 * ((2 * s + (lane >> 5)) ^ gswz(r));
     }
   }
 
@@ -110,58 +133,74 @@ __global__ __launch_bounds__(512) void gemm_nt_mfma(GemmArgs a) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[bn][bm][e] = 0.f;
 
-  // The products of a tile with the four loads of a later tile spread between
-  // them (one after every four products), so that the loads do not stall the
-  // wave in one burst.
-  auto issue_one = [&](int kt, int st, int u) __attribute__((always_inline)) {
-    const int kb = kt * kGK * 2;
-    if (u < 2)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          wrs, (lds_void*)(&lds[st][0][1024 * (2 * wave + u)]), 16, woff[u], kb, 0, 0);
-    else
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          xrs, (lds_void*)(&lds[st][1][1024 * (2 * wave + u - 2)]), 16, xoff[u - 2], kb, 0, 0);
-  };
-  auto compute_loading = [&](int st, bool ld, int kn, int sn) __attribute__((always_inline)) {
-    const unsigned char* wt = lds[st][0];
-    const unsigned char* xt = lds[st][1];
+  // The products of the tile in stage J with the four loads of tile kn (into
+  // stage J + 4) spread between them (one after every four products), so that
+  // the loads do not stall the wave in one burst.
+  auto compute_loading = [&](auto JC, int kn) __attribute__((always_inline)) {
+    constexpr int J = decltype(JC)::value;
+    const unsigned char* t = stage(JC);
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       bf16x8 wf[4], xf[2];
 #pragma unroll
-      for (int bn = 0; bn < 4; ++bn) wf[bn] = as_bf16x8(*reinterpret_cast<const uint4*>(wt + wrd[bn][s]));
+      for (int bn = 0; bn < 4; ++bn) wf[bn] = as_bf16x8(*reinterpret_cast<const uint4*>(t + wrd[bn][s]));
 #pragma unroll
-      for (int bm = 0; bm < 2; ++bm) xf[bm] = as_bf16x8(*reinterpret_cast<const uint4*>(xt + xrd[bm][s]));
+      for (int bm = 0; bm < 2; ++bm) xf[bm] = as_bf16x8(*reinterpret_cast<const uint4*>(t + xrd[bm][s]));
 #pragma unroll
       for (int bn = 0; bn < 4; ++bn) {
 #pragma unroll
         for (int bm = 0; bm < 2; ++bm) acc[bn][bm] = mfma32x32x16(wf[bn], xf[bm], acc[bn][bm]);
         if ((bn & 1) == 1) {
           __builtin_amdgcn_sched_barrier(0);
-          if (ld) issue_one(kn, sn, 2 * s + (bn >> 1));
+          issue_one(std::integral_constant<int, J + kGStages - 1>{}, kn, 2 * s + (bn >> 1));
           __builtin_amdgcn_sched_barrier(0);
         }
       }
     }
   };
 
-  // Iteration kt: wait for this wave's loads of tile kt, barrier (every wave's
-  // loads of tile kt have landed, and every wave is done with tile kt - 1,
-  // whose buffer takes tile kt + 4), products of tile kt with the loads of
-  // tile kt + 4.  (A wave has 4 loads per tile, issued in tile order.)
+  // Iteration kt (stage J = kt % 5): wait for this wave's loads of tile kt,
+  // barrier (every wave's loads of tile kt have landed, and every wave is done
+  // with tile kt - 1, whose stage takes tile kt + 4), products of tile kt with
+  // the loads of tile kt + 4.  Every iteration issues its four loads (a tile
+  // past the last re-reads the last one into a stage that is not read again),
+  // so a wave always has 16 loads in flight at the wait and 12 of them may
+  // stay; with no path that skips loads, the compiler too waits only for the
+  // loads of the stage it reads.  Rounds of five iterations keep every stage
+  // index a constant; only the last, partial round checks kt against nk.
   const int nk = a.K / kGK;
+  auto tile = [&](int kt) __attribute__((always_inline)) { return min(kt, nk - 1); };
 #pragma unroll
-  for (int s = 0; s < kGStages - 1; ++s)
-    if (s < nk) issue(s, s);
-  for (int kt = 0; kt < nk; ++kt) {
-    if (kt + 3 < nk) wait_vmcnt<12>();
-    else if (kt + 2 < nk) wait_vmcnt<8>();
-    else if (kt + 1 < nk) wait_vmcnt<4>();
-    else wait_vmcnt<0>();
+  for (int u = 0; u < 4; ++u) issue_one(std::integral_constant<int, 0>{}, 0, u);
+#pragma unroll
+  for (int u = 0; u < 4; ++u) issue_one(std::integral_constant<int, 1>{}, tile(1), u);
+#pragma unroll
+  for (int u = 0; u < 4; ++u) issue_one(std::integral_constant<int, 2>{}, tile(2), u);
+#pragma unroll
+  for (int u = 0; u < 4; ++u) issue_one(std::integral_constant<int, 3>{}, tile(3), u);
+  auto iter = [&](auto JC, int kt) __attribute__((always_inline)) {
+    wait_vmcnt<12>();
     lds_barrier();
-    compute_loading(kt % kGStages, kt + kGStages - 1 < nk, kt + kGStages - 1,
-                    (kt + kGStages - 1) % kGStages);
+    compute_loading(JC, tile(kt + kGStages - 1));
+  };
+  const int nfull = nk / kGStages;
+  for (int r = 0; r < nfull; ++r) {
+    const int k0 = r * kGStages;
+    iter(std::integral_constant<int, 0>{}, k0);
+    iter(std::integral_constant<int, 1>{}, k0 + 1);
+    iter(std::integral_constant<int, 2>{}, k0 + 2);
+    iter(std::integral_constant<int, 3>{}, k0 + 3);
+    iter(std::integral_constant<int, 4>{}, k0 + 4);
   }
+  {
+    const int k0 = nfull * kGStages, rest = nk - k0;  // 0 to 4 iterations
+    if (rest > 0) iter(std::integral_constant<int, 0>{}, k0);
+    if (rest > 1) iter(std::integral_constant<int, 1>{}, k0 + 1);
+    if (rest > 2) iter(std::integral_constant<int, 2>{}, k0 + 2);
+    if (rest > 3) iter(std::integral_constant<int, 3>{}, k0 + 3);
+  }
+  // no load may still be writing this workgroup's LDS when it exits
+  wait_vmcnt<0>();
 
   // Output: accumulator register e of block (bn, bm) holds feature
   // 32 bn + 8 (e / 4) + 4 (lane / 32) + e % 4 of token 32 bm + lane % 32.
@@ -218,11 +257,11 @@ hipError_t launch_gemm_nt(const void* x, const void* w, void* c, int M, int N, i
 
 }  // namespace
 
-// The matrix-core kernel's shapes: whole 256-feature tiles and 32-wide K
-// steps, 16-byte aligned rows, and byte offsets that fit its 32-bit buffer
+// The matrix-core kernel's shapes: whole 256-feature tiles and whole 32-wide
+// K steps (at least one), 16-byte aligned rows, and byte offsets that fit its 32-bit buffer
 // addressing (rows past M included).
 bool gemm_nt_mfma_shape(int N, int K, int G, int ldx, int ldc, int M) {
-  if (N % kGN != 0 || K % kGK != 0 || ldx % 8 != 0 || ldc % 8 != 0) return false;
+  if (N % kGN != 0 || K < kGK || K % kGK != 0 || ldx % 8 != 0 || ldc % 8 != 0) return false;
   const long mr = ((long)M + kGM - 1) / kGM * kGM;
   return mr * ldx * 2 < 0x7fffffffL && mr * ldc * 2 < 0x7fffffffL &&
          (long)G * N * K * 2 < 0x7fffffffL;

@@ -19,6 +19,11 @@ CASES = {
     "v4_prefill_rows_bf16": ("bf16", 300, 8, 4096, 1024, 4096),   # 8 groups of 8 heads x 512
     "v4_decode_bf16": ("bf16", 64, 8, 4096, 1024, 4096),
     "small_groups_bf16": ("bf16", 50, 4, 64, 256, 256),
+    # K steps of 32 in the matrix-core kernel: 5 then 16 (whole rounds of its
+    # 5-stage ring, then one extra step), 1 then 8, 4 then 24
+    "ksteps_5_bf16": ("bf16", 70, 2, 160, 256, 256),
+    "ksteps_1_bf16": ("bf16", 33, 1, 32, 256, 256),
+    "ksteps_4_bf16": ("bf16", 129, 3, 128, 256, 512),
     "generic_bf16": ("bf16", 20, 2, 40, 24, 16),
     "generic_f32": ("f32", 37, 2, 48, 40, 24),
 }
