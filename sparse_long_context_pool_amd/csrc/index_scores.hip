@@ -161,12 +161,19 @@ __global__ __launch_bounds__(64 * QR) void index_scores_mfma(
         for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) acc[mb][r] = 0.f;
+        // the B fragment of k-step ks + 1 is read before the products of
+        // k-step ks, so its LDS latency hides under them
+        uint4 bv[2];
+        bv[0] = *reinterpret_cast<const uint4*>(buf + nb * 8192 + roff[0]);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-          const uint4 bv = *reinterpret_cast<const uint4*>(buf + nb * 8192 + roff[ks]);
+          if (ks + 1 < KS)
+            bv[(ks + 1) & 1] = *reinterpret_cast<const uint4*>(buf + nb * 8192 + roff[ks + 1]);
+          __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
           for (int mb = 0; mb < MB; ++mb)
-            acc[mb] = mfma32x32x16(a[mb][ks], as_bf16x8(bv), acc[mb]);
+            acc[mb] = mfma32x32x16(a[mb][ks], as_bf16x8(bv[ks & 1]), acc[mb]);
+          __builtin_amdgcn_sched_barrier(0);
         }
         // accumulator register r holds head 32mb + 8(r/4) + 4(lane/32) + r%4
         float p4[4] = {0.f, 0.f, 0.f, 0.f};
@@ -412,12 +419,19 @@ __global__ __launch_bounds__(64 * QR) void index_topk_fused(
         for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) acc[mb][r] = 0.f;
+        // the B fragment of k-step ks + 1 is read before the products of
+        // k-step ks, so its LDS latency hides under them
+        uint4 bv[2];
+        bv[0] = *reinterpret_cast<const uint4*>(buf + nb * 8192 + roff[0]);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-          const uint4 bv = *reinterpret_cast<const uint4*>(buf + nb * 8192 + roff[ks]);
+          if (ks + 1 < KS)
+            bv[(ks + 1) & 1] = *reinterpret_cast<const uint4*>(buf + nb * 8192 + roff[ks + 1]);
+          __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
           for (int mb = 0; mb < MB; ++mb)
-            acc[mb] = mfma32x32x16(a[mb][ks], as_bf16x8(bv), acc[mb]);
+            acc[mb] = mfma32x32x16(a[mb][ks], as_bf16x8(bv[ks & 1]), acc[mb]);
+          __builtin_amdgcn_sched_barrier(0);
         }
         float p4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
