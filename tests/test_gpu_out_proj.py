@@ -62,3 +62,42 @@ def test_grouped_out_proj(name):
     assert np.all(d2 <= b2), (name, float((d2 / b2).max()))
     # and the result is not trivially small
     assert np.abs(out_o).mean() > 0.1
+
+
+def test_grouped_out_proj_full_size_sampled():
+    """The prefill workload's projection at its full size, in the launch the
+    benchmark times ([8192, 64 x 512] -> 8 groups x 1024 -> 4096, bf16, the
+    benchmark's seeded inputs), checked on 24 token rows: both ends, both
+    sides of 256-row tile seams, and 12 seeded random rows."""
+    from sparse_long_context_pool_amd import csa, synth
+    S, H, dv, G, rank, hidden = 8192, 64, 512, 8, 1024, 4096
+    Kg = H * dv // G
+    bf = torch.bfloat16
+    o = synth.normal_torch(0, "attn_out", S, (H * dv,), scale=0.5, dtype=bf).to("cuda")
+    w_a = synth.normal_torch(0, "o_a_proj", G * rank, (Kg,), scale=Kg ** -0.5,
+                             dtype=bf).to("cuda").view(G, rank, Kg)
+    w_b = synth.normal_torch(0, "o_b_proj", hidden, (G * rank,), scale=(G * rank) ** -0.5,
+                             dtype=bf).to("cuda")
+    mid_g, out_g = csa.csa_grouped_out_proj(o, w_a, w_b)
+    rng = np.random.default_rng(8192)
+    rows = np.unique(np.concatenate([[0, 1, 255, 256, 4095, 4096, 7935, 7936, 8190, 8191],
+                                     [2047, 6144], rng.integers(0, S, 12)]))
+    ri = torch.tensor(rows, device="cuda")
+    o_s = host(o.index_select(0, ri))
+    mid_s, out_s = host(mid_g.index_select(0, ri)), host(out_g.index_select(0, ri))
+    wa_h, wb_h = host(w_a), host(w_b)
+    del o, mid_g, out_g
+    torch.cuda.empty_cache()
+    u = 2.0 ** -24
+    mid_o, _ = oracle.grouped_out_proj(o_s, wa_h, wb_h, round_mid_bf16=True)
+    absum = np.concatenate([np.abs(o_s[:, g * Kg:(g + 1) * Kg]).astype(np.float64)
+                            @ np.abs(wa_h[g]).astype(np.float64).T for g in range(G)], axis=1)
+    b1 = Kg * u * absum + 2.0 ** -7 * np.abs(mid_o) + 1e-30
+    d1 = np.abs(mid_s - mid_o)
+    assert np.all(d1 <= b1), float((d1 / b1).max())
+    _, out_o = oracle.grouped_out_proj(None, None, wb_h, mid=mid_s)
+    absum2 = np.abs(mid_s).astype(np.float64) @ np.abs(wb_h).astype(np.float64).T
+    b2 = G * rank * u * absum2 + 2.0 ** -8 * np.abs(out_o) + 1e-30
+    d2 = np.abs(out_s - out_o)
+    assert np.all(d2 <= b2), float((d2 / b2).max())
+    assert np.abs(out_o).mean() > 0.01
